@@ -1,0 +1,230 @@
+/*
+ * pkv.h -- C ABI of libpkv: paged KV-cache write and paged decode attention
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Four operations, each an asynchronous launch on a caller-given HIP stream:
+ *
+ *   pkv_fill_slots          slot mapping from per-sequence block tables
+ *   pkv_cache_write_k_fused RMSNorm -> RoPE -> one rounding, into the K pool
+ *   pkv_cache_write_v       V reshape-and-cache copy into the V pool
+ *   pkv_paged_decode_attn   one-query-token GQA attention through the tables
+ *
+ * Sources (the pages this library implements):
+ *   [p1] docs.atlasinference.io, spark_model/layers/ops/kv_cache.rs
+ *   [p2] docs.metrale.ai, metrale_model_layers/layers/ops/kv_cache_fp8k.rs
+ *   [p3] docs.atlascybernetics.ai, spark_model/kimi_k3/mla_cuda.rs
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Every array argument is DEVICE memory owned by the caller (for
+ *   example a torch tensor's data pointer).  The library never allocates,
+ *   frees, copies between host and device, synchronises, or keeps state
+ *   between calls.  `stream` is a hipStream_t (NULL = the null stream).
+ * Pool layout ("NHD"), [p1] doc of reshape_and_cache_fp8 and [p2] module
+ *   invariants: a pool is [num_blocks, block_size, num_kv_heads, head_dim],
+ *   row-major, addressed from its base.  A slot is a flat row index
+ *   slot = block * block_size + offset; element (slot, h, d) sits at
+ *   (slot * num_kv_heads + h) * head_dim + d.
+ * Status.  0 on success.  A negative code is returned, before anything is
+ *   launched, for arguments the host can check; pkv_last_error() then gives
+ *   a message (thread-local, valid until the next call on that thread):
+ *     PKV_ERR_INVALID     (-1) NULL pointer, zero dimension, bad dtype enum,
+ *                              inconsistent sizes
+ *     PKV_ERR_UNSUPPORTED (-2) a shape/dtype/alignment outside the supported
+ *                              set listed at each call
+ *     PKV_ERR_WORKSPACE   (-3) workspace smaller than required
+ *     PKV_ERR_HIP         (-4) the launch itself failed (HIP error text)
+ *   A call with no work (zero tokens or sequences) returns 0 and launches
+ *   nothing ([p1] fill_slots_from_block_table returns early on count 0).
+ * Device-side conditions are defined behaviour, not errors: a negative slot
+ *   or one past the pool is skipped by the writes; a block-table entry
+ *   outside [0, num_blocks) excludes its tokens from attention; seq_len <= 0
+ *   gives an all-zero output row; table entries past ceil(seq_len /
+ *   block_size) are never read.
+ * Alignment.  Cache rows and input rows are read and written in 16-byte
+ *   pieces: every data pointer and every row stride (in bytes) must be a
+ *   multiple of 16, else PKV_ERR_UNSUPPORTED.
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  PKV_FP8_E4M3 is OCP FP8 E4M3FN (bias 7, no infinities,
+ * largest finite 448), the "FP8 E4M3" of [p1] and [p2]. */
+typedef enum pkv_dtype {
+    PKV_BF16 = 0,
+    PKV_FP8_E4M3 = 1,
+    PKV_FP32 = 2
+} pkv_dtype;
+
+enum {
+    PKV_OK = 0,
+    PKV_ERR_INVALID = -1,
+    PKV_ERR_UNSUPPORTED = -2,
+    PKV_ERR_WORKSPACE = -3,
+    PKV_ERR_HIP = -4
+};
+
+/* Message for the last non-zero status on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version as "major.minor.patch". */
+const char* pkv_version(void);
+
+/*
+ * pkv_fill_slots -- [p1] fill_slots_from_block_table: fill paged-KV slot
+ * mappings on the device from a persistent block table.
+ *
+ * For sequence s (s < num_seqs) and its i-th token, i in
+ * [cu_counts[s], cu_counts[s+1]), position p = start_pos[s] + (i - cu_counts[s]):
+ *     slots[i] = block_tables[s * max_blocks_per_seq + p / block_size]
+ *                * block_size + p % block_size
+ * Batched form of the page's one-sequence call (num_seqs = 1, cu_counts =
+ * {0, count} is that call).  A token whose block index p / block_size is not
+ * below max_blocks_per_seq, or whose p is negative, or that no sequence
+ * covers (i >= cu_counts[num_seqs]), gets slot -1.  A negative table entry
+ * gives a negative slot (skipped by the writes).
+ *
+ *   slots          out  int64 [total_tokens]
+ *   block_tables   in   int32 [num_seqs, max_blocks_per_seq]
+ *   start_pos      in   int32 [num_seqs]
+ *   cu_counts      in   int32 [num_seqs + 1], non-decreasing, cu_counts[0] = 0
+ *   total_tokens        length of `slots` (usually cu_counts[num_seqs])
+ * Supported: block_size in 1..65536.
+ */
+int pkv_fill_slots(int64_t* slots, const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                   const int32_t* start_pos, const int32_t* cu_counts, uint32_t num_seqs,
+                   uint32_t total_tokens, uint32_t block_size, void* stream);
+
+/*
+ * pkv_cache_write_k_fused -- [p1] fused_k_norm_rope_cache_write_{bf16,
+ * bf16_mrope, fp8}: RMSNorm, then RoPE, then ONE rounding at the store, all
+ * in FP32 in between ([p1] doc: K stays FP32 between the three operations;
+ * [p2] module invariants: FP8 stores k / k_scale as E4M3).
+ *
+ * For each token t with 0 <= slot_mapping[t] < num_blocks * block_size and
+ * each kv head h, with x = k_in[t, h, :] (FP32 of the input):
+ *   RMSNorm (norm_weight != NULL):  y = x / sqrt(mean_j x_j^2 + rms_eps) * w
+ *   RoPE (nope == 0, rotary_dim > 0), NeoX rotate-half pairs over dims
+ *     [rope_offset, rope_offset + rotary_dim): for pair i < rotary_dim / 2,
+ *     a = y[o + i], b = y[o + i + rotary_dim/2], angle = fl32(pos * invf_i),
+ *     invf_i = fl32(theta^(-2i / rotary_dim)):
+ *       a' = a cos(angle) - b sin(angle),  b' = b cos(angle) + a sin(angle)
+ *     pos = pos_t[t]; when pos_h and pos_w are both non-NULL (MRoPE,
+ *     [p1] ..._bf16_mrope), pair i uses {pos_t, pos_h, pos_w}[i % 3][t];
+ *     with pos_t == pos_h == pos_w the result is bit-identical to the
+ *     scalar form.
+ *   Store into k_cache[slot, h, :]:
+ *     PKV_BF16      round-to-nearest-even of the FP32 value
+ *     PKV_FP8_E4M3  saturating E4M3 of fl32(value / k_scale): magnitudes
+ *                   above 448 become +-448, NaN stays NaN
+ *     PKV_FP32      the FP32 value
+ *
+ *   k_in          in  [num_tokens, num_kv_heads, head_dim] of in_dtype; token
+ *                     t starts at element t * in_token_stride; heads packed
+ *   norm_weight   in  [head_dim] of in_dtype, shared by all heads; NULL = no norm
+ *   pos_t         in  int32 [num_tokens] (ignored when nope != 0 or rotary_dim == 0)
+ *   pos_h, pos_w  in  int32 [num_tokens] or both NULL
+ *   slot_mapping  in  int64 [num_tokens]
+ *   k_cache       out [num_blocks, block_size, num_kv_heads, head_dim] of cache_dtype
+ *   k_scale           FP8 only: per-tensor scale, finite and > 0
+ * Supported: in_dtype BF16 or FP32; cache_dtype BF16, FP8_E4M3 or FP32;
+ *   head_dim in {64, 128, 192, 256}; rotary_dim even, rope_offset +
+ *   rotary_dim <= head_dim, rope_offset and rotary_dim / 2 multiples of
+ *   the 16-byte input vector (8 BF16 or 4 FP32 elements).
+ */
+int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype, uint64_t in_token_stride,
+                            const void* norm_weight, float rms_eps,
+                            const int32_t* pos_t, const int32_t* pos_h, const int32_t* pos_w,
+                            float theta, uint32_t rope_offset, uint32_t rotary_dim, int nope,
+                            const int64_t* slot_mapping, uint32_t num_tokens,
+                            uint32_t num_kv_heads, uint32_t head_dim, uint32_t block_size,
+                            uint32_t num_blocks, void* k_cache, pkv_dtype cache_dtype,
+                            float k_scale, void* stream);
+
+/*
+ * pkv_cache_write_v -- [p1] reshape_and_cache_flash_v_only: the V-only paged
+ * cache write, companion of the fused K write so that the K side of the
+ * cache is written by the fused kernel alone.
+ *
+ * For each token t with 0 <= slot_mapping[t] < num_blocks * block_size:
+ *   v_cache[slot, h, :] = v[t, h, :]  for every kv head h, byte for byte.
+ *
+ *   v             in  [num_tokens, num_kv_heads, head_dim_v] of dtype, token
+ *                     stride in_token_stride elements
+ *   slot_mapping  in  int64 [num_tokens]
+ *   v_cache       out [num_blocks, block_size, num_kv_heads, head_dim_v] of dtype
+ * Supported: dtype BF16 or FP32; num_kv_heads * head_dim_v * sizeof(dtype)
+ *   a multiple of 16 bytes.
+ */
+int pkv_cache_write_v(const void* v, pkv_dtype dtype, uint64_t in_token_stride,
+                      const int64_t* slot_mapping, uint32_t num_tokens, uint32_t num_kv_heads,
+                      uint32_t head_dim_v, uint32_t block_size, uint32_t num_blocks,
+                      void* v_cache, void* stream);
+
+/*
+ * pkv_decode_workspace_bytes -- bytes of device workspace that
+ * pkv_paged_decode_attn needs for these sizes (split-K partial results).
+ * 0 means none is needed.  Depends only on the arguments given.
+ */
+size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
+                                  uint32_t num_kv_heads, uint32_t head_dim_v,
+                                  uint32_t max_blocks_per_seq, uint32_t block_size);
+
+/*
+ * pkv_paged_decode_attn -- [p1] paged_decode_attn_fp8 and its BF16 sibling
+ * (one query token per sequence, reading K/V through block_tables i32
+ * [num_seqs * max_blocks_per_seq] and seq_lens i32 [num_seqs], GQA through
+ * num_q_heads / num_kv_heads, scaled scores, FP8 K multiplied back by
+ * k_scale), with the optional elementwise output gate of [p3] (SDPA + gate)
+ * and the optional query rotation of [p3] (maybe_rope before SDPA).
+ *
+ * For sequence s, query head h, kv head g = h / (num_q_heads / num_kv_heads),
+ * n = seq_lens[s], tokens t < n at row P * block_size + t % block_size with
+ * P = block_tables[s][t / block_size]:
+ *   q' = q[s, h, :], rotated at position n - 1 when q_rope != 0 (same RoPE
+ *        as the K write over [q_rope_offset, q_rope_offset + q_rope_dim),
+ *        theta q_rope_theta)
+ *   s_t = scale * <q', k_t>, k_t = k_cache row (E4M3 codes times k_scale)
+ *   out[s, h, :] = sum_t softmax(s)_t v_t   (times gate[s, h, :] if given)
+ * Computed in FP32 with split-K over the token range and a log-sum-exp
+ * merge; out is FP32.
+ *
+ *   q             in  [num_seqs, num_q_heads, head_dim_qk] of q_dtype; sequence
+ *                     s starts at element s * q_seq_stride
+ *   k_cache       in  [num_blocks, block_size, num_kv_heads, head_dim_qk] of k_dtype
+ *   v_cache       in  [num_blocks, block_size, num_kv_heads, head_dim_v] of v_dtype
+ *   block_tables  in  int32 [num_seqs, max_blocks_per_seq]
+ *   seq_lens      in  int32 [num_seqs], each <= max_blocks_per_seq * block_size
+ *   gate          in  FP32 [num_seqs, num_q_heads, head_dim_v] or NULL
+ *   out           out FP32 [num_seqs, num_q_heads, head_dim_v]
+ *   workspace     device scratch of at least
+ *                 pkv_decode_workspace_bytes(...) bytes (may be NULL if that is 0)
+ * Supported: (q, K, V) dtypes (BF16, BF16, BF16), (BF16, FP8_E4M3, BF16),
+ *   (FP32, FP32, FP32); num_q_heads % num_kv_heads == 0; block_size 16;
+ *   head_dim_qk in {64, 128, 192, 256}, head_dim_v in {64, 128} (BF16 caches:
+ *   head_dim_qk == head_dim_v in {64, 128}); q_rope_dim even with
+ *   q_rope_offset + q_rope_dim <= head_dim_qk.
+ */
+int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
+                          const void* k_cache, pkv_dtype k_dtype, float k_scale,
+                          const void* v_cache, pkv_dtype v_dtype,
+                          const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                          const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
+                          uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
+                          uint32_t head_dim_v, uint32_t block_size, float scale,
+                          int q_rope, float q_rope_theta, uint32_t q_rope_offset,
+                          uint32_t q_rope_dim, const float* gate, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

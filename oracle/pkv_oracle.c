@@ -1,0 +1,501 @@
+/*
+ * pkv_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct CPU definition of the paged KV-cache path:
+ * slot mapping, the fused K cache write (RMSNorm -> RoPE -> one rounding),
+ * the V reshape-and-cache copy and paged decode attention.
+ *
+ * Only the test suite, the smoke check and the benchmark's CPU-baseline leg
+ * may load this library.  The product (the HIP library) never links, loads or
+ * calls it, and the two share no source, header, table or helper.
+ *
+ * Arithmetic is FP64 except where the pages fix the precision:
+ *   - the K path is held in FP32 at the store ("K stays FP32 between the
+ *     three operations and is rounded only at the cache write": page 1,
+ *     kv_cache.rs, doc of fused_k_norm_rope_cache_write_bf16), so the
+ *     quantisation decision is taken on fl32 of the FP64 result;
+ *   - the RoPE angle is an FP32 product of the FP32 position and an FP32
+ *     inverse frequency (the FP32 regime of the same doc; our reading).
+ *
+ * Sources cited below are the three pages:
+ *   p1 = docs.atlasinference.io .../spark_model/layers/ops/kv_cache.rs
+ *   p2 = docs.metrale.ai .../metrale_model_layers/layers/ops/kv_cache_fp8k.rs
+ *   p3 = docs.atlascybernetics.ai .../spark_model/kimi_k3/mla_cuda.rs
+ * Where the pages leave a step open, the plainest reading is taken and
+ * stated beside the code that makes it.
+ *
+ * Pins (tests/test_oracle_*.py) tie every function here to closed forms,
+ * library routines, format specifications and invariants.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Element types.  Numbered like the product's enum only by convention; the
+ * values are restated here, not included. */
+enum { O_BF16 = 0, O_E4M3 = 1, O_F32 = 2 };
+
+/* ------------------------------------------------------------------ */
+/* Number formats                                                      */
+/* ------------------------------------------------------------------ */
+
+/* bfloat16 -> binary32: bf16 is the upper half of a binary32 pattern. */
+float pkvo_f32_from_bf16(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* binary32 -> bfloat16, IEEE round-to-nearest-even, written from the
+ * definition: take the two bf16 neighbours of x (truncation toward zero and
+ * the next value away from zero) and keep the nearer one, the one with an
+ * even last bit on a tie.  A value past the largest finite bf16 rounds to
+ * infinity exactly when IEEE says so (the "next" neighbour is then inf and
+ * the tie/nearness test is done in double).  NaN returns a quiet NaN of the
+ * same sign. */
+uint16_t pkvo_bf16_from_f32(float x)
+{
+    uint32_t u;
+    memcpy(&u, &x, sizeof u);
+    if (isnan(x))
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint16_t lo = (uint16_t)(u >> 16);           /* |lo| <= |x|, same sign */
+    if ((u & 0xFFFFu) == 0)
+        return lo;                               /* exactly representable */
+    uint16_t hi = (uint16_t)(lo + 1);            /* next bf16 away from zero */
+    double dx = fabs((double)x);
+    double dlo = fabs((double)pkvo_f32_from_bf16(lo));
+    double dhi;
+    if ((hi & 0x7FFFu) == 0x7F80u) {
+        /* The neighbour past the largest finite value is infinity; IEEE
+         * rounds to it when x is at or beyond the midpoint between the
+         * largest finite value and 2^128 (the value the next step would
+         * have had with an unbounded exponent). */
+        dhi = ldexp(1.0, 128);
+    } else {
+        dhi = fabs((double)pkvo_f32_from_bf16(hi));
+    }
+    double elo = dx - dlo, ehi = dhi - dx;
+    if (elo < ehi) return lo;
+    if (ehi < elo) return hi;
+    return (lo & 1u) ? hi : lo;                  /* tie: even last bit */
+}
+
+/* OCP 8-bit floating point, E4M3FN: 1 sign bit, 4 exponent bits (bias 7),
+ * 3 mantissa bits, no infinities, NaN = S.1111.111, largest finite 448.
+ * Value of a non-negative code c (c < 0x7F):
+ *   exponent field e = c >> 3, mantissa m = c & 7
+ *   e == 0 : m * 2^-9                  (subnormal)
+ *   e >= 1 : (8 + m) * 2^(e - 10)      (normal)                        */
+double pkvo_f64_from_e4m3(uint8_t c)
+{
+    int neg = (c & 0x80) != 0;
+    int mag = c & 0x7F;
+    if (mag == 0x7F)
+        return neg ? -NAN : NAN;
+    int e = mag >> 3, m = mag & 7;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return neg ? -v : v;
+}
+
+/* x -> E4M3FN by round-to-nearest-even over the 127 non-negative finite
+ * codes, saturating: a magnitude above 448 (infinity included) becomes 448
+ * ("saturating FP8 cast": p1 kv_cache.rs, doc of
+ * fused_k_norm_rope_cache_write_fp8).  NaN becomes the NaN code of the same
+ * sign.  Zero keeps its sign.  Written as a nearest-value search over the
+ * code table, so it follows the format definition directly. */
+uint8_t pkvo_e4m3_from_f64(double x)
+{
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x))
+        return (uint8_t)(sign | 0x7F);
+    double a = fabs(x);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    int best = 0;
+    double best_err = a;                         /* distance to code 0 */
+    for (int c = 1; c <= 0x7E; ++c) {
+        double err = fabs(a - pkvo_f64_from_e4m3((uint8_t)c));
+        if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+            best = c;
+            best_err = err;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* ------------------------------------------------------------------ */
+/* Threading helper: split [0, n) over nthreads workers.               */
+/* ------------------------------------------------------------------ */
+
+typedef void (*range_fn)(void* ctx, uint64_t begin, uint64_t end);
+
+typedef struct {
+    range_fn fn;
+    void* ctx;
+    uint64_t begin, end;
+} range_job;
+
+static void* range_trampoline(void* p)
+{
+    range_job* j = (range_job*)p;
+    j->fn(j->ctx, j->begin, j->end);
+    return NULL;
+}
+
+static void parallel_for(uint64_t n, int nthreads, range_fn fn, void* ctx)
+{
+    if (nthreads < 1) nthreads = 1;
+    if ((uint64_t)nthreads > n) nthreads = (int)(n ? n : 1);
+    if (nthreads == 1) {
+        fn(ctx, 0, n);
+        return;
+    }
+    pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+    range_job* jobs = (range_job*)malloc(sizeof(range_job) * (size_t)nthreads);
+    for (int i = 0; i < nthreads; ++i) {
+        jobs[i].fn = fn;
+        jobs[i].ctx = ctx;
+        jobs[i].begin = n * (uint64_t)i / (uint64_t)nthreads;
+        jobs[i].end = n * (uint64_t)(i + 1) / (uint64_t)nthreads;
+        pthread_create(&th[i], NULL, range_trampoline, &jobs[i]);
+    }
+    for (int i = 0; i < nthreads; ++i)
+        pthread_join(th[i], NULL);
+    free(th);
+    free(jobs);
+}
+
+/* ------------------------------------------------------------------ */
+/* (1) Slot mapping                                                    */
+/* ------------------------------------------------------------------ */
+
+/* For sequence s and its i-th token (p = start_pos[s] + i, i < count_s):
+ *   slot = block_table[s][p / B] * B + p % B
+ * (p1 kv_cache.rs, doc of fill_slots_from_block_table: slots are filled on
+ * the device from a persistent block table, positions start_pos onward, with
+ * block_size; slot_mapping is i64 per the doc of reshape_and_cache; a slot is
+ * the flat row index of the [num_blocks, block_size] pool).  Batched: token range of sequence s
+ * is [cu_counts[s], cu_counts[s+1]).  A position whose block index falls
+ * outside the table, or a negative position, gives slot -1 (padding). */
+void pkvo_fill_slots(int64_t* slots, const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                     const int32_t* start_pos, const int32_t* cu_counts, uint32_t num_seqs,
+                     uint32_t total_tokens, uint32_t block_size)
+{
+    for (uint32_t i = 0; i < total_tokens; ++i)
+        slots[i] = -1;
+    for (uint32_t s = 0; s < num_seqs; ++s) {
+        for (int64_t i = cu_counts[s]; i < cu_counts[s + 1]; ++i) {
+            if (i < 0 || i >= (int64_t)total_tokens)
+                continue;
+            int64_t p = (int64_t)start_pos[s] + (i - cu_counts[s]);
+            if (p < 0)
+                continue;
+            int64_t b = p / (int64_t)block_size;
+            if (b >= (int64_t)max_blocks_per_seq)
+                continue;
+            int64_t blk = block_tables[(uint64_t)s * max_blocks_per_seq + (uint64_t)b];
+            slots[i] = blk * (int64_t)block_size + p % (int64_t)block_size;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* (2) RoPE frequency                                                  */
+/* ------------------------------------------------------------------ */
+
+/* Inverse frequency of rotation pair i over rotary_dim R:
+ *   theta^(-2i/R), rounded once to FP32.                              */
+float pkvo_rope_inv_freq(float theta, uint32_t i, uint32_t rotary_dim)
+{
+    return (float)pow((double)theta, -(2.0 * (double)i) / (double)rotary_dim);
+}
+
+/* Angle of pair i at integer position pos: one FP32 product. */
+float pkvo_rope_angle(int32_t pos, float inv_freq)
+{
+    volatile float p = (float)pos;               /* keep it a single fp32 multiply */
+    volatile float a = p * inv_freq;
+    return a;
+}
+
+/* Rotate y[offset .. offset+R) in place: NeoX rotate-half pairs (i, i+R/2).
+ * For pair i:  a' = a cos(t) - b sin(t),   b' = b cos(t) + a sin(t),
+ * t the FP32 angle of pair i, cos/sin evaluated in double. */
+static void rope_rotate(double* y, uint32_t offset, uint32_t R, float theta,
+                        const int32_t* pos3 /* pos for i%3 = 0,1,2 */)
+{
+    uint32_t half = R / 2;
+    for (uint32_t i = 0; i < half; ++i) {
+        float invf = pkvo_rope_inv_freq(theta, i, R);
+        float ang = pkvo_rope_angle(pos3[i % 3], invf);
+        double c = cos((double)ang), s = sin((double)ang);
+        double a = y[offset + i], b = y[offset + i + half];
+        y[offset + i] = a * c - b * s;
+        y[offset + i + half] = b * c + a * s;
+    }
+}
+
+static double load_elem(const void* base, int dtype, uint64_t idx)
+{
+    switch (dtype) {
+    case O_BF16: return (double)pkvo_f32_from_bf16(((const uint16_t*)base)[idx]);
+    case O_F32: return (double)((const float*)base)[idx];
+    default: return pkvo_f64_from_e4m3(((const uint8_t*)base)[idx]);
+    }
+}
+
+static size_t elem_size(int dtype)
+{
+    return dtype == O_BF16 ? 2 : dtype == O_F32 ? 4 : 1;
+}
+
+/* ------------------------------------------------------------------ */
+/* (3) Fused K cache write                                             */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const void* k_in; int in_dtype; uint64_t in_token_stride;
+    const void* norm_weight; float eps;
+    const int32_t *pos_t, *pos_h, *pos_w;
+    float theta; uint32_t rope_offset, rotary_dim; int nope;
+    const int64_t* slots; uint32_t num_kv_heads, head_dim;
+    uint64_t num_slots; void* k_cache; int cache_dtype; float k_scale;
+} kwrite_ctx;
+
+static void kwrite_range(void* p, uint64_t t0, uint64_t t1)
+{
+    const kwrite_ctx* c = (const kwrite_ctx*)p;
+    const uint32_t D = c->head_dim, H = c->num_kv_heads;
+    double* y = (double*)malloc(sizeof(double) * D);
+    for (uint64_t t = t0; t < t1; ++t) {
+        int64_t slot = c->slots[t];
+        if (slot < 0 || (uint64_t)slot >= c->num_slots)
+            continue;                            /* padding slot: no write */
+        for (uint32_t h = 0; h < H; ++h) {
+            uint64_t src = t * c->in_token_stride + (uint64_t)h * D;
+            for (uint32_t j = 0; j < D; ++j)
+                y[j] = load_elem(c->k_in, c->in_dtype, src + j);
+            /* RMSNorm over the whole head: y = x / sqrt(mean(x^2) + eps) * w
+             * (p1 fused_k_norm_rope_cache_write_bf16: rms_norm with
+             * k_norm_weight and rms_eps, first of the three fused steps) */
+            if (c->norm_weight) {
+                double ss = 0.0;
+                for (uint32_t j = 0; j < D; ++j)
+                    ss += y[j] * y[j];
+                double r = 1.0 / sqrt(ss / (double)D + (double)c->eps);
+                for (uint32_t j = 0; j < D; ++j)
+                    y[j] = y[j] * r * load_elem(c->norm_weight, c->in_dtype, j);
+            }
+            /* RoPE at the token's position; the MRoPE variant picks the
+             * position axis by pair index mod 3 (p1 doc of
+             * fused_k_norm_rope_cache_write_bf16_mrope); NoPE skips it
+             * (p3 module doc: NoPE skips rotate). */
+            if (!c->nope && c->rotary_dim > 0) {
+                int32_t pos3[3];
+                pos3[0] = c->pos_t[t];
+                pos3[1] = (c->pos_h && c->pos_w) ? c->pos_h[t] : pos3[0];
+                pos3[2] = (c->pos_h && c->pos_w) ? c->pos_w[t] : pos3[0];
+                rope_rotate(y, c->rope_offset, c->rotary_dim, c->theta, pos3);
+            }
+            /* One rounding at the store: the FP32 value of K, then BF16
+             * round-to-nearest-even, or the saturating E4M3 cast of
+             * k / k_scale (p2 module invariants: the write stores k/k_scale
+             * as E4M3), or FP32 unchanged. */
+            uint64_t dst = ((uint64_t)slot * H + h) * D;
+            for (uint32_t j = 0; j < D; ++j) {
+                float k32 = (float)y[j];
+                switch (c->cache_dtype) {
+                case O_BF16:
+                    ((uint16_t*)c->k_cache)[dst + j] = pkvo_bf16_from_f32(k32);
+                    break;
+                case O_F32:
+                    ((float*)c->k_cache)[dst + j] = k32;
+                    break;
+                default: {
+                    float z = (float)((double)k32 / (double)c->k_scale); /* fl32(k/k_scale) */
+                    ((uint8_t*)c->k_cache)[dst + j] = pkvo_e4m3_from_f64((double)z);
+                }
+                }
+            }
+        }
+    }
+    free(y);
+}
+
+void pkvo_cache_write_k(const void* k_in, int in_dtype, uint64_t in_token_stride,
+                        const void* norm_weight, float eps,
+                        const int32_t* pos_t, const int32_t* pos_h, const int32_t* pos_w,
+                        float theta, uint32_t rope_offset, uint32_t rotary_dim, int nope,
+                        const int64_t* slots, uint32_t num_tokens, uint32_t num_kv_heads,
+                        uint32_t head_dim, uint32_t block_size, uint32_t num_blocks,
+                        void* k_cache, int cache_dtype, float k_scale, int nthreads)
+{
+    kwrite_ctx c = {k_in, in_dtype, in_token_stride, norm_weight, eps, pos_t, pos_h, pos_w,
+                    theta, rope_offset, rotary_dim, nope, slots, num_kv_heads, head_dim,
+                    (uint64_t)num_blocks * block_size, k_cache, cache_dtype, k_scale};
+    parallel_for(num_tokens, nthreads, kwrite_range, &c);
+}
+
+/* ------------------------------------------------------------------ */
+/* (4) V reshape-and-cache                                             */
+/* ------------------------------------------------------------------ */
+
+/* v_cache[slot, h, :] = v[t, h, :] byte for byte; padding slots skipped
+ * (p1 reshape_and_cache_flash_v_only: the V-only write that leaves the K
+ * side of the cache to the fused K kernel). */
+void pkvo_cache_write_v(const void* v, int dtype, uint64_t in_token_stride,
+                        const int64_t* slots, uint32_t num_tokens, uint32_t num_kv_heads,
+                        uint32_t head_dim_v, uint32_t block_size, uint32_t num_blocks,
+                        void* v_cache)
+{
+    size_t es = elem_size(dtype);
+    size_t row = (size_t)num_kv_heads * head_dim_v * es;
+    uint64_t num_slots = (uint64_t)num_blocks * block_size;
+    for (uint64_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = slots[t];
+        if (slot < 0 || (uint64_t)slot >= num_slots)
+            continue;
+        memcpy((char*)v_cache + (uint64_t)slot * row,
+               (const char*)v + t * in_token_stride * es, row);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* (5) Paged decode attention                                          */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    const void* q; int q_dtype; uint64_t q_seq_stride;
+    const void* k_cache; int k_dtype; float k_scale;
+    const void* v_cache; int v_dtype; float v_scale;
+    const int32_t* block_tables; uint32_t max_blocks_per_seq;
+    const int32_t* seq_lens; uint32_t num_blocks;
+    uint32_t Hq, Hkv, Dqk, Dv, B; float scale;
+    int q_rope; float q_rope_theta; uint32_t q_rope_offset, q_rope_dim;
+    const float* gate; float* out;
+} decode_ctx;
+
+/* Dequantised cache element: BF16 and FP32 exactly, E4M3 exactly times its
+ * per-tensor scale (p2 module invariants: the decode multiplies by k_scale). */
+static double cache_elem(const void* base, int dtype, float scl, uint64_t idx)
+{
+    double x = load_elem(base, dtype, idx);
+    return dtype == O_E4M3 ? x * (double)scl : x;
+}
+
+static void decode_range(void* p, uint64_t u0, uint64_t u1)
+{
+    const decode_ctx* c = (const decode_ctx*)p;
+    const uint32_t G = c->Hq / c->Hkv;
+    double* q = (double*)malloc(sizeof(double) * c->Dqk);
+    double* o = (double*)malloc(sizeof(double) * c->Dv);
+    for (uint64_t u = u0; u < u1; ++u) {
+        uint32_t s = (uint32_t)(u / c->Hq), h = (uint32_t)(u % c->Hq);
+        uint32_t g = h / G;                      /* GQA: contiguous groups */
+        float* dst = c->out + ((uint64_t)s * c->Hq + h) * c->Dv;
+        int32_t n = c->seq_lens[s];
+        for (uint32_t d = 0; d < c->Dv; ++d)
+            o[d] = 0.0;
+        if (n <= 0) {
+            for (uint32_t d = 0; d < c->Dv; ++d)
+                dst[d] = 0.0f;
+            continue;
+        }
+        uint64_t qoff = (uint64_t)s * c->q_seq_stride + (uint64_t)h * c->Dqk;
+        for (uint32_t j = 0; j < c->Dqk; ++j)
+            q[j] = load_elem(c->q, c->q_dtype, qoff + j);
+        if (c->q_rope && c->q_rope_dim > 0) {
+            int32_t pos3[3] = {n - 1, n - 1, n - 1};   /* the query is the last token */
+            rope_rotate(q, c->q_rope_offset, c->q_rope_dim, c->q_rope_theta, pos3);
+        }
+        /* pass 1: scores and their maximum */
+        double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+        unsigned char* ok = (unsigned char*)malloc((size_t)n);
+        double m = -INFINITY;
+        for (int32_t t = 0; t < n; ++t) {
+            uint32_t b = (uint32_t)t / c->B;
+            ok[t] = 0;
+            if (b >= c->max_blocks_per_seq)
+                continue;
+            int32_t blk = c->block_tables[(uint64_t)s * c->max_blocks_per_seq + b];
+            if (blk < 0 || (uint32_t)blk >= c->num_blocks)
+                continue;                        /* unmapped block: token excluded */
+            uint64_t row = (uint64_t)blk * c->B + (uint32_t)t % c->B;
+            uint64_t koff = (row * c->Hkv + g) * c->Dqk;
+            double dot = 0.0;
+            for (uint32_t j = 0; j < c->Dqk; ++j)
+                dot += q[j] * cache_elem(c->k_cache, c->k_dtype, c->k_scale, koff + j);
+            sc[t] = (double)c->scale * dot;
+            ok[t] = 1;
+            if (sc[t] > m) m = sc[t];
+        }
+        /* pass 2: softmax weights and the weighted sum of V rows */
+        double l = 0.0;
+        for (int32_t t = 0; t < n; ++t) {
+            if (!ok[t]) continue;
+            uint32_t b = (uint32_t)t / c->B;
+            int32_t blk = c->block_tables[(uint64_t)s * c->max_blocks_per_seq + b];
+            uint64_t row = (uint64_t)blk * c->B + (uint32_t)t % c->B;
+            uint64_t voff = (row * c->Hkv + g) * c->Dv;
+            double pt = exp(sc[t] - m);
+            l += pt;
+            for (uint32_t d = 0; d < c->Dv; ++d)
+                o[d] += pt * cache_elem(c->v_cache, c->v_dtype, c->v_scale, voff + d);
+        }
+        for (uint32_t d = 0; d < c->Dv; ++d) {
+            double val = l > 0.0 ? o[d] / l : 0.0;
+            /* optional elementwise output gate (p3 module doc: SDPA + gate) */
+            if (c->gate)
+                val *= (double)c->gate[((uint64_t)s * c->Hq + h) * c->Dv + d];
+            dst[d] = (float)val;
+        }
+        free(sc);
+        free(ok);
+    }
+    free(q);
+    free(o);
+}
+
+void pkvo_paged_decode(const void* q, int q_dtype, uint64_t q_seq_stride,
+                       const void* k_cache, int k_dtype, float k_scale,
+                       const void* v_cache, int v_dtype, float v_scale,
+                       const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                       const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
+                       uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
+                       uint32_t head_dim_v, uint32_t block_size, float scale,
+                       int q_rope, float q_rope_theta, uint32_t q_rope_offset,
+                       uint32_t q_rope_dim, const float* gate, float* out, int nthreads)
+{
+    decode_ctx c = {q, q_dtype, q_seq_stride, k_cache, k_dtype, k_scale, v_cache, v_dtype,
+                    v_scale, block_tables, max_blocks_per_seq, seq_lens, num_blocks,
+                    num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, block_size, scale,
+                    q_rope, q_rope_theta, q_rope_offset, q_rope_dim, gate, out};
+    parallel_for((uint64_t)num_seqs * num_q_heads, nthreads, decode_range, &c);
+}
+
+/* ------------------------------------------------------------------ */
+/* Array forms of the converters (for the pin tests).                  */
+/* ------------------------------------------------------------------ */
+
+void pkvo_bf16_from_f32_array(const float* x, uint16_t* out, uint64_t n)
+{
+    for (uint64_t i = 0; i < n; ++i)
+        out[i] = pkvo_bf16_from_f32(x[i]);
+}
+
+void pkvo_e4m3_from_f32_array(const float* x, uint8_t* out, uint64_t n)
+{
+    for (uint64_t i = 0; i < n; ++i)
+        out[i] = pkvo_e4m3_from_f64((double)x[i]);
+}
+
+void pkvo_f64_from_e4m3_array(const uint8_t* c, double* out, uint64_t n)
+{
+    for (uint64_t i = 0; i < n; ++i)
+        out[i] = pkvo_f64_from_e4m3(c[i]);
+}
