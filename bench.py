@@ -1,0 +1,338 @@
+"""Benchmark of the paged KV-cache hot path on one MI355X.
+
+A step is one decode step of the whole path over a full-size batch:
+  fill_slots (one new token per sequence, position seq_len-1)
+  -> fused K write (RMSNorm, RoPE, one rounding) -> V write
+  -> paged decode attention over every sequence's whole history.
+Before timing, the history of every sequence is written into the shuffled
+pools through the same write calls (the population write); that write is
+timed on its own and reported as the cache-write throughput.
+
+Workloads (seeded, synthetic): ``decode_bf16_256seq`` (default; 256 sequences,
+lengths U[512, 8192], Hq 32 / Hkv 8, D 128, BF16 K and V) and
+``decode_fp8k_64seq_long`` (64 sequences, U[16384, 32768], Hq 64 / Hkv 8,
+FP8 E4M3 K with k_scale = max|stored K| / 448, BF16 V).
+
+Prints one JSON line.  ``value`` is the algorithmic HBM bytes of one step
+divided by the step time (GB/s); the decode attention's KV read is >99.9% of
+those bytes.  ``roofline`` covers the decode attention call (its split-K
+kernel and its merge kernel), timed with HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD_INDEX = {"decode_bf16_256seq": 2, "decode_fp8k_64seq_long": 3}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="decode_bf16_256seq", choices=sorted(WORKLOAD_INDEX))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--split-tokens", type=int, default=0)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain 2 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# --------------------------------------------------------------------------
+# algorithmic bytes (what the method must move)
+# --------------------------------------------------------------------------
+
+def decode_bytes(lens, Hq, Hkv, D, Dv, kb, vb, qb, B=16):
+    """KV rows read + block-table entries + seq_len + q read + FP32 out written."""
+    n = np.asarray(lens, np.int64)
+    kv = int(n.sum()) * Hkv * (D * kb + Dv * vb)
+    bt = int(((n + B - 1) // B).sum()) * 4
+    S = n.size
+    return kv + bt + 4 * S + S * Hq * D * qb + S * Hq * Dv * 4
+
+
+def kwrite_bytes(T, Hkv, D, in_b, out_b):
+    """K rows read and written, slot (8 B) and position (4 B) per token."""
+    return T * (Hkv * D * (in_b + out_b) + 8 + 4)
+
+
+def vwrite_bytes(T, Hkv, Dv, b):
+    return T * (Hkv * Dv * 2 * b + 8)
+
+
+def slots_bytes(T, S, B=16):
+    return T * 8 + int(math.ceil(T / B)) * 4 + S * 8
+
+
+# --------------------------------------------------------------------------
+
+def copy_probe():
+    import torch
+    n = 2 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
+
+
+def traffic_from_profile(kernel_src_hash: str, workload: str):
+    """HBM bytes per decode call measured with rocprofv3 --pmc (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain copy's counters), stored in profiles/ with the
+    hash of the kernel source they were taken on; None when stale or absent."""
+    path = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_pmc.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_call:\s*([0-9.e+]+)", text)
+    if not h or not t or h.group(1) != kernel_src_hash:
+        return None
+    return float(t.group(1))
+
+
+def kernel_source_hash():
+    import hashlib
+    src = os.path.join(ROOT, "paged_kv_cache_fill_amd", "csrc", "decode_attn.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this path has no "
+              "multi-GPU mode; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import torch
+
+    import paged_kv_cache_fill_amd as pkv
+    import pkv_workloads as W
+
+    pkv.load()
+    idx = WORKLOAD_INDEX[args.workload]
+    lay = W.layout(idx)
+    cfg = lay.cfg
+    S, Hq, Hkv, D, B = lay.num_seqs, cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], 16
+    Dv = cfg["head_dim_v"]
+    fp8 = cfg["k_cache_dtype"] == "fp8"
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    log(f"workload {args.workload}: {S} seqs, {lay.total_tokens} tokens, pool {lay.num_blocks} blocks")
+
+    # ---------------- pools and the population write ----------------
+    lens = lay.seq_lens.astype(np.int64)
+    hist_lens = lens - 1
+    Th = int(hist_lens.sum())
+    kdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
+    k_pool = torch.empty((lay.num_blocks, B, Hkv, D), dtype=kdt, device=dev)
+    v_pool = torch.empty((lay.num_blocks, B, Hkv, Dv), dtype=torch.bfloat16, device=dev)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    seq_lens = torch.from_numpy(lay.seq_lens).to(dev)
+    w = torch.from_numpy(W.norm_weight(idx).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    k_hist = W.device_normal(idx, W.S_K, (Th, Hkv, D), torch.bfloat16, dev, outliers=fp8)
+    v_hist = W.device_normal(idx, W.S_V, (Th, Hkv, Dv), torch.bfloat16, dev)
+    start_h, cu_h, pos_h = W.positions_history(lay)
+    slots_h = torch.empty(Th, dtype=torch.int64, device=dev)
+    pos_h_t = torch.from_numpy(pos_h).to(dev)
+    pkv.fill_slots(slots_h, bt, torch.from_numpy(start_h).to(dev),
+                   torch.from_numpy(cu_h.astype(np.int32)).to(dev), B)
+
+    k_scale = 1.0
+    if fp8:
+        # k_scale = max |stored FP32 K| / 448 over the whole history (the
+        # K path's FP32 output, computed in chunks through the FP32 store)
+        amax = torch.zeros((), dtype=torch.float32, device=dev)
+        chunk = 1 << 16
+        tmp = torch.empty((chunk // B, B, Hkv, D), dtype=torch.float32, device=dev)
+        ident = torch.arange(chunk, dtype=torch.int64, device=dev)
+        for t0 in range(0, Th, chunk):
+            t1 = min(Th, t0 + chunk)
+            pkv.cache_write_k_fused(k_hist[t0:t1], ident[:t1 - t0], tmp, norm_weight=w,
+                                    eps=cfg["eps"], pos_t=pos_h_t[t0:t1], theta=cfg["theta"])
+            amax = torch.maximum(amax, tmp.view(-1)[:(t1 - t0) * Hkv * D].abs().max())
+        k_scale = float(amax.item()) / 448.0
+        del tmp
+        log(f"k_scale = {k_scale:.6g}")
+
+    def populate():
+        pkv.cache_write_k_fused(k_hist, slots_h, k_pool, norm_weight=w, eps=cfg["eps"],
+                                pos_t=pos_h_t, theta=cfg["theta"], k_scale=k_scale)
+
+    def populate_v():
+        pkv.cache_write_v(v_hist, slots_h, v_pool)
+
+    def time_call(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    populate()
+    populate_v()
+    torch.cuda.synchronize()
+    kw_ms = float(np.median(time_call(populate, 5)))
+    vw_ms = float(np.median(time_call(populate_v, 5)))
+    del k_hist, v_hist
+    torch.cuda.empty_cache()
+    kw_bytes = kwrite_bytes(Th, Hkv, D, 2, 1 if fp8 else 2)
+    vw_bytes = vwrite_bytes(Th, Hkv, Dv, 2)
+    log(f"population write: K {kw_ms:.3f} ms ({kw_bytes / kw_ms / 1e6:.0f} GB/s), "
+        f"V {vw_ms:.3f} ms ({vw_bytes / vw_ms / 1e6:.0f} GB/s)")
+
+    # ---------------- the decode step ----------------
+    k_new = W.device_normal(idx, W.S_KNEW, (S, Hkv, D), torch.bfloat16, dev, outliers=fp8)
+    v_new = W.device_normal(idx, W.S_VNEW, (S, Hkv, Dv), torch.bfloat16, dev)
+    q = W.device_normal(idx, W.S_Q, (S, Hq, D), torch.bfloat16, dev, outliers=fp8)
+    start_d, cu_d, pos_d = W.positions_decode(lay)
+    start_d_t = torch.from_numpy(start_d).to(dev)
+    cu_d_t = torch.from_numpy(cu_d.astype(np.int32)).to(dev)
+    pos_d_t = torch.from_numpy(pos_d).to(dev)
+    slots_d = torch.empty(S, dtype=torch.int64, device=dev)
+    out = torch.empty((S, Hq, Dv), dtype=torch.float32, device=dev)
+    ws_n = pkv.decode_workspace_bytes(S, Hq, Hkv, Dv, lay.max_blocks_per_seq, B, args.split_tokens)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+    scale = D ** -0.5
+
+    def step_writes():
+        pkv.fill_slots(slots_d, bt, start_d_t, cu_d_t, B)
+        pkv.cache_write_k_fused(k_new, slots_d, k_pool, norm_weight=w, eps=cfg["eps"],
+                                pos_t=pos_d_t, theta=cfg["theta"], k_scale=k_scale)
+        pkv.cache_write_v(v_new, slots_d, v_pool)
+
+    def step_attn():
+        pkv.paged_decode_attn(q, k_pool, v_pool, bt, seq_lens, scale=scale, k_scale=k_scale,
+                              out=out, split_tokens=args.split_tokens, workspace=ws)
+
+    def step():
+        step_writes()
+        step_attn()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # per-call HIP-event timings on the launch stream
+    attn_ms = float(np.mean(time_call(step_attn, args.steps)))
+    write_ms = float(np.mean(time_call(step_writes, args.steps)))
+    log(f"step {ms_per_step:.3f} ms (decode call {attn_ms:.3f} ms, step writes {write_ms * 1e3:.1f} us)")
+
+    dec_b = decode_bytes(lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 2, 2)
+    step_b = (dec_b + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2) + vwrite_bytes(S, Hkv, Dv, 2)
+              + slots_bytes(S, S))
+    value = step_b / (ms_per_step * 1e-3) / 1e9
+    achieved = dec_b / (attn_ms * 1e-3) / 1e9
+    traffic = traffic_from_profile(kernel_source_hash(), args.workload)
+
+    result = {
+        "metric": "paged decode-attn KV GB/s + cache-write tokens/s (fraction of HBM peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 K / bf16 V, f32 accumulate" if fp8 else "bf16 K/V, f32 accumulate",
+        "data": "synthetic (seeded)",
+        "config": {"workload": args.workload, "num_seqs": S, "seq_len_range": [cfg["len_lo"], cfg["len_hi"]],
+                   "total_tokens": int(lens.sum()), "num_q_heads": Hq, "num_kv_heads": Hkv,
+                   "head_dim": D, "block_size": B, "parallelism": "single GPU"},
+        "decode_attn": {"ms": round(attn_ms, 4), "algorithmic_bytes": dec_b,
+                        "GB_per_s": round(achieved, 1), "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4)},
+        "cache_write": {
+            "population_tokens": Th,
+            "k_fused": {"ms": round(kw_ms, 4), "tokens_per_s": round(Th / kw_ms * 1e3),
+                        "GB_per_s": round(kw_bytes / kw_ms / 1e6, 1),
+                        "frac_of_hbm_peak": round(kw_bytes / kw_ms / 1e6 / HBM_PEAK_GBS, 4)},
+            "v": {"ms": round(vw_ms, 4), "tokens_per_s": round(Th / vw_ms * 1e3),
+                  "GB_per_s": round(vw_bytes / vw_ms / 1e6, 1),
+                  "frac_of_hbm_peak": round(vw_bytes / vw_ms / 1e6 / HBM_PEAK_GBS, 4)},
+            "decode_step_writes_us": round(write_ms * 1e3, 2),
+        },
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "paged_decode_attn (split-K + merge)"},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(idx, lay, k_scale)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(idx, lay, k_scale):
+    """The oracle, as it stands, timed on this host on a bounded sample of the
+    workload: the decode step (slots, K write, V write, attention) of the first
+    sequences, on random pools of the workload's shapes."""
+    import oracle
+    import pkv_workloads as W
+    cores = max(1, min(16, os.cpu_count() or 1))
+    cfg = lay.cfg
+    # sample: leading sequences up to ~150k tokens of history
+    lens = lay.seq_lens.astype(np.int64)
+    n_s = int(np.searchsorted(np.cumsum(lens), 150000)) + 1
+    n_s = max(1, min(n_s, lay.num_seqs))
+    sub = W.layout_for(idx, lay.seq_lens[:n_s])
+    kp, vp = W.random_pools(idx, sub, poison_pad=False)
+    Hq, Hkv, D, Dv = cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], cfg["head_dim_v"]
+    q = W.queries(idx, n_s)
+    k_new = W.kv_tokens(idx, n_s, "k")
+    v_new = W.kv_tokens(idx, n_s, "v")
+    w = W.norm_weight(idx)
+    start, cu, pos = W.positions_decode(sub)
+    fp8 = cfg["k_cache_dtype"] == "fp8"
+    t0 = time.perf_counter()
+    slots = oracle.fill_slots(sub.block_tables, start, cu, n_s, 16)
+    oracle.cache_write_k(k_new, "bf16", slots, kp, cfg["k_cache_dtype"], num_kv_heads=Hkv,
+                         head_dim=D, block_size=16, norm_weight=w, eps=cfg["eps"], pos_t=pos,
+                         theta=cfg["theta"], k_scale=k_scale, nthreads=cores)
+    oracle.cache_write_v(v_new, "bf16", slots, vp, num_kv_heads=Hkv, head_dim_v=Dv, block_size=16)
+    oracle.paged_decode(q, "bf16", kp, cfg["k_cache_dtype"], vp, "bf16", sub.block_tables,
+                        sub.seq_lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D,
+                        head_dim_v=Dv, block_size=16, scale=D ** -0.5, k_scale=k_scale,
+                        nthreads=cores)
+    dt = time.perf_counter() - t0
+    b = (decode_bytes(sub.seq_lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 2, 2)
+         + kwrite_bytes(n_s, Hkv, D, 2, 1 if fp8 else 2) + vwrite_bytes(n_s, Hkv, Dv, 2)
+         + slots_bytes(n_s, n_s))
+    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"decode step of the first {n_s} of {lay.num_seqs} sequences "
+                      f"({int(sub.seq_lens.sum())} tokens of history), {dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

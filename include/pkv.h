@@ -170,12 +170,15 @@ int pkv_cache_write_v(const void* v, pkv_dtype dtype, uint64_t in_token_stride,
 
 /*
  * pkv_decode_workspace_bytes -- bytes of device workspace that
- * pkv_paged_decode_attn needs for these sizes (split-K partial results).
- * 0 means none is needed.  Depends only on the arguments given.
+ * pkv_paged_decode_attn needs for these sizes (split-K partial results:
+ * (head_dim_v + 2) FP32 per sequence, query head and split).  0 means none is
+ * needed.  Depends only on the arguments given; split_tokens as for
+ * pkv_paged_decode_attn.
  */
 size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
                                   uint32_t num_kv_heads, uint32_t head_dim_v,
-                                  uint32_t max_blocks_per_seq, uint32_t block_size);
+                                  uint32_t max_blocks_per_seq, uint32_t block_size,
+                                  uint32_t split_tokens);
 
 /*
  * pkv_paged_decode_attn -- [p1] paged_decode_attn_fp8 and its BF16 sibling
@@ -201,9 +204,14 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *   k_cache       in  [num_blocks, block_size, num_kv_heads, head_dim_qk] of k_dtype
  *   v_cache       in  [num_blocks, block_size, num_kv_heads, head_dim_v] of v_dtype
  *   block_tables  in  int32 [num_seqs, max_blocks_per_seq]
- *   seq_lens      in  int32 [num_seqs], each <= max_blocks_per_seq * block_size
+ *   seq_lens      in  int32 [num_seqs]; tokens past max_blocks_per_seq *
+ *                     block_size are excluded
  *   gate          in  FP32 [num_seqs, num_q_heads, head_dim_v] or NULL
  *   out           out FP32 [num_seqs, num_q_heads, head_dim_v]
+ *   split_tokens  tokens per split-K piece, rounded up to whole blocks and
+ *                 capped at 64 blocks; 0 = the library's choice (enough pieces
+ *                 to cover the GPU several times over).  The result does not
+ *                 depend on it beyond FP32 rounding.
  *   workspace     device scratch of at least
  *                 pkv_decode_workspace_bytes(...) bytes (may be NULL if that is 0)
  * Supported: (q, K, V) dtypes (BF16, BF16, BF16), (BF16, FP8_E4M3, BF16),
@@ -221,7 +229,8 @@ int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_strid
                           uint32_t head_dim_v, uint32_t block_size, float scale,
                           int q_rope, float q_rope_theta, uint32_t q_rope_offset,
                           uint32_t q_rope_dim, const float* gate, float* out,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          uint32_t split_tokens, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 #ifdef __cplusplus
 }

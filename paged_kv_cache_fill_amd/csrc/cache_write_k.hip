@@ -1,0 +1,422 @@
+// cache_write_k.hip -- pkv_cache_write_k_fused: RMSNorm -> RoPE -> one
+// rounding, written into the paged K pool (page 1, kv_cache.rs,
+// fused_k_norm_rope_cache_write_{bf16, bf16_mrope, fp8}: K kept in FP32
+// between the three steps and rounded once at the cache write; page 2,
+// kv_cache_fp8k.rs, module invariants: the FP8 store is k / k_scale as E4M3;
+// page 3, mla_cuda.rs: NoPE skips the rotation).
+//
+// Lane layout.  A (token, kv head) row of D elements is split into 16-byte
+// chunks of VEC elements (8 BF16 or 4 FP32).  A row is owned by L lanes;
+// lane j of the row holds chunks j, j + L, j + 2L, ... (NC chunks).  L is
+// chosen (host side) so that it divides the distance, in chunks, between
+// the two halves of every rotation pair, so both members of every RoPE pair
+// sit in the same lane and the rotation needs no cross-lane exchange.  Each
+// load instruction of a row is L consecutive 16-byte chunks (coalesced).
+// RMSNorm's sum of squares is reduced over the L lanes with xor shuffles.
+//
+// cos/sin of a (token, pair) angle are computed once per wave-unit by one
+// lane and shared through LDS with all rows (kv heads) of the unit, so the
+// transcendental work is per token, not per (token, head).
+#include "pkv_internal.h"
+
+namespace pkv {
+
+enum { IN_BF16 = 0, IN_F32 = 2 };
+enum { OUT_BF16 = 0, OUT_FP8 = 1, OUT_F32 = 2 };
+
+constexpr int kKThreads = 256;
+constexpr int kKWaves = kKThreads / 64;
+constexpr int kMaxHalf = 128;  // rotation pairs per row (rotary_dim <= 256)
+
+struct KWriteArgs {
+    const void* k_in;
+    const void* norm_w;     // NULL: no RMSNorm
+    const int32_t* pos_t;
+    const int32_t* pos_h;   // MRoPE when pos_h and pos_w are both set
+    const int32_t* pos_w;
+    const int64_t* slots;
+    void* k_cache;
+    uint64_t in_stride;     // elements between tokens
+    uint64_t num_slots;
+    uint64_t num_units;     // tokens * units_per_token
+    float eps;
+    float theta;
+    float k_scale;
+    float inv_k_scale;
+    uint32_t D;
+    uint32_t Hkv;
+    uint32_t rope_first;    // first rotated chunk (rope_offset / VEC)
+    uint32_t rope_chunks;   // chunks in the first half of the rotation (R/2/VEC)
+    uint32_t half;          // R/2 (0: no rotation)
+    uint32_t rot_dim;       // R
+    uint32_t L;             // lanes per row (power of two)
+    uint32_t rows_per_wave; // 64 / L
+    uint32_t units_per_token;
+    uint32_t units_per_wave;
+};
+
+template <int IN>
+struct InVec;
+template <>
+struct InVec<IN_BF16> {
+    static constexpr int VEC = 8;
+    __device__ static void load(const void* base, uint64_t elem, float* x)
+    {
+        u32x4 w = load_nt((const u32x4*)((const uint16_t*)base + elem));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = bf16_lo(w[i]);
+            x[2 * i + 1] = bf16_hi(w[i]);
+        }
+    }
+    __device__ static float scalar(const void* base, uint64_t elem)
+    {
+        return __uint_as_float((uint32_t)((const uint16_t*)base)[elem] << 16);
+    }
+};
+template <>
+struct InVec<IN_F32> {
+    static constexpr int VEC = 4;
+    __device__ static void load(const void* base, uint64_t elem, float* x)
+    {
+        u32x4 w = load_nt((const u32x4*)((const float*)base + elem));
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            x[i] = __uint_as_float(w[i]);
+    }
+    __device__ static float scalar(const void* base, uint64_t elem)
+    {
+        return ((const float*)base)[elem];
+    }
+};
+
+// Store VEC FP32 values at element offset `elem` of the cache.
+template <int OUT, int VEC>
+__device__ __forceinline__ void store_chunk(void* cache, uint64_t elem, const float* y,
+                                            float k_scale, float inv_k_scale)
+{
+    if constexpr (OUT == OUT_BF16) {
+        uint32_t w[VEC / 2];
+#pragma unroll
+        for (int i = 0; i < VEC / 2; ++i)
+            w[i] = pack_bf16(y[2 * i], y[2 * i + 1]);
+        uint16_t* p = (uint16_t*)cache + elem;
+        if constexpr (VEC == 8) {
+            store_nt((u32x4*)p, u32x4{w[0], w[1], w[2], w[3]});
+        } else {
+            __builtin_nontemporal_store(u32x2{w[0], w[1]}, (u32x2*)p);
+        }
+    } else if constexpr (OUT == OUT_FP8) {
+        float z[VEC];
+        bool any_nan = false;
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) {
+            // fl32(y / k_scale): product by the reciprocal plus one FMA
+            // correction step (the residual y - q*k_scale is exact).
+            // An infinite q makes the residual NaN (inf - inf): keep q then.
+            // A zero quotient takes q's sign (the residual sum is +0).
+            float q = y[i] * inv_k_scale;
+            float r = __builtin_fmaf(-q, k_scale, y[i]);
+            float v = __builtin_fmaf(r, inv_k_scale, q);
+            v = v == v ? __builtin_copysignf(v, q) : q;
+            // saturate finite and infinite magnitudes to 448; NaN passes
+            v = v > 448.0f ? 448.0f : v;
+            v = v < -448.0f ? -448.0f : v;
+            any_nan |= v != v;
+            z[i] = v;
+        }
+        uint32_t w[VEC / 4];
+#pragma unroll
+        for (int j = 0; j < VEC / 4; ++j)
+            w[j] = pack_e4m3x4(z[4 * j], z[4 * j + 1], z[4 * j + 2], z[4 * j + 3]);
+        if (any_nan) {
+            // NaN is stored as the E4M3FN NaN code S.1111.111 with its sign
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) {
+                if (z[i] != z[i]) {
+                    const uint32_t sh = 8u * (i % 4);
+                    const uint32_t code = 0x7Fu | ((__float_as_uint(z[i]) >> 24) & 0x80u);
+                    w[i / 4] = (w[i / 4] & ~(0xFFu << sh)) | (code << sh);
+                }
+            }
+        }
+        uint8_t* p = (uint8_t*)cache + elem;
+        if constexpr (VEC == 8) {
+            __builtin_nontemporal_store(u32x2{w[0], w[1]}, (u32x2*)p);
+        } else {
+            __builtin_nontemporal_store(w[0], (uint32_t*)p);
+        }
+    } else {
+        float* p = (float*)cache + elem;
+#pragma unroll
+        for (int i = 0; i < VEC; i += 4)
+            store_nt((u32x4*)(p + i), u32x4{__float_as_uint(y[i]), __float_as_uint(y[i + 1]),
+                                            __float_as_uint(y[i + 2]),
+                                            __float_as_uint(y[i + 3])});
+    }
+}
+
+template <int IN, int OUT, int NC>
+__global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(KWriteArgs a)
+{
+    constexpr int VEC = InVec<IN>::VEC;
+    __shared__ float s_cos[kKWaves][kMaxHalf];
+    __shared__ float s_sin[kKWaves][kMaxHalf];
+
+    const uint32_t wave = threadIdx.x / 64;
+    const uint32_t lane = threadIdx.x % 64;
+    const uint32_t rr = lane / a.L;         // row within the wave
+    const uint32_t lir = lane % a.L;        // lane within the row
+
+    // per-lane constants: norm weight of the lane's chunks, inverse frequencies
+    float w[NC][VEC];
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+            w[k][e] = a.norm_w ? InVec<IN>::scalar(a.norm_w, (uint64_t)(lir + a.L * k) * VEC + e)
+                               : 1.0f;
+    // invf_i = fl32(theta^(-2i/R)); lane computes pairs lane and lane + 64
+    float invf0 = 0.f, invf1 = 0.f;
+    if (a.half > 0) {
+        invf0 = (float)pow((double)a.theta, -(2.0 * (double)lane) / (double)a.rot_dim);
+        invf1 = (float)pow((double)a.theta, -(2.0 * (double)(lane + 64)) / (double)a.rot_dim);
+    }
+    const bool mrope = a.pos_h != nullptr && a.pos_w != nullptr;
+    const uint32_t kp = a.half ? a.rope_chunks / a.L : 0;  // chunk-slot distance of a pair
+
+    const uint64_t gwave = (uint64_t)blockIdx.x * kKWaves + wave;
+    const uint64_t u0 = gwave * a.units_per_wave;
+    const uint64_t u1 = u0 + a.units_per_wave < a.num_units ? u0 + a.units_per_wave : a.num_units;
+
+    for (uint64_t u = u0; u < u1; ++u) {
+        const uint64_t t = u / a.units_per_token;
+        const uint32_t grp = (uint32_t)(u % a.units_per_token);
+        const int64_t slot = a.slots[t];
+        if (slot < 0 || (uint64_t)slot >= a.num_slots)
+            continue;                                   // padding slot: no write
+        const uint32_t h = grp * a.rows_per_wave + rr;
+        const bool row_ok = h < a.Hkv;
+
+        float y[NC][VEC];
+        if (row_ok) {
+            const uint64_t src = t * a.in_stride + (uint64_t)h * a.D;
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+                InVec<IN>::load(a.k_in, src + (uint64_t)(lir + a.L * k) * VEC, y[k]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    y[k][e] = 0.f;
+        }
+
+        // angles of this token, one (token, pair) per lane, shared via LDS
+        if (a.half > 0) {
+#pragma unroll
+            for (int rep = 0; rep < 2; ++rep) {
+                const uint32_t i = lane + 64u * rep;
+                if (i < a.half) {
+                    int32_t p = a.pos_t[t];
+                    if (mrope) {
+                        const uint32_t ax = i % 3u;
+                        p = ax == 0 ? p : ax == 1 ? a.pos_h[t] : a.pos_w[t];
+                    }
+                    const float ang = (float)p * (rep ? invf1 : invf0);
+                    float sn, cs;
+                    sincosf(ang, &sn, &cs);
+                    s_cos[wave][i] = cs;
+                    s_sin[wave][i] = sn;
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+
+        if (a.norm_w) {
+            float ss = 0.f;
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    ss = __builtin_fmaf(y[k][e], y[k][e], ss);
+            for (uint32_t m = 1; m < a.L; m <<= 1)
+                ss += __shfl_xor(ss, (int)m, 64);
+            const float r = rsqrtf(ss / (float)a.D + a.eps);
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    y[k][e] = y[k][e] * r * w[k][e];
+        }
+
+        if (a.half > 0) {
+#pragma unroll
+            for (int k = 0; k < NC; ++k) {
+                const uint32_t ci = lir + a.L * k;
+                if (ci >= a.rope_first && ci < a.rope_first + a.rope_chunks) {
+                    const uint32_t i0 = (ci - a.rope_first) * VEC;
+                    // partner chunk slot k + kp (kp >= 1 by construction)
+#pragma unroll
+                    for (int k2 = k + 1; k2 < NC; ++k2) {
+                        if ((uint32_t)(k2 - k) == kp) {
+#pragma unroll
+                            for (int e = 0; e < VEC; ++e) {
+                                const float cs = s_cos[wave][i0 + e];
+                                const float sn = s_sin[wave][i0 + e];
+                                const float x0 = y[k][e], x1 = y[k2][e];
+                                y[k][e] = x0 * cs - x1 * sn;
+                                y[k2][e] = x1 * cs + x0 * sn;
+                            }
+                        }
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+
+        if (row_ok) {
+            const uint64_t dst = ((uint64_t)slot * a.Hkv + h) * a.D;
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+                store_chunk<OUT, VEC>(a.k_cache, dst + (uint64_t)(lir + a.L * k) * VEC, y[k],
+                                      a.k_scale, a.inv_k_scale);
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host
+
+template <int IN, int OUT>
+static bool launch_nc(int nc, dim3 grid, hipStream_t st, const KWriteArgs& a)
+{
+    switch (nc) {
+    case 1: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 1>), grid, dim3(kKThreads), 0, st, a); return true;
+    case 2: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 2>), grid, dim3(kKThreads), 0, st, a); return true;
+    case 3: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 3>), grid, dim3(kKThreads), 0, st, a); return true;
+    case 4: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 4>), grid, dim3(kKThreads), 0, st, a); return true;
+    case 6: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 6>), grid, dim3(kKThreads), 0, st, a); return true;
+    case 8: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 8>), grid, dim3(kKThreads), 0, st, a); return true;
+    default: return false;
+    }
+}
+
+template <int IN>
+static bool launch_out(pkv_dtype out, int nc, dim3 grid, hipStream_t st, const KWriteArgs& a)
+{
+    switch (out) {
+    case PKV_BF16: return launch_nc<IN, OUT_BF16>(nc, grid, st, a);
+    case PKV_FP8_E4M3: return launch_nc<IN, OUT_FP8>(nc, grid, st, a);
+    default: return launch_nc<IN, OUT_F32>(nc, grid, st, a);
+    }
+}
+
+}  // namespace pkv
+
+extern "C" int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype,
+                                       uint64_t in_token_stride, const void* norm_weight,
+                                       float rms_eps, const int32_t* pos_t, const int32_t* pos_h,
+                                       const int32_t* pos_w, float theta, uint32_t rope_offset,
+                                       uint32_t rotary_dim, int nope,
+                                       const int64_t* slot_mapping, uint32_t num_tokens,
+                                       uint32_t num_kv_heads, uint32_t head_dim,
+                                       uint32_t block_size, uint32_t num_blocks, void* k_cache,
+                                       pkv_dtype cache_dtype, float k_scale, void* stream)
+{
+    using namespace pkv;
+    clear_error();
+    if (num_tokens == 0)
+        return PKV_OK;
+    if (!k_in || !slot_mapping || !k_cache)
+        return fail(PKV_ERR_INVALID, "cache_write_k_fused: k_in, slot_mapping and k_cache must be non-NULL");
+    if (!valid_dtype(in_dtype) || !valid_dtype(cache_dtype))
+        return fail(PKV_ERR_INVALID, "cache_write_k_fused: bad dtype");
+    if (in_dtype != PKV_BF16 && in_dtype != PKV_FP32)
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_k_fused: in_dtype must be BF16 or FP32");
+    if (num_kv_heads == 0 || head_dim == 0 || block_size == 0 || num_blocks == 0)
+        return fail(PKV_ERR_INVALID, "cache_write_k_fused: zero dimension");
+    if (head_dim != 64 && head_dim != 128 && head_dim != 192 && head_dim != 256)
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_k_fused: head_dim %u not in {64,128,192,256}", head_dim);
+    const uint64_t row = (uint64_t)num_kv_heads * head_dim;
+    if (in_token_stride < row)
+        return fail(PKV_ERR_INVALID, "cache_write_k_fused: in_token_stride smaller than a token row");
+    const uint32_t es = (uint32_t)dtype_size(in_dtype);
+    const uint32_t VEC = 16 / es;
+    if ((in_token_stride * es) % 16 || !aligned16(k_in) || !aligned16(k_cache))
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_k_fused: k_in/k_cache and the token stride must be 16-byte aligned");
+    if (cache_dtype == PKV_FP8_E4M3 && !(k_scale > 0.0f && k_scale < INFINITY))
+        return fail(PKV_ERR_INVALID, "cache_write_k_fused: k_scale must be finite and > 0");
+    const bool rope = !nope && rotary_dim > 0;
+    if (rope) {
+        if (!pos_t)
+            return fail(PKV_ERR_INVALID, "cache_write_k_fused: pos_t must be non-NULL when rotating");
+        if ((pos_h == nullptr) != (pos_w == nullptr))
+            return fail(PKV_ERR_INVALID, "cache_write_k_fused: pos_h and pos_w must be both set or both NULL");
+        if (rotary_dim % 2 || (uint64_t)rope_offset + rotary_dim > head_dim)
+            return fail(PKV_ERR_INVALID, "cache_write_k_fused: rotary_dim must be even and rope_offset + rotary_dim <= head_dim");
+        if (rotary_dim / 2 > (uint32_t)kMaxHalf)
+            return fail(PKV_ERR_UNSUPPORTED, "cache_write_k_fused: rotary_dim above 256");
+        if (rope_offset % VEC || (rotary_dim / 2) % VEC)
+            return fail(PKV_ERR_UNSUPPORTED, "cache_write_k_fused: rope_offset and rotary_dim/2 must be multiples of %u", VEC);
+    }
+    // lanes per row: the largest power of two <= 16 that divides the row's
+    // chunk count and (when rotating) the pair distance in chunks, leaving a
+    // supported number of chunks per lane
+    const uint32_t chunks = head_dim / VEC;
+    const uint32_t pair = rope ? (rotary_dim / 2) / VEC : 0;
+    uint32_t L = 0, NC = 0;
+    for (uint32_t l = 16; l >= 1; l >>= 1) {
+        if (chunks % l || (rope && pair % l))
+            continue;
+        uint32_t nc = chunks / l;
+        if (nc == 1 || nc == 2 || nc == 3 || nc == 4 || nc == 6 || nc == 8) {
+            if (rope && nc < 2)
+                continue;
+            L = l;
+            NC = nc;
+            break;
+        }
+    }
+    if (L == 0)
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_k_fused: no lane layout for head_dim %u rotary_dim %u", head_dim, rotary_dim);
+
+    KWriteArgs a{};
+    a.k_in = k_in;
+    a.norm_w = norm_weight;
+    a.pos_t = pos_t;
+    a.pos_h = pos_h;
+    a.pos_w = pos_w;
+    a.slots = slot_mapping;
+    a.k_cache = k_cache;
+    a.in_stride = in_token_stride;
+    a.num_slots = (uint64_t)num_blocks * block_size;
+    a.eps = rms_eps;
+    a.theta = theta;
+    a.k_scale = k_scale;
+    a.inv_k_scale = cache_dtype == PKV_FP8_E4M3 ? 1.0f / k_scale : 1.0f;
+    a.D = head_dim;
+    a.Hkv = num_kv_heads;
+    a.rope_first = rope ? rope_offset / VEC : 0;
+    a.rope_chunks = pair;
+    a.half = rope ? rotary_dim / 2 : 0;
+    a.rot_dim = rope ? rotary_dim : 1;
+    a.L = L;
+    a.rows_per_wave = 64 / L;
+    a.units_per_token = ceil_div(num_kv_heads, a.rows_per_wave);
+    a.num_units = (uint64_t)num_tokens * a.units_per_token;
+    // a few units per wave: enough waves to fill 256 CUs many times over
+    const uint64_t target_waves = 256ull * 32;
+    uint64_t upw = a.num_units / target_waves;
+    upw = upw < 1 ? 1 : upw > 8 ? 8 : upw;
+    a.units_per_wave = (uint32_t)upw;
+    const uint64_t waves = (a.num_units + upw - 1) / upw;
+    const uint64_t blocks = (waves + kKWaves - 1) / kKWaves;
+    const dim3 grid((uint32_t)blocks);
+    hipStream_t st = (hipStream_t)stream;
+    bool ok = in_dtype == PKV_BF16 ? launch_out<IN_BF16>(cache_dtype, (int)NC, grid, st, a)
+                                   : launch_out<IN_F32>(cache_dtype, (int)NC, grid, st, a);
+    if (!ok)
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_k_fused: chunk count %u per lane", NC);
+    return check_launch("cache_write_k_fused");
+}

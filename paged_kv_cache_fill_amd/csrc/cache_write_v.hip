@@ -1,0 +1,95 @@
+// cache_write_v.hip -- pkv_cache_write_v: the V reshape-and-cache copy
+// (page 1, kv_cache.rs, reshape_and_cache_flash_v_only: V rows copied into
+// the paged V pool at slot_mapping, leaving the K side to the fused K write).
+//
+// A token's V row (num_kv_heads * head_dim_v elements) is contiguous in the
+// input and, under the [num_blocks, block_size, Hkv, Dv] layout, contiguous
+// at its slot in the pool.  So the copy is a row gather/scatter in 16-byte
+// pieces: each thread owns one 16-byte column of the row and walks a run of
+// tokens, issuing all of a run's loads before its stores so that several
+// kilobytes per wave are in flight.  Both sides are touched once: loads and
+// stores are non-temporal.
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int kVThreads = 256;
+constexpr int kVRun = 4;  // tokens per thread per pass (loads in flight)
+
+// cols = row bytes / 16; tpb = tokens handled side by side by one block
+// (kVThreads / cols when a row fits in a block, else 1 with a column loop).
+__global__ __launch_bounds__(kVThreads) void cache_write_v_kernel(
+    const u32x4* __restrict__ v, uint64_t in_stride16, const int64_t* __restrict__ slots,
+    uint32_t num_tokens, uint32_t cols, uint32_t tpb, uint64_t num_slots,
+    u32x4* __restrict__ cache)
+{
+    const uint32_t lane_tok = threadIdx.x / cols;       // which token of the block's group
+    const uint32_t col0 = threadIdx.x % cols;
+    if (lane_tok >= tpb)
+        return;
+    const uint32_t col_step = cols < kVThreads ? cols : kVThreads;  // columns per pass
+    // Token runs: block b handles tokens [b * tpb * kVRun, (b+1) * tpb * kVRun),
+    // token = base + r * tpb + lane_tok.
+    const uint64_t base = (uint64_t)blockIdx.x * tpb * kVRun;
+    int64_t slot[kVRun];
+    uint64_t tok[kVRun];
+#pragma unroll
+    for (int r = 0; r < kVRun; ++r) {
+        tok[r] = base + (uint64_t)r * tpb + lane_tok;
+        int64_t s = tok[r] < num_tokens ? slots[tok[r]] : -1;
+        slot[r] = (s >= 0 && (uint64_t)s < num_slots) ? s : -1;
+    }
+    for (uint32_t c = col0; c < cols; c += col_step) {
+        u32x4 buf[kVRun];
+#pragma unroll
+        for (int r = 0; r < kVRun; ++r)
+            if (slot[r] >= 0)
+                buf[r] = load_nt(v + tok[r] * in_stride16 + c);
+#pragma unroll
+        for (int r = 0; r < kVRun; ++r)
+            if (slot[r] >= 0)
+                store_nt(cache + (uint64_t)slot[r] * cols + c, buf[r]);
+    }
+}
+
+}  // namespace pkv
+
+extern "C" int pkv_cache_write_v(const void* v, pkv_dtype dtype, uint64_t in_token_stride,
+                                 const int64_t* slot_mapping, uint32_t num_tokens,
+                                 uint32_t num_kv_heads, uint32_t head_dim_v, uint32_t block_size,
+                                 uint32_t num_blocks, void* v_cache, void* stream)
+{
+    using namespace pkv;
+    clear_error();
+    if (num_tokens == 0)
+        return PKV_OK;
+    if (!v || !slot_mapping || !v_cache)
+        return fail(PKV_ERR_INVALID, "cache_write_v: v, slot_mapping and v_cache must be non-NULL");
+    if (!valid_dtype(dtype))
+        return fail(PKV_ERR_INVALID, "cache_write_v: bad dtype %d", (int)dtype);
+    if (dtype != PKV_BF16 && dtype != PKV_FP32)
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: dtype must be BF16 or FP32");
+    if (num_kv_heads == 0 || head_dim_v == 0 || block_size == 0 || num_blocks == 0)
+        return fail(PKV_ERR_INVALID, "cache_write_v: zero dimension");
+    const uint64_t row_elems = (uint64_t)num_kv_heads * head_dim_v;
+    const uint64_t row_bytes = row_elems * dtype_size(dtype);
+    if (in_token_stride < row_elems)
+        return fail(PKV_ERR_INVALID, "cache_write_v: in_token_stride %llu < row of %llu elements",
+                    (unsigned long long)in_token_stride, (unsigned long long)row_elems);
+    const uint64_t stride_bytes = in_token_stride * dtype_size(dtype);
+    if (row_bytes % 16 || stride_bytes % 16 || !aligned16(v) || !aligned16(v_cache))
+        return fail(PKV_ERR_UNSUPPORTED,
+                    "cache_write_v: rows, strides and pointers must be 16-byte aligned");
+    const uint64_t cols64 = row_bytes / 16;
+    if (cols64 > (1u << 24))
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: row too long");
+    const uint32_t cols = (uint32_t)cols64;
+    const uint32_t tpb = cols <= (uint32_t)kVThreads ? (uint32_t)kVThreads / cols : 1u;
+    const uint64_t per_block = (uint64_t)tpb * kVRun;
+    const uint64_t blocks = (num_tokens + per_block - 1) / per_block;
+    hipLaunchKernelGGL(cache_write_v_kernel, dim3((uint32_t)blocks), dim3(kVThreads), 0,
+                       (hipStream_t)stream, (const u32x4*)v, stride_bytes / 16, slot_mapping,
+                       num_tokens, cols, tpb, (uint64_t)num_blocks * block_size,
+                       (u32x4*)v_cache);
+    return check_launch("cache_write_v");
+}

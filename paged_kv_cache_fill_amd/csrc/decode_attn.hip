@@ -1,0 +1,833 @@
+// decode_attn.hip -- pkv_paged_decode_attn: one-query-token paged decode
+// attention with GQA, split-K over the token range and a log-sum-exp merge
+// (page 1, kv_cache.rs, paged_decode_attn_fp8 and its BF16 sibling: Q, K/V
+// pools, block_tables i32, seq_lens i32, num_q_heads / num_kv_heads,
+// inv_sqrt_d, k_scale; page 3, mla_cuda.rs: RoPE on q then SDPA + gate).
+//
+// Work decomposition.  A work-group handles one (sequence, split) pair for
+// a group of kv heads, one wavefront per kv head; a split is `chunk_blocks`
+// consecutive cache blocks of the sequence.  The work-group's waves read
+// neighbouring rows of the same pool blocks, so together they stream whole
+// blocks ([block_size, Hkv, D] is contiguous).  Every query head of a kv
+// head's GQA group is served by the same wave from the same K/V registers:
+// K and V are read from HBM exactly once.
+//
+// BF16 / FP8-K caches (MFMA path).  Per 16-token cache block a wave computes
+//   S^T[t, g] = K[t, :] . q[g, :]    v_mfma_f32_16x16x32_bf16  (M=t, N=g)
+//   O[g, d]  += P[g, t] V[t, d]      v_mfma_f32_16x16x16_bf16  (M=g, N=d)
+// The S^T accumulator layout (lane = t-group x g) is exactly the A-operand
+// layout of the PV product, so softmax weights never leave their lanes.  The
+// head dimension is permuted consistently on q and K so that every lane
+// loads 16 contiguous bytes; V's columns are permuted so that a lane's 16-byte
+// load feeds all eight N-tiles.  P is split into hi + lo BF16 parts (two PV
+// MFMAs), which keeps the weights to ~16 bits; BF16 q x BF16 (or E4M3) K
+// products are exact in FP32.  Online softmax runs in the log2 domain.
+//
+// FP32 caches (VALU path).  Four tokens per wave step (16 lanes per token
+// row, 16-byte loads), one online-softmax stream per row, merged at the end.
+#include "pkv_internal.h"
+
+namespace pkv {
+
+constexpr int kBS = 16;                 // tokens per cache block
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBufferFlags = 0x00020000; // buffer resource word 3: raw 32-bit dwords
+constexpr int kNT = 2;                   // cache policy of streaming loads: non-temporal
+
+// Launch shape of the MFMA path.
+constexpr uint32_t kKvPerGroup = 2;     // kv heads (waves) per work-group, at most
+constexpr int kPrefetch = 1;            // cache blocks loaded ahead of the one in use
+constexpr uint64_t kTargetGroups = 2048;// (sequence, split, kv group) work-groups wanted
+constexpr uint32_t kMinChunk = 4;       // blocks per split, automatic choice: at least
+constexpr uint32_t kMaxChunk = 128;     // ... and at most (two table entries per lane)
+
+struct DecodeArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* bt;
+    const int32_t* seq_lens;
+    const float* gate;
+    float* out;
+    float* part_o;          // [S][max_splits][Hq][Dv]
+    float* part_ml;         // [S][max_splits][Hq][2]  (max in log2 units, sum)
+    uint64_t q_stride;      // elements between sequences
+    uint32_t M;             // max_blocks_per_seq
+    uint32_t num_blocks;
+    uint32_t Hq, Hkv, G;
+    uint32_t chunk_blocks;
+    uint32_t max_splits;
+    float qk_scale;         // scale * log2(e) (* k_scale for E4M3 K)
+    // query rotation (FP32 path)
+    uint32_t q_rope;
+    float q_rope_theta;
+    uint32_t q_rope_offset;
+    uint32_t q_rope_dim;
+};
+
+// ------------------------------------------------------------------ helpers
+
+// Cache blocks of a sequence of n tokens that the table can address; tokens
+// whose block index is past the table are excluded.
+__device__ __forceinline__ uint32_t seq_blocks(int32_t n, uint32_t M)
+{
+    const uint32_t nb = n > 0 ? ((uint32_t)n + kBS - 1) / kBS : 0;
+    return nb < M ? nb : M;
+}
+
+__device__ __forceinline__ float wave_max_xor16_32(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16, 64));
+    v = fmaxf(v, __shfl_xor(v, 32, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum_xor16_32(float v)
+{
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// bytes 2,3 of lo and 2,3 of hi -> one word (two BF16 from two FP32)
+__device__ __forceinline__ uint32_t hi16_pair(uint32_t lo, uint32_t hi)
+{
+    return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
+}
+// low halves of lo and hi -> one word
+__device__ __forceinline__ uint32_t lo16_pair(uint32_t lo, uint32_t hi)
+{
+    return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// Writes the finished (single-split) or partial result of one wave.
+// o[nt][r]: row g = 4*(lane/16) + r of the GQA group, column d = DPL*(lane%16) + nt.
+template <int DV>
+__device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint32_t kvh,
+                                          uint32_t split, uint32_t nsplit, int lane,
+                                          const f32x4 (&o)[DV / 16], float m, float l)
+{
+    constexpr int NT = DV / 16, DPL = DV / 16;
+    const int kg = lane >> 4, n = lane & 15;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t g = 4 * kg + r;
+        const float lg = __shfl(l, (int)g, 64);
+        const float mg = __shfl(m, (int)g, 64);
+        if (g >= a.G)
+            continue;
+        const uint32_t h = kvh * a.G + g;
+        float vals[NT];
+        if (nsplit == 1) {
+            const float inv = lg > 0.f ? 1.0f / lg : 0.f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                vals[nt] = o[nt][r] * inv;
+            const uint64_t base = ((uint64_t)s * a.Hq + h) * DV + (uint64_t)DPL * n;
+            if (a.gate) {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    vals[nt] *= a.gate[base + nt];
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; nt += 4)
+                *(f32x4*)(a.out + base + nt) = f32x4{vals[nt], vals[nt + 1], vals[nt + 2], vals[nt + 3]};
+        } else {
+            const uint64_t prow = ((uint64_t)s * a.max_splits + split) * a.Hq + h;
+            const uint64_t base = prow * DV + (uint64_t)DPL * n;
+#pragma unroll
+            for (int nt = 0; nt < NT; nt += 4)
+                *(f32x4*)(a.part_o + base + nt) = f32x4{o[nt][r], o[nt + 1][r], o[nt + 2][r], o[nt + 3][r]};
+            if (n == 0)
+                *(f32x2*)(a.part_ml + prow * 2) = f32x2{mg, lg};
+        }
+    }
+}
+
+// ------------------------------------------------------------------ MFMA path
+
+// KT: 0 = BF16 K, 1 = E4M3 K.  D: head dim of q, K and V (64 or 128).
+//
+// K reaches the MFMA in two steps.  (1) Coalesced loads: a K row of one head
+// is CPR 16-byte chunks; load j of a lane covers row j * (64 / CPR) + lane /
+// CPR, chunk lane % CPR, so each load instruction reads whole rows.  (2) A
+// wave-private LDS tile [16 rows][CPR chunks] turns that into the MFMA
+// operand layout (lane = token row ln, chunk group kg).  Chunk c of row r is
+// stored at position c ^ swz(r), which makes both the row-wise writes and the
+// column-wise operand reads free of bank conflicts.
+template <int KT, int D>
+struct KFrag {
+    static constexpr int KES = KT == 0 ? 2 : 1;      // K element bytes
+    static constexpr int CPR = D * KES / 16;         // 16-byte chunks per row
+    static constexpr int RPL = 64 / CPR;             // rows per load instruction
+    static constexpr int NL = 16 / RPL;              // loads (and LDS chunks) per lane
+    static constexpr int NI = D / 32;                // MFMAs over the head dim (16x16x32)
+    static constexpr int RP = 16 / CPR;              // rows per 256-byte LDS line
+    __device__ static uint32_t swz(uint32_t row) { return (row / RP) & (CPR - 1); }
+    // LDS byte offset of chunk c of row r
+    __device__ static uint32_t lds_off(uint32_t r, uint32_t c) { return (r * CPR + (c ^ swz(r))) * 16; }
+    // physical element of logical k = 8*kg + r of MFMA i (same permutation on q)
+    __device__ static uint32_t phys(int i, int kg)
+    {
+        return KT == 0 ? 32u * i + 8u * kg : 64u * (i / 2) + 16u * kg + 8u * (i % 2);
+    }
+    // chunk holding the operand of MFMA i (BF16) or MFMAs 2i, 2i+1 (E4M3) for group kg
+    __device__ static uint32_t op_chunk(int j, int kg) { return 4u * j + kg; }
+    // MFMA operand i (8 BF16) from the operand chunks w[]
+    __device__ static bf16x8 operand(const u32x4 (&w)[NL], int i)
+    {
+        if constexpr (KT == 0) {
+            return __builtin_bit_cast(bf16x8, w[i]);
+        } else {
+            const u32x4 src = w[i / 2];
+            const int base = (i % 2) * 2;     // words base, base+1 hold 8 codes
+            u32x4 r;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t word = src[base + q];
+                f32x2 a = unpack_e4m3x2(word, false);
+                f32x2 b = unpack_e4m3x2(word, true);
+                // E4M3 values are exact in BF16: keep the upper halves
+                r[2 * q] = hi16_pair(__float_as_uint(a.x), __float_as_uint(a.y));
+                r[2 * q + 1] = hi16_pair(__float_as_uint(b.x), __float_as_uint(b.y));
+            }
+            return __builtin_bit_cast(bf16x8, r);
+        }
+    }
+};
+
+template <int KT, int D, int PF>
+__global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t kv_groups)
+{
+    using KF = KFrag<KT, D>;
+    constexpr int NI = KF::NI, NL = KF::NL;
+    __shared__ u32x4 s_k[8][16 * KF::CPR];          // one K tile per wave
+    constexpr int NT = D / 16;                 // PV N-tiles
+    constexpr int DPL = D / 16;                // V dims per lane
+    constexpr int VW = DPL / 2;                // V words per lane per token (4 or 2)
+    constexpr uint32_t KES = KT == 0 ? 2 : 1;  // K element bytes
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int kg = lane >> 4;                  // 0..3
+    const int ln = lane & 15;
+    // Dispatch order is split-major: x = sequence * kv_groups + kv group,
+    // y = split.  Work-groups are dealt to the XCDs round-robin by linear id,
+    // so each split "layer" spreads the sequences that reach it evenly over
+    // the XCDs (a sequence-major order would pile the always-present early
+    // splits onto the same XCDs).  The kv groups of one (sequence, split) are
+    // neighbours, so they stream the same cache blocks at about the same time.
+    const uint32_t split = blockIdx.y;
+    const uint32_t s = blockIdx.x / kv_groups;
+    const uint32_t kvh = (blockIdx.x % kv_groups) * (blockDim.x >> 6) + wave;
+    if (kvh >= a.Hkv)
+        return;
+
+    const int32_t n = a.seq_lens[s];
+    const uint32_t nblk = seq_blocks(n, a.M);
+    const uint32_t b0 = split * a.chunk_blocks;
+    if (b0 >= nblk) {
+        if (n <= 0 && split == 0) {
+            // empty sequence: zero output rows of this kv head's group
+            for (uint32_t idx = lane; idx < a.G * D; idx += 64)
+                a.out[((uint64_t)s * a.Hq + kvh * a.G) * D + idx] = 0.f;
+        }
+        return;
+    }
+    const uint32_t b1 = min(b0 + a.chunk_blocks, nblk);
+    const uint32_t nsplit = (nblk + a.chunk_blocks - 1) / a.chunk_blocks;
+
+    // q fragments: B operand of S^T = K q^T; lane (g = ln, kg)
+    bf16x8 qf[NI];
+    {
+        const uint32_t g = ln;
+        const uint16_t* qrow = (const uint16_t*)a.q + (uint64_t)s * a.q_stride +
+                               (uint64_t)(kvh * a.G + g) * D;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            u32x4 w = u32x4{0u, 0u, 0u, 0u};
+            if (g < a.G)
+                w = *(const u32x4*)(qrow + KF::phys(i, kg));
+            qf[i] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    // block-table entries of this split, two per lane (chunk_blocks <= 128):
+    // entry i is lane i % 64 of bt_lane[i / 64]; lanes past the split re-read
+    // its last entry, so the loads are unconditional
+    int32_t bt_lane[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t idx = b0 + 64 * h + lane;
+        bt_lane[h] = a.bt[(uint64_t)s * a.M + (idx < b1 ? idx : b1 - 1)];
+    }
+    auto table_entry = [&](uint32_t i) -> int32_t {
+        return i < 64 ? __builtin_amdgcn_readlane(bt_lane[0], (int)i)
+                      : __builtin_amdgcn_readlane(bt_lane[1], (int)(i - 64));
+    };
+
+    const uint8_t* kbase = (const uint8_t*)a.k_cache;
+    const uint16_t* vbase = (const uint16_t*)a.v_cache;
+    const uint64_t krow_stride = (uint64_t)a.Hkv * D * KES;   // bytes per cache row
+    const uint64_t vrow_stride = (uint64_t)a.Hkv * D;         // elements per cache row
+
+    f32x4 o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    struct Stage {
+        u32x4 k[NL];
+        uint32_t v[4][VW];
+    };
+
+    // Addresses: the block id is wave-uniform, so each block gets a buffer
+    // resource built in scalar registers (its record count bounds every access
+    // to that block); each lane's byte offsets inside a block are
+    // loop-invariant 32-bit values.
+    const uint32_t kblk_bytes = (uint32_t)(kBS * krow_stride);
+    const uint32_t vblk_bytes = (uint32_t)(kBS * vrow_stride * 2);
+    const uint32_t koff = (uint32_t)((lane / KF::CPR) * krow_stride + (uint64_t)kvh * D * KES +
+                                     16 * (lane % KF::CPR));
+    const uint32_t kstep = (uint32_t)(KF::RPL * krow_stride);     // next load: RPL rows down
+    // LDS positions: written chunk of load j, operand chunk of MFMA group j
+    uint32_t lds_w[NL], lds_r[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        lds_w[j] = KF::lds_off(j * KF::RPL + lane / KF::CPR, lane % KF::CPR);
+        lds_r[j] = KF::lds_off(ln, KF::op_chunk(j, kg));
+    }
+    uint8_t* ktile = (uint8_t*)&s_k[wave][0];
+    const uint32_t voff = (uint32_t)((4 * kg) * vrow_stride * 2 + ((uint64_t)kvh * D + DPL * ln) * 2);
+    const uint32_t vrow_bytes = (uint32_t)(vrow_stride * 2);
+
+    // An unmapped block is read from block 0 instead (always inside the pool):
+    // compute_block masks all of its tokens, so what it holds never counts.
+    auto load_block = [&](uint32_t bi, Stage& st) {
+        int32_t pb = table_entry(bi - b0);
+        pb = (pb >= 0 && (uint32_t)pb < a.num_blocks) ? pb : 0;
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kbase + (uint64_t)pb * kblk_bytes), 0, (int)kblk_bytes, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((const uint8_t*)vbase + (uint64_t)pb * vblk_bytes), 0, (int)vblk_bytes, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {                                    // K: token t = ln
+            const u32x4 w = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff, j * kstep, kNT));
+            st.k[j] = w;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {                                     // V: t = 4kg + r
+            if constexpr (VW == 4) {
+                const u32x4 t4 = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, r * vrow_bytes, kNT));
+                st.v[r][0] = t4[0]; st.v[r][1] = t4[1]; st.v[r][2] = t4[2]; st.v[r][3] = t4[3];
+            } else {
+                const u32x2 t2 = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr, voff, r * vrow_bytes, kNT));
+                st.v[r][0] = t2[0]; st.v[r][1] = t2[1];
+            }
+        }
+    };
+
+    auto compute_block = [&](uint32_t bi, Stage& st) {
+        const int32_t pb = table_entry(bi - b0);
+        const bool blk_ok = pb >= 0 && (uint32_t)pb < a.num_blocks;
+        const int32_t rem = n - (int32_t)(bi * kBS);
+        const int ntok = blk_ok ? (rem < kBS ? rem : kBS) : 0;
+
+        // K rows -> MFMA operand layout through the wave's LDS tile (lanes
+        // exchange data: order the writes after the previous block's reads
+        // and before this block's reads, at wavefront scope)
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            *(u32x4*)(ktile + lds_w[j]) = st.k[j];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        u32x4 kop[NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            kop[j] = *(const u32x4*)(ktile + lds_r[j]);
+
+        // S^T = K q^T : lane holds S[t = 4kg + r][g = ln]
+        f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KF::operand(kop, i), qf[i], sacc, 0, 0, 0);
+
+        float sv[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = 4 * kg + r;
+            sv[r] = t < ntok ? sacc[r] * a.qk_scale : -INFINITY;
+            mx = fmaxf(mx, sv[r]);
+        }
+        mx = wave_max_xor16_32(mx);
+        const float m_new = fmaxf(m, mx);
+        // while no token has counted yet (m_new = -inf) use 0 as the reference:
+        // masked scores give p = 0, and alpha = 0 leaves the zero state zero
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            p[r] = __builtin_amdgcn_exp2f(sv[r] - m_ref);
+        l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+        m = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+            // O rows are g = 4kg + r; their factor lives in lane g
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * kg + r, 64);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    o[nt][r] *= ar;
+            }
+        }
+
+        // P as hi + lo BF16 (A operand: lane holds P[g = ln][t = 4kg + r])
+        uint32_t ph[2], pl[2];
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+            const uint32_t hw = pack_bf16(p[2 * r2], p[2 * r2 + 1]);
+            ph[r2] = hw;
+            pl[r2] = pack_bf16(p[2 * r2] - bf16_lo(hw), p[2 * r2 + 1] - bf16_hi(hw));
+        }
+        const i16x4 a_hi = __builtin_bit_cast(i16x4, u32x2{ph[0], ph[1]});
+        const i16x4 a_lo = __builtin_bit_cast(i16x4, u32x2{pl[0], pl[1]});
+
+        // tokens past the sequence end must not bring NaN/Inf into 0 * V
+        if (ntok < kBS) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * kg + r >= ntok)
+#pragma unroll
+                    for (int w = 0; w < VW; ++w)
+                        st.v[r][w] = 0u;
+        }
+
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int w = nt >> 1;
+            uint32_t b01, b23;
+            if (nt & 1) {
+                b01 = hi16_pair(st.v[0][w], st.v[1][w]);
+                b23 = hi16_pair(st.v[2][w], st.v[3][w]);
+            } else {
+                b01 = lo16_pair(st.v[0][w], st.v[1][w]);
+                b23 = lo16_pair(st.v[2][w], st.v[3][w]);
+            }
+            const i16x4 bv = __builtin_bit_cast(i16x4, u32x2{b01, b23});
+            o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bv, o[nt], 0, 0, 0);
+            o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_lo, bv, o[nt], 0, 0, 0);
+        }
+    };
+
+    // Ring of PF + 1 register stages; block b lives in stage (b - b0) % NS.
+    // The main loop prefetches unconditionally (every block it handles has a
+    // block PF ahead), so the compiler's wait before each compute covers only
+    // the stage in use; the tail handles the last blocks with conditional
+    // prefetch.  The prologue clamps to the last block instead of branching.
+    constexpr int NS = PF + 1;
+    Stage st[NS];
+#pragma unroll
+    for (int f = 0; f < PF; ++f)
+        load_block(b0 + f < b1 ? b0 + f : b1 - 1, st[f]);
+    uint32_t bi = b0;
+    for (; bi + NS + PF - 1 < b1; bi += NS) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            load_block(bi + u + PF, st[(u + PF) % NS]);
+            compute_block(bi + u, st[u]);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NS + PF - 1; ++u) {
+        const uint32_t b = bi + u;
+        if (b >= b1)
+            break;
+        if (b + PF < b1)
+            load_block(b + PF, st[(u + PF) % NS]);
+        compute_block(b, st[u % NS]);
+    }
+
+    l = wave_sum_xor16_32(l);
+    emit_mfma<D>(a, s, kvh, split, nsplit, lane, o, m, l);
+}
+
+// ------------------------------------------------------------------ FP32 path
+
+template <int DQK, int DV, int G>
+__global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
+{
+    constexpr int JK = DQK / 64;               // float4 loads of K per lane
+    constexpr int JV = DV / 64;                // float4 loads of V per lane
+    __shared__ float s_q[G][DQK];
+
+    const int lane = threadIdx.x;
+    const int row = lane >> 4;                 // token row 0..3
+    const int c = lane & 15;
+    // split-major dispatch order (see decode_mfma_kernel)
+    const uint32_t kvh = blockIdx.x;
+    const uint32_t s = blockIdx.y;
+    const uint32_t split = blockIdx.z;
+
+    const int32_t n = a.seq_lens[s];
+    const uint32_t nblk = seq_blocks(n, a.M);
+    const uint32_t b0 = split * a.chunk_blocks;
+    if (b0 >= nblk) {
+        if (n <= 0 && split == 0)
+            for (uint32_t idx = lane; idx < (uint32_t)G * DV; idx += 64)
+                a.out[((uint64_t)s * a.Hq + kvh * G) * DV + idx] = 0.f;
+        return;
+    }
+    const uint32_t b1 = min(b0 + a.chunk_blocks, nblk);
+    const uint32_t nsplit = (nblk + a.chunk_blocks - 1) / a.chunk_blocks;
+
+    // q rows of the group into LDS, rotated at position n - 1 if asked
+    const float* qsrc = (const float*)a.q + (uint64_t)s * a.q_stride + (uint64_t)kvh * G * DQK;
+    for (int idx = lane; idx < G * DQK; idx += 64)
+        s_q[idx / DQK][idx % DQK] = qsrc[idx];
+    __syncthreads();
+    if (a.q_rope && a.q_rope_dim > 0) {
+        const uint32_t half = a.q_rope_dim / 2;
+        for (uint32_t idx = lane; idx < (uint32_t)G * half; idx += 64) {
+            const uint32_t g = idx / half, i = idx % half;
+            const float invf =
+                (float)pow((double)a.q_rope_theta, -(2.0 * (double)i) / (double)a.q_rope_dim);
+            const float ang = (float)(n - 1) * invf;
+            float sn, cs;
+            sincosf(ang, &sn, &cs);
+            const float x0 = s_q[g][a.q_rope_offset + i];
+            const float x1 = s_q[g][a.q_rope_offset + i + half];
+            s_q[g][a.q_rope_offset + i] = x0 * cs - x1 * sn;
+            s_q[g][a.q_rope_offset + i + half] = x1 * cs + x0 * sn;
+        }
+        __syncthreads();
+    }
+    f32x4 qv[G][JK];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < JK; ++j)
+            qv[g][j] = *(const f32x4*)&s_q[g][64 * j + 4 * c];
+
+    float m[G], l[G];
+    f32x4 o[G][JV];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        m[g] = -INFINITY;
+        l[g] = 0.f;
+#pragma unroll
+        for (int j = 0; j < JV; ++j)
+            o[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const float* kb = (const float*)a.k_cache;
+    const float* vb = (const float*)a.v_cache;
+    const uint64_t krs = (uint64_t)a.Hkv * DQK, vrs = (uint64_t)a.Hkv * DV;
+    const uint32_t t_end = min((uint32_t)n, b1 * kBS);
+    for (uint32_t t0 = b0 * kBS; t0 < t_end; t0 += 4) {
+        const uint32_t t = t0 + row;
+        const int32_t pb = a.bt[(uint64_t)s * a.M + t / kBS];
+        const bool ok = t < t_end && pb >= 0 && (uint32_t)pb < a.num_blocks;
+        f32x4 kv[JK], vv[JV];
+        if (ok) {
+            const uint64_t r = (uint64_t)pb * kBS + t % kBS;
+#pragma unroll
+            for (int j = 0; j < JK; ++j)
+                kv[j] = __builtin_nontemporal_load((const f32x4*)(kb + r * krs + (uint64_t)kvh * DQK + 64 * j + 4 * c));
+#pragma unroll
+            for (int j = 0; j < JV; ++j)
+                vv[j] = __builtin_nontemporal_load((const f32x4*)(vb + r * vrs + (uint64_t)kvh * DV + 64 * j + 4 * c));
+        } else {
+#pragma unroll
+            for (int j = 0; j < JK; ++j) kv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < JV; ++j) vv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            float d = 0.f;
+#pragma unroll
+            for (int j = 0; j < JK; ++j)
+                d += qv[g][j].x * kv[j].x + qv[g][j].y * kv[j].y + qv[g][j].z * kv[j].z +
+                     qv[g][j].w * kv[j].w;
+            d += __shfl_xor(d, 1, 64);
+            d += __shfl_xor(d, 2, 64);
+            d += __shfl_xor(d, 4, 64);
+            d += __shfl_xor(d, 8, 64);
+            const float sc = ok ? d * a.qk_scale : -INFINITY;
+            const float m_new = fmaxf(m[g], sc);
+            if (m_new != -INFINITY) {
+                const float alpha = __builtin_amdgcn_exp2f(m[g] - m_new);
+                const float p = __builtin_amdgcn_exp2f(sc - m_new);
+                l[g] = l[g] * alpha + p;
+#pragma unroll
+                for (int j = 0; j < JV; ++j)
+                    o[g][j] = o[g][j] * alpha + vv[j] * p;
+                m[g] = m_new;
+            }
+        }
+    }
+    // merge the four row streams
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const float mt = wave_max_xor16_32(m[g]);
+        const float f = mt == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[g] - mt);
+        float lt = wave_sum_xor16_32(l[g] * f);
+#pragma unroll
+        for (int j = 0; j < JV; ++j) {
+            f32x4 v = o[g][j] * f;
+            v.x = wave_sum_xor16_32(v.x);
+            v.y = wave_sum_xor16_32(v.y);
+            v.z = wave_sum_xor16_32(v.z);
+            v.w = wave_sum_xor16_32(v.w);
+            o[g][j] = v;
+        }
+        if (row != 0)
+            continue;
+        const uint32_t h = kvh * G + g;
+        if (nsplit == 1) {
+            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+            const uint64_t base = ((uint64_t)s * a.Hq + h) * DV;
+#pragma unroll
+            for (int j = 0; j < JV; ++j) {
+                f32x4 v = o[g][j] * inv;
+                if (a.gate)
+                    v = v * *(const f32x4*)(a.gate + base + 64 * j + 4 * c);
+                *(f32x4*)(a.out + base + 64 * j + 4 * c) = v;
+            }
+        } else {
+            const uint64_t prow = ((uint64_t)s * a.max_splits + split) * a.Hq + h;
+#pragma unroll
+            for (int j = 0; j < JV; ++j)
+                *(f32x4*)(a.part_o + prow * DV + 64 * j + 4 * c) = o[g][j];
+            if (c == 0)
+                *(f32x2*)(a.part_ml + prow * 2) = f32x2{mt, lt};
+        }
+    }
+}
+
+// ------------------------------------------------------------------ merge
+
+// One work-group per (sequence, query head) with more than one split:
+//   M = max_i m_i, w_i = 2^(m_i - M), out = sum_i w_i o_i / sum_i w_i l_i.
+__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, uint32_t Dv)
+{
+    const uint32_t s = blockIdx.x, h = blockIdx.y;
+    const int32_t n = a.seq_lens[s];
+    const uint32_t nblk = seq_blocks(n, a.M);
+    const uint32_t nsplit = (nblk + a.chunk_blocks - 1) / a.chunk_blocks;
+    if (nsplit <= 1)
+        return;
+    const uint64_t prow0 = ((uint64_t)s * a.max_splits) * a.Hq + h;
+    float M = -INFINITY;
+    for (uint32_t i = 0; i < nsplit; ++i)
+        M = fmaxf(M, a.part_ml[(prow0 + (uint64_t)i * a.Hq) * 2]);
+    for (uint32_t d = threadIdx.x; d < Dv; d += blockDim.x) {
+        float L = 0.f, acc = 0.f;
+        if (M != -INFINITY) {
+            for (uint32_t i = 0; i < nsplit; ++i) {
+                const uint64_t prow = prow0 + (uint64_t)i * a.Hq;
+                const float w = __builtin_amdgcn_exp2f(a.part_ml[prow * 2] - M);
+                L += w * a.part_ml[prow * 2 + 1];
+                acc += w * a.part_o[prow * Dv + d];
+            }
+        }
+        float v = L > 0.f ? acc / L : 0.f;
+        const uint64_t oi = ((uint64_t)s * a.Hq + h) * Dv + d;
+        if (a.gate)
+            v *= a.gate[oi];
+        a.out[oi] = v;
+    }
+}
+
+// ------------------------------------------------------------------ host
+
+struct Plan {
+    uint32_t chunk_blocks;
+    uint32_t max_splits;
+    size_t workspace;
+};
+
+// Split plan: enough (sequence, split) work-groups to cover the chip several
+// times over, each split a whole number of blocks, at most 128 blocks (so a
+// split's block-table entries fit two per lane).
+static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads,
+                      uint32_t head_dim_v, uint32_t max_blocks_per_seq, uint32_t block_size,
+                      uint32_t split_tokens)
+{
+    Plan p{};
+    uint32_t cb;
+    if (split_tokens) {
+        cb = ceil_div(split_tokens, block_size);
+    } else {
+        // count (sequence, kv group) pairs; FP32 path: one wave per kv head
+        const uint32_t kv_groups = ceil_div(num_kv_heads, kKvPerGroup);
+        const uint64_t units = (uint64_t)num_seqs * kv_groups;
+        const uint64_t want = units >= kTargetGroups ? 1 : (kTargetGroups + units - 1) / units;
+        cb = ceil_div(max_blocks_per_seq, want);
+        cb = cb < kMinChunk ? kMinChunk : cb;
+    }
+    cb = cb < 1 ? 1 : cb > kMaxChunk ? kMaxChunk : cb;
+    p.chunk_blocks = cb;
+    p.max_splits = ceil_div(max_blocks_per_seq, cb);
+    if (p.max_splits > 1)
+        p.workspace = (size_t)num_seqs * p.max_splits * num_q_heads * (head_dim_v + 2) * sizeof(float);
+    return p;
+}
+
+}  // namespace pkv
+
+extern "C" size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
+                                             uint32_t num_kv_heads, uint32_t head_dim_v,
+                                             uint32_t max_blocks_per_seq, uint32_t block_size,
+                                             uint32_t split_tokens)
+{
+    if (!num_seqs || !num_q_heads || !num_kv_heads || !head_dim_v || !max_blocks_per_seq ||
+        !block_size)
+        return 0;
+    return pkv::make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim_v, max_blocks_per_seq,
+                          block_size, split_tokens)
+        .workspace;
+}
+
+extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
+                                     const void* k_cache, pkv_dtype k_dtype, float k_scale,
+                                     const void* v_cache, pkv_dtype v_dtype,
+                                     const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, uint32_t num_seqs,
+                                     uint32_t num_blocks, uint32_t num_q_heads,
+                                     uint32_t num_kv_heads, uint32_t head_dim_qk,
+                                     uint32_t head_dim_v, uint32_t block_size, float scale,
+                                     int q_rope, float q_rope_theta, uint32_t q_rope_offset,
+                                     uint32_t q_rope_dim, const float* gate, float* out,
+                                     uint32_t split_tokens, void* workspace,
+                                     size_t workspace_bytes, void* stream)
+{
+    using namespace pkv;
+    clear_error();
+    if (num_seqs == 0)
+        return PKV_OK;
+    if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
+        return fail(PKV_ERR_INVALID, "paged_decode_attn: q, caches, block_tables, seq_lens and out must be non-NULL");
+    if (!valid_dtype(q_dtype) || !valid_dtype(k_dtype) || !valid_dtype(v_dtype))
+        return fail(PKV_ERR_INVALID, "paged_decode_attn: bad dtype");
+    if (!num_q_heads || !num_kv_heads || !head_dim_qk || !head_dim_v || !max_blocks_per_seq ||
+        !num_blocks || !block_size)
+        return fail(PKV_ERR_INVALID, "paged_decode_attn: zero dimension");
+    if (num_q_heads % num_kv_heads)
+        return fail(PKV_ERR_INVALID, "paged_decode_attn: num_q_heads %% num_kv_heads != 0");
+    if (block_size != (uint32_t)kBS)
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: block_size must be 16");
+    if (q_seq_stride < (uint64_t)num_q_heads * head_dim_qk)
+        return fail(PKV_ERR_INVALID, "paged_decode_attn: q_seq_stride smaller than a query row");
+    const uint32_t G = num_q_heads / num_kv_heads;
+    const bool mfma_path = q_dtype == PKV_BF16 && v_dtype == PKV_BF16 &&
+                           (k_dtype == PKV_BF16 || k_dtype == PKV_FP8_E4M3);
+    const bool f32_path = q_dtype == PKV_FP32 && k_dtype == PKV_FP32 && v_dtype == PKV_FP32;
+    if (!mfma_path && !f32_path)
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: dtypes (q,K,V) must be (BF16,BF16,BF16), (BF16,E4M3,BF16) or (FP32,FP32,FP32)");
+    if ((q_seq_stride * dtype_size(q_dtype)) % 16 || !aligned16(q) || !aligned16(k_cache) ||
+        !aligned16(v_cache) || !aligned16(out) || (gate && !aligned16(gate)))
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: pointers and q stride must be 16-byte aligned");
+    if (k_dtype == PKV_FP8_E4M3 && !(k_scale > 0.0f && k_scale < INFINITY))
+        return fail(PKV_ERR_INVALID, "paged_decode_attn: k_scale must be finite and > 0");
+    if (q_rope && q_rope_dim > 0) {
+        if (!f32_path)
+            return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: query rotation is supported for FP32 q/K/V");
+        if (q_rope_dim % 2 || (uint64_t)q_rope_offset + q_rope_dim > head_dim_qk)
+            return fail(PKV_ERR_INVALID, "paged_decode_attn: q_rope_dim must be even and fit the head");
+    }
+    if (mfma_path) {
+        if (head_dim_qk != head_dim_v || (head_dim_qk != 64 && head_dim_qk != 128))
+            return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: BF16/E4M3 caches need head_dim_qk == head_dim_v in {64,128}");
+        if (G > 16)
+            return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: GQA group above 16");
+    } else {
+        if ((head_dim_qk != 64 && head_dim_qk != 128 && head_dim_qk != 192 && head_dim_qk != 256) ||
+            (head_dim_v != 64 && head_dim_v != 128))
+            return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: FP32 path needs head_dim_qk in {64,128,192,256}, head_dim_v in {64,128}");
+        if (G != 1 && G != 2 && G != 4 && G != 8)
+            return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: FP32 path needs a GQA group of 1, 2, 4 or 8");
+    }
+    const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim_v,
+                                max_blocks_per_seq, block_size, split_tokens);
+    if (plan.workspace > 0 && (workspace_bytes < plan.workspace || !workspace))
+        return fail(PKV_ERR_WORKSPACE, "paged_decode_attn: workspace of %zu bytes needed, %zu given",
+                    plan.workspace, workspace_bytes);
+    if (plan.workspace > 0 && !aligned16(workspace))
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: workspace must be 16-byte aligned");
+
+    DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.bt = block_tables;
+    a.seq_lens = seq_lens;
+    a.gate = gate;
+    a.out = out;
+    a.part_o = (float*)workspace;
+    a.part_ml = plan.workspace
+                    ? (float*)workspace + (size_t)num_seqs * plan.max_splits * num_q_heads * head_dim_v
+                    : nullptr;
+    a.q_stride = q_seq_stride;
+    a.M = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.G = G;
+    a.chunk_blocks = plan.chunk_blocks;
+    a.max_splits = plan.max_splits;
+    a.qk_scale = scale * kLog2e * (k_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f);
+    a.q_rope = (q_rope && q_rope_dim > 0) ? 1u : 0u;
+    a.q_rope_theta = q_rope_theta;
+    a.q_rope_offset = q_rope_offset;
+    a.q_rope_dim = q_rope_dim;
+    hipStream_t st = (hipStream_t)stream;
+
+    if (mfma_path) {
+        uint32_t kvpb = kKvPerGroup;
+        while (num_kv_heads % kvpb)
+            kvpb >>= 1;
+        const uint32_t kvg = num_kv_heads / kvpb;
+        const dim3 grid(num_seqs * kvg, plan.max_splits);
+        const dim3 block(64 * kvpb);
+        if (k_dtype == PKV_BF16) {
+            if (head_dim_qk == 128)
+                hipLaunchKernelGGL((decode_mfma_kernel<0, 128, kPrefetch>), grid, block, 0, st, a, kvg);
+            else
+                hipLaunchKernelGGL((decode_mfma_kernel<0, 64, kPrefetch>), grid, block, 0, st, a, kvg);
+        } else {
+            if (head_dim_qk == 128)
+                hipLaunchKernelGGL((decode_mfma_kernel<1, 128, kPrefetch>), grid, block, 0, st, a, kvg);
+            else
+                hipLaunchKernelGGL((decode_mfma_kernel<1, 64, kPrefetch>), grid, block, 0, st, a, kvg);
+        }
+    } else {
+        const dim3 grid(num_kv_heads, num_seqs, plan.max_splits);
+#define PKV_F32(DQK, DV, GG)                                                              \
+    if (head_dim_qk == DQK && head_dim_v == DV && G == GG)                                \
+        hipLaunchKernelGGL((decode_f32_kernel<DQK, DV, GG>), grid, dim3(64), 0, st, a);
+#define PKV_F32_G(DQK, DV) PKV_F32(DQK, DV, 1) PKV_F32(DQK, DV, 2) PKV_F32(DQK, DV, 4) PKV_F32(DQK, DV, 8)
+        PKV_F32_G(64, 64) PKV_F32_G(128, 64) PKV_F32_G(192, 64) PKV_F32_G(256, 64)
+        PKV_F32_G(64, 128) PKV_F32_G(128, 128) PKV_F32_G(192, 128) PKV_F32_G(256, 128)
+#undef PKV_F32_G
+#undef PKV_F32
+    }
+    int rc = check_launch("paged_decode_attn");
+    if (rc)
+        return rc;
+    if (plan.max_splits > 1) {
+        hipLaunchKernelGGL(decode_merge_kernel, dim3(num_seqs, num_q_heads), dim3(128), 0, st, a,
+                           head_dim_v);
+        rc = check_launch("paged_decode_attn merge");
+    }
+    return rc;
+}

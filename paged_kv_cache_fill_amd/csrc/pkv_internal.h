@@ -1,0 +1,80 @@
+// pkv_internal.h -- shared device helpers and host-side status plumbing of
+// libpkv (gfx950).  Not part of the public ABI (that is include/pkv.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "pkv.h"
+
+namespace pkv {
+
+// ---------------------------------------------------------------- host side
+
+// Records a message for pkv_last_error() and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clears the message (start of every entry point).
+void clear_error();
+// Checks the launch that just happened on the calling thread.
+int check_launch(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline size_t dtype_size(pkv_dtype t)
+{
+    return t == PKV_BF16 ? 2 : t == PKV_FP32 ? 4 : 1;
+}
+
+inline bool valid_dtype(int t) { return t == PKV_BF16 || t == PKV_FP8_E4M3 || t == PKV_FP32; }
+
+inline uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
+
+// ---------------------------------------------------------------- device side
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Two BF16 halves of a 32-bit word -> FP32 (exact: BF16 is the top half of
+// a binary32 pattern).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two FP32 -> packed BF16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b)
+{
+    bf16x2 v;
+    v.x = (__bf16)a;
+    v.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Four FP32 -> four E4M3FN bytes in a word (v_cvt_pk_fp8_f32, round to
+// nearest even).  Callers clamp finite magnitudes to 448 first.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d)
+{
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+    return (uint32_t)w;
+}
+
+// Two E4M3FN bytes (selected by `hi`) -> two FP32, exact.
+__device__ __forceinline__ f32x2 unpack_e4m3x2(uint32_t w, bool hi)
+{
+    return hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+              : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+}
+
+// Streaming (read-once / write-once) 16-byte accesses.
+__device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+}  // namespace pkv

@@ -140,6 +140,26 @@ def layout(index: int, num_seqs: int | None = None, len_hi: int | None = None) -
     return Layout(index, lens, bt, pool, pad_block, B, cfg)
 
 
+def layout_for(index: int, lens, max_blocks_per_seq: int | None = None) -> Layout:
+    """Block tables (seeded shuffle of a pool sized to fit, plus one padding
+    block) for explicitly given sequence lengths."""
+    cfg = dict(WORKLOADS[index])
+    B = cfg["block_size"]
+    lens = np.asarray(lens, np.int32)
+    nblk = (np.maximum(lens.astype(np.int64), 0) + B - 1) // B
+    M = int(max(1, nblk.max())) if max_blocks_per_seq is None else int(max_blocks_per_seq)
+    used = int(nblk.sum())
+    pool = used + 1
+    perm = rng(index, S_BLOCKS + 200).permutation(pool).astype(np.int32)
+    pad_block = int(perm[-1])
+    bt = np.full((lens.size, M), pad_block, np.int32)
+    off = 0
+    for s in range(lens.size):
+        bt[s, :nblk[s]] = perm[off:off + nblk[s]]
+        off += int(nblk[s])
+    return Layout(index, lens, bt, pool, pad_block, B, cfg)
+
+
 def normal(index: int, stream: int, shape, outliers: bool = False) -> np.ndarray:
     x = rng(index, stream).standard_normal(size=shape, dtype=np.float32)
     if outliers:
