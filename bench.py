@@ -295,43 +295,55 @@ def main():
 
 
 def cpu_baseline(idx, lay, k_scale):
-    """The oracle, as it stands, timed on this host on a bounded sample of the
-    workload: the decode step (slots, K write, V write, attention) of the first
-    sequences, on random pools of the workload's shapes."""
+    """The oracle, as it stands, timed on this host on the decode step of the
+    whole workload (slots, K write, V write, attention over every sequence).
+    Pools are drawn on the device by the seeded generator and copied to the
+    host; nothing in them comes from the HIP path."""
+    import torch
+
     import oracle
     import pkv_workloads as W
     cores = max(1, min(16, os.cpu_count() or 1))
     cfg = lay.cfg
-    # sample: leading sequences up to ~150k tokens of history
-    lens = lay.seq_lens.astype(np.int64)
-    n_s = int(np.searchsorted(np.cumsum(lens), 150000)) + 1
-    n_s = max(1, min(n_s, lay.num_seqs))
-    sub = W.layout_for(idx, lay.seq_lens[:n_s])
-    kp, vp = W.random_pools(idx, sub, poison_pad=False)
     Hq, Hkv, D, Dv = cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], cfg["head_dim_v"]
-    q = W.queries(idx, n_s)
-    k_new = W.kv_tokens(idx, n_s, "k")
-    v_new = W.kv_tokens(idx, n_s, "v")
-    w = W.norm_weight(idx)
-    start, cu, pos = W.positions_decode(sub)
     fp8 = cfg["k_cache_dtype"] == "fp8"
+    shape = (lay.num_blocks, 16, Hkv, D)
+    if fp8:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(W.seed_of(idx) * 1000 + W.S_POOLK)
+        mag = torch.randint(0, 0x50, shape, dtype=torch.uint8, device="cuda", generator=g)
+        sign = torch.randint(0, 2, shape, dtype=torch.uint8, device="cuda", generator=g) << 7
+        kp = (mag | sign).cpu().numpy()
+        del mag, sign
+    else:
+        kp = W.device_normal(idx, W.S_POOLK, shape, torch.bfloat16, "cuda").view(torch.int16) \
+            .cpu().numpy().view(np.uint16)
+    vp = W.device_normal(idx, W.S_POOLV, (lay.num_blocks, 16, Hkv, Dv), torch.bfloat16, "cuda") \
+        .view(torch.int16).cpu().numpy().view(np.uint16)
+    torch.cuda.empty_cache()
+    S = lay.num_seqs
+    q = W.queries(idx, S)
+    k_new = W.kv_tokens(idx, S, "k")
+    v_new = W.kv_tokens(idx, S, "v")
+    w = W.norm_weight(idx)
+    start, cu, pos = W.positions_decode(lay)
     t0 = time.perf_counter()
-    slots = oracle.fill_slots(sub.block_tables, start, cu, n_s, 16)
+    slots = oracle.fill_slots(lay.block_tables, start, cu, S, 16)
     oracle.cache_write_k(k_new, "bf16", slots, kp, cfg["k_cache_dtype"], num_kv_heads=Hkv,
                          head_dim=D, block_size=16, norm_weight=w, eps=cfg["eps"], pos_t=pos,
                          theta=cfg["theta"], k_scale=k_scale, nthreads=cores)
     oracle.cache_write_v(v_new, "bf16", slots, vp, num_kv_heads=Hkv, head_dim_v=Dv, block_size=16)
-    oracle.paged_decode(q, "bf16", kp, cfg["k_cache_dtype"], vp, "bf16", sub.block_tables,
-                        sub.seq_lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D,
+    oracle.paged_decode(q, "bf16", kp, cfg["k_cache_dtype"], vp, "bf16", lay.block_tables,
+                        lay.seq_lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D,
                         head_dim_v=Dv, block_size=16, scale=D ** -0.5, k_scale=k_scale,
                         nthreads=cores)
     dt = time.perf_counter() - t0
-    b = (decode_bytes(sub.seq_lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 2, 2)
-         + kwrite_bytes(n_s, Hkv, D, 2, 1 if fp8 else 2) + vwrite_bytes(n_s, Hkv, Dv, 2)
-         + slots_bytes(n_s, n_s))
+    b = (decode_bytes(lay.seq_lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 2, 2)
+         + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2) + vwrite_bytes(S, Hkv, Dv, 2)
+         + slots_bytes(S, S))
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"decode step of the first {n_s} of {lay.num_seqs} sequences "
-                      f"({int(sub.seq_lens.sum())} tokens of history), {dt:.2f} s"}
+            "sample": f"the whole decode step of all {S} sequences "
+                      f"({int(lay.seq_lens.astype(np.int64).sum())} tokens), {dt:.2f} s"}
 
 
 if __name__ == "__main__":
