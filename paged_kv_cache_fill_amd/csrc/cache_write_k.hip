@@ -42,7 +42,8 @@ struct KWriteArgs {
     float eps;
     float theta;
     float k_scale;
-    float inv_k_scale;
+    float inv_k_scale;      // 1 / k_scale for the E4M3 store, else 1
+    float inv_d;            // 1 / head_dim
     uint32_t D;
     uint32_t Hkv;
     uint32_t rope_first;    // first rotated chunk (rope_offset / VEC)
@@ -60,9 +61,12 @@ struct InVec;
 template <>
 struct InVec<IN_BF16> {
     static constexpr int VEC = 8;
-    __device__ static void load(const void* base, uint64_t elem, float* x)
+    __device__ static u32x4 raw(const void* base, uint64_t elem)
     {
-        u32x4 w = load_nt((const u32x4*)((const uint16_t*)base + elem));
+        return load_nt((const u32x4*)((const uint16_t*)base + elem));
+    }
+    __device__ static void cvt(const u32x4& w, float* x)
+    {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             x[2 * i] = bf16_lo(w[i]);
@@ -77,9 +81,12 @@ struct InVec<IN_BF16> {
 template <>
 struct InVec<IN_F32> {
     static constexpr int VEC = 4;
-    __device__ static void load(const void* base, uint64_t elem, float* x)
+    __device__ static u32x4 raw(const void* base, uint64_t elem)
     {
-        u32x4 w = load_nt((const u32x4*)((const float*)base + elem));
+        return load_nt((const u32x4*)((const float*)base + elem));
+    }
+    __device__ static void cvt(const u32x4& w, float* x)
+    {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             x[i] = __uint_as_float(w[i]);
@@ -92,8 +99,7 @@ struct InVec<IN_F32> {
 
 // Store VEC FP32 values at element offset `elem` of the cache.
 template <int OUT, int VEC>
-__device__ __forceinline__ void store_chunk(void* cache, uint64_t elem, const float* y,
-                                            float k_scale, float inv_k_scale)
+__device__ __forceinline__ void store_chunk(void* cache, uint64_t elem, const float* y)
 {
     if constexpr (OUT == OUT_BF16) {
         uint32_t w[VEC / 2];
@@ -107,23 +113,14 @@ __device__ __forceinline__ void store_chunk(void* cache, uint64_t elem, const fl
             __builtin_nontemporal_store(u32x2{w[0], w[1]}, (u32x2*)p);
         }
     } else if constexpr (OUT == OUT_FP8) {
+        // y already carries the 1/k_scale factor (folded into the row scale):
+        // clamp finite and infinite magnitudes to 448 (v_med3), then round
         float z[VEC];
         bool any_nan = false;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-            // fl32(y / k_scale): product by the reciprocal plus one FMA
-            // correction step (the residual y - q*k_scale is exact).
-            // An infinite q makes the residual NaN (inf - inf): keep q then.
-            // A zero quotient takes q's sign (the residual sum is +0).
-            float q = y[i] * inv_k_scale;
-            float r = __builtin_fmaf(-q, k_scale, y[i]);
-            float v = __builtin_fmaf(r, inv_k_scale, q);
-            v = v == v ? __builtin_copysignf(v, q) : q;
-            // saturate finite and infinite magnitudes to 448; NaN passes
-            v = v > 448.0f ? 448.0f : v;
-            v = v < -448.0f ? -448.0f : v;
-            any_nan |= v != v;
-            z[i] = v;
+            any_nan |= y[i] != y[i];
+            z[i] = __builtin_amdgcn_fmed3f(y[i], -448.0f, 448.0f);
         }
         uint32_t w[VEC / 4];
 #pragma unroll
@@ -133,9 +130,9 @@ __device__ __forceinline__ void store_chunk(void* cache, uint64_t elem, const fl
             // NaN is stored as the E4M3FN NaN code S.1111.111 with its sign
 #pragma unroll
             for (int i = 0; i < VEC; ++i) {
-                if (z[i] != z[i]) {
+                if (y[i] != y[i]) {
                     const uint32_t sh = 8u * (i % 4);
-                    const uint32_t code = 0x7Fu | ((__float_as_uint(z[i]) >> 24) & 0x80u);
+                    const uint32_t code = 0x7Fu | ((__float_as_uint(y[i]) >> 24) & 0x80u);
                     w[i / 4] = (w[i / 4] & ~(0xFFu << sh)) | (code << sh);
                 }
             }
@@ -156,14 +153,20 @@ __device__ __forceinline__ void store_chunk(void* cache, uint64_t elem, const fl
     }
 }
 
+// Per-token arrays are separate restrict parameters: the compiler may then
+// read them with scalar loads (they cannot alias the cache being written).
 template <int IN, int OUT, int NC>
-__global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(KWriteArgs a)
+__global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(
+    KWriteArgs a, const int64_t* __restrict__ slots, const int32_t* __restrict__ pos_t,
+    const int32_t* __restrict__ pos_h, const int32_t* __restrict__ pos_w)
 {
     constexpr int VEC = InVec<IN>::VEC;
     __shared__ float s_cos[kKWaves][kMaxHalf];
     __shared__ float s_sin[kKWaves][kMaxHalf];
 
-    const uint32_t wave = threadIdx.x / 64;
+    // wave index made explicitly uniform: the token cursors derived from it
+    // then live in scalar registers and per-token loads are scalar loads
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
     const uint32_t lane = threadIdx.x % 64;
     const uint32_t rr = lane / a.L;         // row within the wave
     const uint32_t lir = lane % a.L;        // lane within the row
@@ -189,43 +192,54 @@ __global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(KWriteArgs a)
     const uint64_t u0 = gwave * a.units_per_wave;
     const uint64_t u1 = u0 + a.units_per_wave < a.num_units ? u0 + a.units_per_wave : a.num_units;
 
-    for (uint64_t u = u0; u < u1; ++u) {
-        const uint64_t t = u / a.units_per_token;
-        const uint32_t grp = (uint32_t)(u % a.units_per_token);
-        const int64_t slot = a.slots[t];
+    // Software pipeline over the wave's units: the next unit's row is loaded
+    // while the current one is computed and stored.  Loads are unconditional
+    // (rows past Hkv re-read the last head's row), so the compiler's wait
+    // before each unit covers only that unit's loads.
+    struct Raw {
+        u32x4 w[NC];
+    };
+    auto load_unit = [&](uint32_t t, uint32_t grp, Raw& r) {
+        uint32_t h = grp * a.rows_per_wave + rr;
+        h = h < a.Hkv ? h : a.Hkv - 1;
+        const uint64_t src = (uint64_t)t * a.in_stride + (uint64_t)h * a.D;
+#pragma unroll
+        for (int k = 0; k < NC; ++k)
+            r.w[k] = InVec<IN>::raw(a.k_in, src + (uint64_t)(lir + a.L * k) * VEC);
+    };
+
+    auto process = [&](uint32_t t, uint32_t grp, const Raw& raw) {
+        const int64_t slot = slots[t];
         if (slot < 0 || (uint64_t)slot >= a.num_slots)
-            continue;                                   // padding slot: no write
+            return;                                     // padding slot: no write
         const uint32_t h = grp * a.rows_per_wave + rr;
         const bool row_ok = h < a.Hkv;
 
         float y[NC][VEC];
-        if (row_ok) {
-            const uint64_t src = t * a.in_stride + (uint64_t)h * a.D;
 #pragma unroll
-            for (int k = 0; k < NC; ++k)
-                InVec<IN>::load(a.k_in, src + (uint64_t)(lir + a.L * k) * VEC, y[k]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < NC; ++k)
-#pragma unroll
-                for (int e = 0; e < VEC; ++e)
-                    y[k][e] = 0.f;
-        }
-
+        for (int k = 0; k < NC; ++k)
+            InVec<IN>::cvt(raw.w[k], y[k]);
         // angles of this token, one (token, pair) per lane, shared via LDS
         if (a.half > 0) {
+            // positions are per token (wave-uniform): load them outside the
+            // lane-dependent branch
+            const int32_t pt = pos_t[t];
+            const int32_t ph = mrope ? pos_h[t] : pt;
+            const int32_t pw = mrope ? pos_w[t] : pt;
 #pragma unroll
             for (int rep = 0; rep < 2; ++rep) {
                 const uint32_t i = lane + 64u * rep;
                 if (i < a.half) {
-                    int32_t p = a.pos_t[t];
-                    if (mrope) {
-                        const uint32_t ax = i % 3u;
-                        p = ax == 0 ? p : ax == 1 ? a.pos_h[t] : a.pos_w[t];
-                    }
+                    const uint32_t ax = i % 3u;
+                    const int32_t p = ax == 0 ? pt : ax == 1 ? ph : pw;
                     const float ang = (float)p * (rep ? invf1 : invf0);
-                    float sn, cs;
-                    sincosf(ang, &sn, &cs);
+                    // reduce the FP32 angle to [-1/2, 1/2] revolution in double
+                    // (exact enough for any int32 position), then the hardware
+                    // sin/cos, which take revolutions
+                    const double rev = (double)ang * 0.15915494309189535;
+                    const float f = (float)(rev - __builtin_rint(rev));
+                    const float sn = __builtin_amdgcn_sinf(f);
+                    const float cs = __builtin_amdgcn_cosf(f);
                     s_cos[wave][i] = cs;
                     s_sin[wave][i] = sn;
                 }
@@ -234,6 +248,9 @@ __global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(KWriteArgs a)
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 
+        // row factor: 1/rms (RMSNorm) times 1/k_scale (E4M3 store; 1 otherwise).
+        // Rotation is linear, so scaling before it equals dividing the rotated
+        // row by k_scale up to FP32 rounding.
         if (a.norm_w) {
             float ss = 0.f;
 #pragma unroll
@@ -241,14 +258,24 @@ __global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(KWriteArgs a)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     ss = __builtin_fmaf(y[k][e], y[k][e], ss);
-            for (uint32_t m = 1; m < a.L; m <<= 1)
-                ss += __shfl_xor(ss, (int)m, 64);
-            const float r = rsqrtf(ss / (float)a.D + a.eps);
+            // butterfly over the row's L lanes (L <= 16), unrolled; the
+            // predicate is wave-uniform
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1)
+                if ((uint32_t)m < a.L)
+                    ss += __shfl_xor(ss, m, 64);
+            const float r = rsqrtf(__builtin_fmaf(ss, a.inv_d, a.eps)) * a.inv_k_scale;
 #pragma unroll
             for (int k = 0; k < NC; ++k)
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     y[k][e] = y[k][e] * r * w[k][e];
+        } else if (OUT == OUT_FP8) {
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e)
+                    y[k][e] = y[k][e] * a.inv_k_scale;
         }
 
         if (a.half > 0) {
@@ -280,8 +307,45 @@ __global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(KWriteArgs a)
             const uint64_t dst = ((uint64_t)slot * a.Hkv + h) * a.D;
 #pragma unroll
             for (int k = 0; k < NC; ++k)
-                store_chunk<OUT, VEC>(a.k_cache, dst + (uint64_t)(lir + a.L * k) * VEC, y[k],
-                                      a.k_scale, a.inv_k_scale);
+                store_chunk<OUT, VEC>(a.k_cache, dst + (uint64_t)(lir + a.L * k) * VEC, y[k]);
+        }
+    };
+
+    if (u0 < u1) {
+        // (token, group) cursors instead of dividing the unit index each time
+        const uint32_t U = a.units_per_token;
+        // token indices fit 32 bits (num_tokens is a uint32); readfirstlane
+        // keeps the cursors in scalar registers
+        uint32_t lt = __builtin_amdgcn_readfirstlane((uint32_t)(u0 / U)), pt = lt;
+        uint32_t lg = __builtin_amdgcn_readfirstlane((uint32_t)(u0 % U)), pg = lg;
+        auto next = [&](uint32_t& t, uint32_t& g) {
+            if (++g == U) {
+                g = 0;
+                ++t;
+            }
+        };
+        const uint32_t n = (uint32_t)(u1 - u0);
+        Raw ra, rb;
+        load_unit(lt, lg, ra);
+        next(lt, lg);
+        uint32_t i = 0;
+        for (; i + 2 < n; i += 2) {                     // both successors exist
+            load_unit(lt, lg, rb);
+            next(lt, lg);
+            process(pt, pg, ra);
+            next(pt, pg);
+            load_unit(lt, lg, ra);
+            next(lt, lg);
+            process(pt, pg, rb);
+            next(pt, pg);
+        }
+        if (i + 1 < n) {
+            load_unit(lt, lg, rb);
+            process(pt, pg, ra);
+            next(pt, pg);
+            process(pt, pg, rb);
+        } else {
+            process(pt, pg, ra);
         }
     }
 }
@@ -292,12 +356,12 @@ template <int IN, int OUT>
 static bool launch_nc(int nc, dim3 grid, hipStream_t st, const KWriteArgs& a)
 {
     switch (nc) {
-    case 1: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 1>), grid, dim3(kKThreads), 0, st, a); return true;
-    case 2: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 2>), grid, dim3(kKThreads), 0, st, a); return true;
-    case 3: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 3>), grid, dim3(kKThreads), 0, st, a); return true;
-    case 4: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 4>), grid, dim3(kKThreads), 0, st, a); return true;
-    case 6: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 6>), grid, dim3(kKThreads), 0, st, a); return true;
-    case 8: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 8>), grid, dim3(kKThreads), 0, st, a); return true;
+    case 1: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 1>), grid, dim3(kKThreads), 0, st, a, a.slots, a.pos_t, a.pos_h, a.pos_w); return true;
+    case 2: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 2>), grid, dim3(kKThreads), 0, st, a, a.slots, a.pos_t, a.pos_h, a.pos_w); return true;
+    case 3: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 3>), grid, dim3(kKThreads), 0, st, a, a.slots, a.pos_t, a.pos_h, a.pos_w); return true;
+    case 4: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 4>), grid, dim3(kKThreads), 0, st, a, a.slots, a.pos_t, a.pos_h, a.pos_w); return true;
+    case 6: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 6>), grid, dim3(kKThreads), 0, st, a, a.slots, a.pos_t, a.pos_h, a.pos_w); return true;
+    case 8: hipLaunchKernelGGL((cache_write_k_kernel<IN, OUT, 8>), grid, dim3(kKThreads), 0, st, a, a.slots, a.pos_t, a.pos_h, a.pos_w); return true;
     default: return false;
     }
 }
@@ -395,6 +459,7 @@ extern "C" int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype,
     a.theta = theta;
     a.k_scale = k_scale;
     a.inv_k_scale = cache_dtype == PKV_FP8_E4M3 ? 1.0f / k_scale : 1.0f;
+    a.inv_d = 1.0f / (float)head_dim;
     a.D = head_dim;
     a.Hkv = num_kv_heads;
     a.rope_first = rope ? rope_offset / VEC : 0;
@@ -408,7 +473,7 @@ extern "C" int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype,
     // a few units per wave: enough waves to fill 256 CUs many times over
     const uint64_t target_waves = 256ull * 32;
     uint64_t upw = a.num_units / target_waves;
-    upw = upw < 1 ? 1 : upw > 8 ? 8 : upw;
+    upw = upw < 1 ? 1 : upw > 16 ? 16 : upw;
     a.units_per_wave = (uint32_t)upw;
     const uint64_t waves = (a.num_units + upw - 1) / upw;
     const uint64_t blocks = (waves + kKWaves - 1) / kKWaves;
