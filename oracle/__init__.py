@@ -67,11 +67,11 @@ def lib():
         L.pkvo_cache_write_k.argtypes = [P, I32, U64, P, F32, P, P, P, F32, U32, U32, I32,
                                          P, U32, U32, U32, U32, U32, P, I32, F32, I32]
         L.pkvo_cache_write_k.restype = None
-        L.pkvo_cache_write_v.argtypes = [P, I32, U64, P, U32, U32, U32, U32, U32, P]
+        L.pkvo_cache_write_v.argtypes = [P, I32, U64, P, U32, U32, U32, U32, U32, P, I32, F32]
         L.pkvo_cache_write_v.restype = None
         L.pkvo_paged_decode.argtypes = [P, I32, U64, P, I32, F32, P, I32, F32, P, U32, P, U32,
-                                        U32, U32, U32, U32, U32, U32, F32, I32, F32, U32, U32,
-                                        P, P, I32]
+                                        U32, U32, U32, U32, U32, U32, F32, U32, P, I32, F32,
+                                        U32, U32, P, P, I32]
         L.pkvo_paged_decode.restype = None
         _lib = L
     return _lib
@@ -181,23 +181,27 @@ def cache_write_k(k_in, in_dtype, slots, k_cache, cache_dtype, *, num_kv_heads, 
 
 
 def cache_write_v(v, dtype, slots, v_cache, *, num_kv_heads, head_dim_v, block_size,
-                  in_token_stride=None):
-    """Byte copy of V rows into ``v_cache`` (modified in place)."""
+                  in_token_stride=None, cache_dtype=None, v_scale=1.0):
+    """V rows into ``v_cache`` (modified in place): a byte copy when the cache
+    has the input's dtype, else (``cache_dtype="fp8"``) E4M3 of v / v_scale."""
+    cache_dtype = cache_dtype or dtype
     v = _c(v, NP_TYPES[dtype])
     T = int(slots.size)
     stride = in_token_stride if in_token_stride is not None else num_kv_heads * head_dim_v
-    assert v_cache.flags.c_contiguous and v_cache.dtype == NP_TYPES[dtype]
+    assert v_cache.flags.c_contiguous and v_cache.dtype == NP_TYPES[cache_dtype]
     num_blocks = v_cache.size // (block_size * num_kv_heads * head_dim_v)
     sl = _c(slots, np.int64)
     lib().pkvo_cache_write_v(_ptr(v), DTYPES[dtype], stride, _ptr(sl), T, num_kv_heads,
-                             head_dim_v, block_size, num_blocks, _ptr(v_cache))
+                             head_dim_v, block_size, num_blocks, _ptr(v_cache),
+                             DTYPES[cache_dtype], v_scale)
     return v_cache
 
 
 def paged_decode(q, q_dtype, k_cache, k_dtype, v_cache, v_dtype, block_tables, seq_lens, *,
                  num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, block_size, scale,
-                 k_scale=1.0, v_scale=1.0, q_rope=False, q_rope_theta=10000.0,
-                 q_rope_offset=0, q_rope_dim=0, gate=None, q_seq_stride=None, nthreads=1):
+                 k_scale=1.0, v_scale=1.0, sliding_window=0, sinks=None, q_rope=False,
+                 q_rope_theta=10000.0, q_rope_offset=0, q_rope_dim=0, gate=None,
+                 q_seq_stride=None, nthreads=1):
     """Decode attention, one query token per sequence.  Returns FP32
     [num_seqs, num_q_heads, head_dim_v]."""
     q = _c(q, NP_TYPES[q_dtype])
@@ -211,10 +215,12 @@ def paged_decode(q, q_dtype, k_cache, k_dtype, v_cache, v_dtype, block_tables, s
     num_blocks = kc.size // (block_size * num_kv_heads * head_dim_qk)
     qs = q_seq_stride if q_seq_stride is not None else num_q_heads * head_dim_qk
     g = _c(gate, np.float32)
+    sk = _c(sinks, np.float32)
     out = np.empty((S, num_q_heads, head_dim_v), np.float32)
     lib().pkvo_paged_decode(_ptr(q), DTYPES[q_dtype], qs, _ptr(kc), DTYPES[k_dtype], k_scale,
                             _ptr(vc), DTYPES[v_dtype], v_scale, _ptr(bt), bt.shape[1], _ptr(sl),
                             S, num_blocks, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v,
-                            block_size, scale, int(q_rope), q_rope_theta, q_rope_offset,
+                            block_size, scale, sliding_window, _ptr(sk), int(q_rope),
+                            q_rope_theta, q_rope_offset,
                             q_rope_dim, _ptr(g), _ptr(out), nthreads)
     return out

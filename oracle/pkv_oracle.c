@@ -345,23 +345,35 @@ void pkvo_cache_write_k(const void* k_in, int in_dtype, uint64_t in_token_stride
 /* (4) V reshape-and-cache                                             */
 /* ------------------------------------------------------------------ */
 
-/* v_cache[slot, h, :] = v[t, h, :] byte for byte; padding slots skipped
- * (p1 reshape_and_cache_flash_v_only: the V-only write that leaves the K
- * side of the cache to the fused K kernel). */
-void pkvo_cache_write_v(const void* v, int dtype, uint64_t in_token_stride,
+/* Same dtype in and out: v_cache[slot, h, :] = v[t, h, :] byte for byte
+ * (p1 reshape_and_cache_flash_v_only: the V-only write that leaves the K side
+ * of the cache to the fused K kernel).  E4M3 cache: each element is stored as
+ * the saturating E4M3 cast of fl32(v / v_scale), the same store as an FP8 K
+ * cache (p1 reshape_and_cache_fp8 writes K and V to FP8 with k_scale and
+ * v_scale; p2 module invariants fix the store as value / scale).  Padding
+ * slots (negative or past the pool) are skipped. */
+void pkvo_cache_write_v(const void* v, int in_dtype, uint64_t in_token_stride,
                         const int64_t* slots, uint32_t num_tokens, uint32_t num_kv_heads,
                         uint32_t head_dim_v, uint32_t block_size, uint32_t num_blocks,
-                        void* v_cache)
+                        void* v_cache, int cache_dtype, float v_scale)
 {
-    size_t es = elem_size(dtype);
-    size_t row = (size_t)num_kv_heads * head_dim_v * es;
+    size_t es = elem_size(in_dtype);
+    uint64_t row_elems = (uint64_t)num_kv_heads * head_dim_v;
     uint64_t num_slots = (uint64_t)num_blocks * block_size;
     for (uint64_t t = 0; t < num_tokens; ++t) {
         int64_t slot = slots[t];
         if (slot < 0 || (uint64_t)slot >= num_slots)
             continue;
-        memcpy((char*)v_cache + (uint64_t)slot * row,
-               (const char*)v + t * in_token_stride * es, row);
+        if (cache_dtype == in_dtype) {
+            memcpy((char*)v_cache + (uint64_t)slot * row_elems * es,
+                   (const char*)v + t * in_token_stride * es, row_elems * es);
+            continue;
+        }
+        for (uint64_t e = 0; e < row_elems; ++e) {
+            double x = load_elem(v, in_dtype, t * in_token_stride + e);
+            float z = (float)(x / (double)v_scale);               /* fl32(v/v_scale) */
+            ((uint8_t*)v_cache)[(uint64_t)slot * row_elems + e] = pkvo_e4m3_from_f64((double)z);
+        }
     }
 }
 
@@ -376,6 +388,7 @@ typedef struct {
     const int32_t* block_tables; uint32_t max_blocks_per_seq;
     const int32_t* seq_lens; uint32_t num_blocks;
     uint32_t Hq, Hkv, Dqk, Dv, B; float scale;
+    uint32_t window; const float* sinks;
     int q_rope; float q_rope_theta; uint32_t q_rope_offset, q_rope_dim;
     const float* gate; float* out;
 } decode_ctx;
@@ -417,9 +430,16 @@ static void decode_range(void* p, uint64_t u0, uint64_t u1)
         double* sc = (double*)malloc(sizeof(double) * (size_t)n);
         unsigned char* ok = (unsigned char*)malloc((size_t)n);
         double m = -INFINITY;
+        /* Sliding window of W tokens (p1/p3 decode launchers take a
+         * sliding_window argument, semantics unstated; our reading): the query
+         * at position n-1 sees the W most recent tokens, positions
+         * [n - W, n); W = 0 means no window. */
+        int32_t lo = (c->window > 0 && (int64_t)n > (int64_t)c->window) ? n - (int32_t)c->window : 0;
         for (int32_t t = 0; t < n; ++t) {
             uint32_t b = (uint32_t)t / c->B;
             ok[t] = 0;
+            if (t < lo)
+                continue;                        /* outside the window */
             if (b >= c->max_blocks_per_seq)
                 continue;
             int32_t blk = c->block_tables[(uint64_t)s * c->max_blocks_per_seq + b];
@@ -447,6 +467,19 @@ static void decode_range(void* p, uint64_t u0, uint64_t u1)
             for (uint32_t d = 0; d < c->Dv; ++d)
                 o[d] += pt * cache_elem(c->v_cache, c->v_dtype, c->v_scale, voff + d);
         }
+        /* Attention sink (p1 mla_paged_decode_fp8 takes a `sinks` pointer,
+         * semantics unstated; our reading): one logit per query head, in the
+         * units of the scaled scores, that joins the softmax normalisation
+         * and carries no value, i.e. the denominator gains exp(sink - m).
+         * With no attended token the output stays zero. */
+        if (c->sinks && l > 0.0) {
+            double sk = (double)c->sinks[h];
+            double mm = sk > m ? sk : m;
+            double f = exp(m - mm);
+            l = l * f + exp(sk - mm);
+            for (uint32_t d = 0; d < c->Dv; ++d)
+                o[d] *= f;
+        }
         for (uint32_t d = 0; d < c->Dv; ++d) {
             double val = l > 0.0 ? o[d] / l : 0.0;
             /* optional elementwise output gate (p3 module doc: SDPA + gate) */
@@ -468,13 +501,14 @@ void pkvo_paged_decode(const void* q, int q_dtype, uint64_t q_seq_stride,
                        const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
                        uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
                        uint32_t head_dim_v, uint32_t block_size, float scale,
+                       uint32_t sliding_window, const float* sinks,
                        int q_rope, float q_rope_theta, uint32_t q_rope_offset,
                        uint32_t q_rope_dim, const float* gate, float* out, int nthreads)
 {
     decode_ctx c = {q, q_dtype, q_seq_stride, k_cache, k_dtype, k_scale, v_cache, v_dtype,
                     v_scale, block_tables, max_blocks_per_seq, seq_lens, num_blocks,
                     num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, block_size, scale,
-                    q_rope, q_rope_theta, q_rope_offset, q_rope_dim, gate, out};
+                    sliding_window, sinks, q_rope, q_rope_theta, q_rope_offset, q_rope_dim, gate, out};
     parallel_for((uint64_t)num_seqs * num_q_heads, nthreads, decode_range, &c);
 }
 

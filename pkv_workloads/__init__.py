@@ -231,26 +231,35 @@ def positions_decode(lay: Layout):
     return start, cu, start.copy()
 
 
-def random_pools(index: int, lay: Layout, poison_pad: bool = True):
+def e4m3_codes(index: int, stream: int, shape) -> np.ndarray:
+    """Random finite E4M3 codes with exponent field <= 9 (|value| <= 7.5),
+    random sign."""
+    r = rng(index, stream)
+    mag = r.integers(0, 0x50, size=shape).astype(np.uint8)
+    sign = (r.integers(0, 2, size=shape).astype(np.uint8) << 7).astype(np.uint8)
+    return (mag | sign).astype(np.uint8)
+
+
+def random_pools(index: int, lay: Layout, poison_pad: bool = True, v_dtype: str = None):
     """K and V pools [num_blocks, B, Hkv, D] filled directly with random
     values (decode tested on its own).  K is N(0,1) (BF16 or FP32; the FP8
-    pool holds random finite E4M3 codes); with ``poison_pad`` the padding
-    block is NaN.  Returns (k_pool, v_pool) as numpy arrays."""
+    pool holds random finite E4M3 codes); V likewise, or E4M3 codes with
+    ``v_dtype="fp8"``; with ``poison_pad`` the padding block is NaN.
+    Returns (k_pool, v_pool) as numpy arrays."""
     cfg = WORKLOADS[index]
     H, D, Dv, B = cfg["num_kv_heads"], cfg["head_dim"], cfg["head_dim_v"], cfg["block_size"]
     kshape = (lay.num_blocks, B, H, D)
     vshape = (lay.num_blocks, B, H, Dv)
     if cfg["k_cache_dtype"] == "fp8":
-        # random finite E4M3 codes with exponent field <= 9 (|value| <= 7.5)
-        r = rng(index, S_POOLK)
-        mag = r.integers(0, 0x50, size=kshape).astype(np.uint8)
-        sign = (r.integers(0, 2, size=kshape).astype(np.uint8) << 7).astype(np.uint8)
-        kp = (mag | sign).astype(np.uint8)
+        kp = e4m3_codes(index, S_POOLK, kshape)
     else:
         kx = normal(index, S_POOLK, kshape, outliers=(index == 3))
         kp = bf16_bits(kx) if cfg["k_cache_dtype"] == "bf16" else kx
-    vx = normal(index, S_POOLV, vshape)
-    vp = bf16_bits(vx) if cfg["kv_dtype"] == "bf16" else vx
+    if v_dtype == "fp8":
+        vp = e4m3_codes(index, S_POOLV, vshape)
+    else:
+        vx = normal(index, S_POOLV, vshape)
+        vp = bf16_bits(vx) if cfg["kv_dtype"] == "bf16" else vx
     if poison_pad and lay.pad_block >= 0:
         if kp.dtype == np.uint8:
             kp[lay.pad_block] = 0x7F
@@ -258,7 +267,9 @@ def random_pools(index: int, lay: Layout, poison_pad: bool = True):
             kp[lay.pad_block] = 0x7FC0
         else:
             kp[lay.pad_block] = np.nan
-        if vp.dtype == np.uint16:
+        if vp.dtype == np.uint8:
+            vp[lay.pad_block] = 0x7F
+        elif vp.dtype == np.uint16:
             vp[lay.pad_block] = 0x7FC0
         else:
             vp[lay.pad_block] = np.nan
