@@ -6,7 +6,7 @@
  *
  *   pkv_fill_slots          slot mapping from per-sequence block tables
  *   pkv_cache_write_k_fused RMSNorm -> RoPE -> one rounding, into the K pool
- *   pkv_cache_write_v       V reshape-and-cache copy into the V pool
+ *   pkv_cache_write_v       V reshape-and-cache copy (or E4M3 store) into the V pool
  *   pkv_paged_decode_attn   one-query-token GQA attention through the tables
  *
  * Sources (the pages this library implements):
@@ -40,7 +40,7 @@
  *   or one past the pool is skipped by the writes; a block-table entry
  *   outside [0, num_blocks) excludes its tokens from attention; seq_len <= 0
  *   gives an all-zero output row; table entries past ceil(seq_len /
- *   block_size) are never read.
+ *   block_size), and those wholly before a sliding window, are never read.
  * Alignment.  Cache rows and input rows are read and written in 16-byte
  *   pieces: every data pointer and every row stride (in bytes) must be a
  *   multiple of 16, else PKV_ERR_UNSUPPORTED.
@@ -151,82 +151,105 @@ int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype, uint64_t in_to
 /*
  * pkv_cache_write_v -- [p1] reshape_and_cache_flash_v_only: the V-only paged
  * cache write, companion of the fused K write so that the K side of the
- * cache is written by the fused kernel alone.
+ * cache is written by the fused kernel alone; with an E4M3 cache, the V half
+ * of [p1] reshape_and_cache_fp8 (K and V to FP8 with k_scale and v_scale).
  *
- * For each token t with 0 <= slot_mapping[t] < num_blocks * block_size:
- *   v_cache[slot, h, :] = v[t, h, :]  for every kv head h, byte for byte.
+ * For each token t with 0 <= slot_mapping[t] < num_blocks * block_size and
+ * every kv head h:
+ *   cache_dtype == in_dtype:  v_cache[slot, h, :] = v[t, h, :], byte for byte
+ *   cache_dtype == FP8_E4M3:  v_cache[slot, h, d] = saturating E4M3 of
+ *                             fl32(v[t, h, d] / v_scale) (correctly rounded
+ *                             FP32 division, then round-to-nearest-even;
+ *                             magnitudes above 448 become +-448, NaN stays NaN)
  *
- *   v             in  [num_tokens, num_kv_heads, head_dim_v] of dtype, token
+ *   v             in  [num_tokens, num_kv_heads, head_dim_v] of in_dtype, token
  *                     stride in_token_stride elements
  *   slot_mapping  in  int64 [num_tokens]
- *   v_cache       out [num_blocks, block_size, num_kv_heads, head_dim_v] of dtype
- * Supported: dtype BF16 or FP32; num_kv_heads * head_dim_v * sizeof(dtype)
- *   a multiple of 16 bytes.
+ *   v_cache       out [num_blocks, block_size, num_kv_heads, head_dim_v] of cache_dtype
+ *   v_scale           E4M3 cache only: per-tensor scale, finite and > 0
+ * Supported: (in_dtype, cache_dtype) (BF16, BF16), (FP32, FP32),
+ *   (BF16, FP8_E4M3), (FP32, FP8_E4M3); the cache row num_kv_heads *
+ *   head_dim_v elements a multiple of 16 bytes in both dtypes.
  */
-int pkv_cache_write_v(const void* v, pkv_dtype dtype, uint64_t in_token_stride,
+int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_token_stride,
                       const int64_t* slot_mapping, uint32_t num_tokens, uint32_t num_kv_heads,
                       uint32_t head_dim_v, uint32_t block_size, uint32_t num_blocks,
-                      void* v_cache, void* stream);
+                      void* v_cache, pkv_dtype cache_dtype, float v_scale, void* stream);
 
 /*
  * pkv_decode_workspace_bytes -- bytes of device workspace that
  * pkv_paged_decode_attn needs for these sizes (split-K partial results:
  * (head_dim_v + 2) FP32 per sequence, query head and split).  0 means none is
- * needed.  Depends only on the arguments given; split_tokens as for
- * pkv_paged_decode_attn.
+ * needed.  Depends only on the arguments given; sliding_window and
+ * split_tokens as for pkv_paged_decode_attn.
  */
 size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
                                   uint32_t num_kv_heads, uint32_t head_dim_v,
                                   uint32_t max_blocks_per_seq, uint32_t block_size,
-                                  uint32_t split_tokens);
+                                  uint32_t sliding_window, uint32_t split_tokens);
 
 /*
  * pkv_paged_decode_attn -- [p1] paged_decode_attn_fp8 and its BF16 sibling
  * (one query token per sequence, reading K/V through block_tables i32
  * [num_seqs * max_blocks_per_seq] and seq_lens i32 [num_seqs], GQA through
- * num_q_heads / num_kv_heads, scaled scores, FP8 K multiplied back by
- * k_scale), with the optional elementwise output gate of [p3] (SDPA + gate)
- * and the optional query rotation of [p3] (maybe_rope before SDPA).
+ * num_q_heads / num_kv_heads, scaled scores, FP8 K and V multiplied back by
+ * k_scale and v_scale), with the sliding window of the [p1] decode launchers
+ * and the attention sinks of [p1] mla_paged_decode_fp8, the optional
+ * elementwise output gate of [p3] (SDPA + gate) and the optional query
+ * rotation of [p3] (maybe_rope before SDPA).
  *
  * For sequence s, query head h, kv head g = h / (num_q_heads / num_kv_heads),
- * n = seq_lens[s], tokens t < n at row P * block_size + t % block_size with
- * P = block_tables[s][t / block_size]:
+ * n = seq_lens[s], attended tokens t in [lo, n) with lo = n - sliding_window
+ * when 0 < sliding_window < n, else 0, each at row P * block_size +
+ * t % block_size with P = block_tables[s][t / block_size]:
  *   q' = q[s, h, :], rotated at position n - 1 when q_rope != 0 (same RoPE
  *        as the K write over [q_rope_offset, q_rope_offset + q_rope_dim),
  *        theta q_rope_theta)
  *   s_t = scale * <q', k_t>, k_t = k_cache row (E4M3 codes times k_scale)
- *   out[s, h, :] = sum_t softmax(s)_t v_t   (times gate[s, h, :] if given)
- * Computed in FP32 with split-K over the token range and a log-sum-exp
- * merge; out is FP32.
+ *   Z   = sum_t exp(s_t) (+ exp(sinks[h]) when sinks is given)
+ *   out[s, h, :] = sum_t exp(s_t) / Z * v_t   (v_t: E4M3 codes times
+ *                  v_scale), times gate[s, h, :] if given
+ * The window and sink semantics are not stated by the pages; this is the
+ * reading taken: the window holds the sliding_window most recent tokens
+ * (0 = no window), and a sink is a per-query-head logit, in the units of
+ * s_t, that joins the normalisation and carries no value.  A sequence with
+ * no attended token gives an all-zero row.  Table entries of blocks wholly
+ * before the window are never read.  Computed in FP32 with split-K over the
+ * attended range and a log-sum-exp merge; out is FP32.
  *
  *   q             in  [num_seqs, num_q_heads, head_dim_qk] of q_dtype; sequence
  *                     s starts at element s * q_seq_stride
  *   k_cache       in  [num_blocks, block_size, num_kv_heads, head_dim_qk] of k_dtype
  *   v_cache       in  [num_blocks, block_size, num_kv_heads, head_dim_v] of v_dtype
+ *   k_scale, v_scale  E4M3 caches only: per-tensor scales, finite and > 0
  *   block_tables  in  int32 [num_seqs, max_blocks_per_seq]
  *   seq_lens      in  int32 [num_seqs]; tokens past max_blocks_per_seq *
  *                     block_size are excluded
+ *   sliding_window    tokens in the window, 0 = attend to all
+ *   sinks         in  FP32 [num_q_heads] or NULL
  *   gate          in  FP32 [num_seqs, num_q_heads, head_dim_v] or NULL
  *   out           out FP32 [num_seqs, num_q_heads, head_dim_v]
  *   split_tokens  tokens per split-K piece, rounded up to whole blocks and
- *                 capped at 64 blocks; 0 = the library's choice (enough pieces
- *                 to cover the GPU several times over).  The result does not
- *                 depend on it beyond FP32 rounding.
+ *                 capped at 128 blocks; 0 = the library's choice (enough
+ *                 pieces to cover the GPU several times over).  The result
+ *                 does not depend on it beyond FP32 rounding.
  *   workspace     device scratch of at least
  *                 pkv_decode_workspace_bytes(...) bytes (may be NULL if that is 0)
- * Supported: (q, K, V) dtypes (BF16, BF16, BF16), (BF16, FP8_E4M3, BF16),
+ * Supported: (q, K, V) dtypes (BF16, BF16 or FP8_E4M3, BF16 or FP8_E4M3),
  *   (FP32, FP32, FP32); num_q_heads % num_kv_heads == 0; block_size 16;
- *   head_dim_qk in {64, 128, 192, 256}, head_dim_v in {64, 128} (BF16 caches:
- *   head_dim_qk == head_dim_v in {64, 128}); q_rope_dim even with
+ *   head_dim_qk in {64, 128, 192, 256}, head_dim_v in {64, 128} (BF16/E4M3
+ *   caches: head_dim_qk == head_dim_v in {64, 128}, GQA group <= 16; FP32:
+ *   group 1, 2, 4 or 8); q_rope (FP32 only) with q_rope_dim even and
  *   q_rope_offset + q_rope_dim <= head_dim_qk.
  */
 int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
                           const void* k_cache, pkv_dtype k_dtype, float k_scale,
-                          const void* v_cache, pkv_dtype v_dtype,
+                          const void* v_cache, pkv_dtype v_dtype, float v_scale,
                           const int32_t* block_tables, uint32_t max_blocks_per_seq,
                           const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
                           uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
                           uint32_t head_dim_v, uint32_t block_size, float scale,
+                          uint32_t sliding_window, const float* sinks,
                           int q_rope, float q_rope_theta, uint32_t q_rope_offset,
                           uint32_t q_rope_dim, const float* gate, float* out,
                           uint32_t split_tokens, void* workspace, size_t workspace_bytes,

@@ -36,11 +36,12 @@ _SIGNATURES = {
     "pkv_fill_slots": ([_P, _P, _U32, _P, _P, _U32, _U32, _U32, _P], _I32),
     "pkv_cache_write_k_fused": ([_P, _I32, _U64, _P, _F32, _P, _P, _P, _F32, _U32, _U32, _I32,
                                  _P, _U32, _U32, _U32, _U32, _U32, _P, _I32, _F32, _P], _I32),
-    "pkv_cache_write_v": ([_P, _I32, _U64, _P, _U32, _U32, _U32, _U32, _U32, _P, _P], _I32),
-    "pkv_decode_workspace_bytes": ([_U32, _U32, _U32, _U32, _U32, _U32, _U32], _SZ),
-    "pkv_paged_decode_attn": ([_P, _I32, _U64, _P, _I32, _F32, _P, _I32, _P, _U32, _P, _U32,
-                               _U32, _U32, _U32, _U32, _U32, _U32, _F32, _I32, _F32, _U32,
-                               _U32, _P, _P, _U32, _P, _SZ, _P], _I32),
+    "pkv_cache_write_v": ([_P, _I32, _U64, _P, _U32, _U32, _U32, _U32, _U32, _P, _I32, _F32,
+                           _P], _I32),
+    "pkv_decode_workspace_bytes": ([_U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32], _SZ),
+    "pkv_paged_decode_attn": ([_P, _I32, _U64, _P, _I32, _F32, _P, _I32, _F32, _P, _U32, _P,
+                               _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32, _U32, _P, _I32,
+                               _F32, _U32, _U32, _P, _P, _U32, _P, _SZ, _P], _I32),
 }
 
 
@@ -172,40 +173,42 @@ def cache_write_k_fused(k_in, slot_mapping, k_cache, *, norm_weight=None, eps: f
     return k_cache
 
 
-def cache_write_v(v, slot_mapping, v_cache):
-    """Byte copy of V rows into the V pool at their slots (pkv_cache_write_v)."""
+def cache_write_v(v, slot_mapping, v_cache, v_scale: float = 1.0):
+    """V rows into the V pool at their slots (pkv_cache_write_v): a byte copy
+    when the pool has v's dtype, E4M3 of v / v_scale for an FP8 pool."""
     _dev(v, slot_mapping, v_cache)
     nb, B, H, D = _pool(v_cache, "v_cache")
     T = v.shape[0]
-    if v.shape[1:] != (H, D) or v.dtype != v_cache.dtype:
-        raise ValueError("v [T, Hkv, Dv] must match the pool's shape and dtype")
+    if v.shape[1:] != (H, D):
+        raise ValueError("v [T, Hkv, Dv] must match the pool's shape")
     if slot_mapping.numel() != T or slot_mapping.dtype != torch.int64:
         raise ValueError("slot_mapping must be int64 [T]")
     stride = _token_stride(v, "v")
     _check(load().pkv_cache_write_v(_ptr(v), _dtype(v), stride, _ptr(slot_mapping), T, H, D, B,
-                                    nb, _ptr(v_cache), _stream()))
+                                    nb, _ptr(v_cache), _dtype(v_cache), v_scale, _stream()))
     return v_cache
 
 
 def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim_v, max_blocks_per_seq,
-                           block_size=16, split_tokens=0) -> int:
+                           block_size=16, split_tokens=0, sliding_window=0) -> int:
     return int(load().pkv_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads,
                                                  head_dim_v, max_blocks_per_seq, block_size,
-                                                 split_tokens))
+                                                 sliding_window, split_tokens))
 
 
 def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: float,
-                      k_scale: float = 1.0, gate=None, out=None, q_rope: bool = False,
+                      k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0,
+                      sinks=None, gate=None, out=None, q_rope: bool = False,
                       q_rope_theta: float = 10000.0, q_rope_offset: int = 0,
                       q_rope_dim: int = 0, split_tokens: int = 0, workspace=None):
     """One-query-token paged decode attention (pkv_paged_decode_attn).
 
     q [S, Hq, Dqk]; k_cache [nb, B, Hkv, Dqk]; v_cache [nb, B, Hkv, Dv];
-    block_tables int32 [S, M]; seq_lens int32 [S]; gate FP32 [S, Hq, Dv] or
-    None.  Returns out FP32 [S, Hq, Dv].  ``workspace`` (uint8 device tensor)
-    is allocated here when not given.
+    block_tables int32 [S, M]; seq_lens int32 [S]; sinks FP32 [Hq] or None;
+    gate FP32 [S, Hq, Dv] or None.  Returns out FP32 [S, Hq, Dv].
+    ``workspace`` (uint8 device tensor) is allocated here when not given.
     """
-    _dev(q, k_cache, v_cache, block_tables, seq_lens, gate, out, workspace)
+    _dev(q, k_cache, v_cache, block_tables, seq_lens, sinks, gate, out, workspace)
     nb, B, Hkv, Dqk = _pool(k_cache, "k_cache")
     nb2, B2, Hkv2, Dv = _pool(v_cache, "v_cache")
     if (nb2, B2, Hkv2) != (nb, B, Hkv):
@@ -221,19 +224,23 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: flo
     if gate is not None and (gate.dtype != torch.float32 or gate.shape != (S, Hq, Dv) or
                              not gate.is_contiguous()):
         raise ValueError("gate must be FP32 [S, Hq, Dv] contiguous")
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != Hq or
+                              not sinks.is_contiguous()):
+        raise ValueError("sinks must be FP32 [Hq] contiguous")
     if out is None:
         out = torch.empty((S, Hq, Dv), dtype=torch.float32, device=q.device)
     elif out.dtype != torch.float32 or out.shape != (S, Hq, Dv) or not out.is_contiguous():
         raise ValueError("out must be FP32 [S, Hq, Dv] contiguous")
     M = block_tables.shape[1]
-    need = decode_workspace_bytes(S, Hq, Hkv, Dv, M, B, split_tokens) if S else 0
+    need = decode_workspace_bytes(S, Hq, Hkv, Dv, M, B, split_tokens, sliding_window) if S else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     q_stride = q.stride(0) if S > 1 else Hq * Dqk
     _check(load().pkv_paged_decode_attn(
         _ptr(q), _dtype(q), q_stride, _ptr(k_cache), _dtype(k_cache), k_scale, _ptr(v_cache),
-        _dtype(v_cache), _ptr(block_tables), M, _ptr(seq_lens), S, nb, Hq, Hkv, Dqk, Dv, B,
-        scale, int(bool(q_rope)), q_rope_theta, q_rope_offset, q_rope_dim, _ptr(gate), _ptr(out),
+        _dtype(v_cache), v_scale, _ptr(block_tables), M, _ptr(seq_lens), S, nb, Hq, Hkv, Dqk, Dv,
+        B, scale, sliding_window, _ptr(sinks), int(bool(q_rope)), q_rope_theta, q_rope_offset,
+        q_rope_dim, _ptr(gate), _ptr(out),
         split_tokens, _ptr(workspace), ws_bytes, _stream()))
     return out

@@ -113,30 +113,11 @@ __device__ __forceinline__ void store_chunk(void* cache, uint64_t elem, const fl
             __builtin_nontemporal_store(u32x2{w[0], w[1]}, (u32x2*)p);
         }
     } else if constexpr (OUT == OUT_FP8) {
-        // y already carries the 1/k_scale factor (folded into the row scale):
-        // clamp finite and infinite magnitudes to 448 (v_med3), then round
-        float z[VEC];
-        bool any_nan = false;
-#pragma unroll
-        for (int i = 0; i < VEC; ++i) {
-            any_nan |= y[i] != y[i];
-            z[i] = __builtin_amdgcn_fmed3f(y[i], -448.0f, 448.0f);
-        }
+        // y already carries the 1/k_scale factor (folded into the row scale)
         uint32_t w[VEC / 4];
 #pragma unroll
         for (int j = 0; j < VEC / 4; ++j)
-            w[j] = pack_e4m3x4(z[4 * j], z[4 * j + 1], z[4 * j + 2], z[4 * j + 3]);
-        if (any_nan) {
-            // NaN is stored as the E4M3FN NaN code S.1111.111 with its sign
-#pragma unroll
-            for (int i = 0; i < VEC; ++i) {
-                if (y[i] != y[i]) {
-                    const uint32_t sh = 8u * (i % 4);
-                    const uint32_t code = 0x7Fu | ((__float_as_uint(y[i]) >> 24) & 0x80u);
-                    w[i / 4] = (w[i / 4] & ~(0xFFu << sh)) | (code << sh);
-                }
-            }
-        }
+            w[j] = e4m3_sat_x4(y[4 * j], y[4 * j + 1], y[4 * j + 2], y[4 * j + 3]);
         uint8_t* p = (uint8_t*)cache + elem;
         if constexpr (VEC == 8) {
             __builtin_nontemporal_store(u32x2{w[0], w[1]}, (u32x2*)p);

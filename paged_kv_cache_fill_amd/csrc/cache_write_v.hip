@@ -1,6 +1,8 @@
 // cache_write_v.hip -- pkv_cache_write_v: the V reshape-and-cache copy
 // (page 1, kv_cache.rs, reshape_and_cache_flash_v_only: V rows copied into
-// the paged V pool at slot_mapping, leaving the K side to the fused K write).
+// the paged V pool at slot_mapping, leaving the K side to the fused K write),
+// and its E4M3 form (page 1, reshape_and_cache_fp8: V stored as FP8 with a
+// per-tensor v_scale).
 //
 // A token's V row (num_kv_heads * head_dim_v elements) is contiguous in the
 // input and, under the [num_blocks, block_size, Hkv, Dv] layout, contiguous
@@ -52,12 +54,72 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_kernel(
     }
 }
 
+// E4M3 store: each thread owns 16 consecutive elements of the row (one
+// 16-byte column of the E4M3 row; 2 or 4 16-byte loads of the input) and
+// walks kVRun tokens the same way.  v / v_scale is a correctly rounded FP32
+// division, so the stored code is the E4M3 rounding of fl32(v / v_scale).
+template <int IN>   // 0 = BF16 input, 2 = FP32 input
+__global__ __launch_bounds__(kVThreads) void cache_write_v_e4m3_kernel(
+    const u32x4* __restrict__ v, uint64_t in_stride16, const int64_t* __restrict__ slots,
+    uint32_t num_tokens, uint32_t cols, uint32_t tpb, uint64_t num_slots, float v_scale,
+    u32x4* __restrict__ cache)
+{
+    constexpr int NLD = IN == 0 ? 2 : 4;                // input loads per 16 elements
+    const uint32_t lane_tok = threadIdx.x / cols;
+    const uint32_t col0 = threadIdx.x % cols;
+    if (lane_tok >= tpb)
+        return;
+    const uint32_t col_step = cols < kVThreads ? cols : kVThreads;
+    const uint64_t base = (uint64_t)blockIdx.x * tpb * kVRun;
+    int64_t slot[kVRun];
+    uint64_t tok[kVRun];
+#pragma unroll
+    for (int r = 0; r < kVRun; ++r) {
+        tok[r] = base + (uint64_t)r * tpb + lane_tok;
+        int64_t s = tok[r] < num_tokens ? slots[tok[r]] : -1;
+        slot[r] = (s >= 0 && (uint64_t)s < num_slots) ? s : -1;
+    }
+    for (uint32_t c = col0; c < cols; c += col_step) {
+        u32x4 buf[kVRun][NLD];
+#pragma unroll
+        for (int r = 0; r < kVRun; ++r)
+            if (slot[r] >= 0)
+#pragma unroll
+                for (int j = 0; j < NLD; ++j)
+                    buf[r][j] = load_nt(v + tok[r] * in_stride16 + (uint64_t)c * NLD + j);
+#pragma unroll
+        for (int r = 0; r < kVRun; ++r) {
+            if (slot[r] < 0)
+                continue;
+            float x[16];
+#pragma unroll
+            for (int j = 0; j < NLD; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if constexpr (IN == 0) {
+                        x[8 * j + 2 * e] = bf16_lo(buf[r][j][e]);
+                        x[8 * j + 2 * e + 1] = bf16_hi(buf[r][j][e]);
+                    } else {
+                        x[4 * j + e] = __uint_as_float(buf[r][j][e]);
+                    }
+                }
+            u32x4 w;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                w[q] = e4m3_sat_x4(x[4 * q] / v_scale, x[4 * q + 1] / v_scale,
+                                   x[4 * q + 2] / v_scale, x[4 * q + 3] / v_scale);
+            store_nt(cache + (uint64_t)slot[r] * cols + c, w);
+        }
+    }
+}
+
 }  // namespace pkv
 
-extern "C" int pkv_cache_write_v(const void* v, pkv_dtype dtype, uint64_t in_token_stride,
+extern "C" int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_token_stride,
                                  const int64_t* slot_mapping, uint32_t num_tokens,
                                  uint32_t num_kv_heads, uint32_t head_dim_v, uint32_t block_size,
-                                 uint32_t num_blocks, void* v_cache, void* stream)
+                                 uint32_t num_blocks, void* v_cache, pkv_dtype cache_dtype,
+                                 float v_scale, void* stream)
 {
     using namespace pkv;
     clear_error();
@@ -65,31 +127,49 @@ extern "C" int pkv_cache_write_v(const void* v, pkv_dtype dtype, uint64_t in_tok
         return PKV_OK;
     if (!v || !slot_mapping || !v_cache)
         return fail(PKV_ERR_INVALID, "cache_write_v: v, slot_mapping and v_cache must be non-NULL");
-    if (!valid_dtype(dtype))
-        return fail(PKV_ERR_INVALID, "cache_write_v: bad dtype %d", (int)dtype);
-    if (dtype != PKV_BF16 && dtype != PKV_FP32)
-        return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: dtype must be BF16 or FP32");
+    if (!valid_dtype(in_dtype) || !valid_dtype(cache_dtype))
+        return fail(PKV_ERR_INVALID, "cache_write_v: bad dtype (%d, %d)", (int)in_dtype,
+                    (int)cache_dtype);
+    if (in_dtype != PKV_BF16 && in_dtype != PKV_FP32)
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: input dtype must be BF16 or FP32");
+    if (cache_dtype != in_dtype && cache_dtype != PKV_FP8_E4M3)
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: cache dtype must be the input's or E4M3");
+    const bool e4m3 = cache_dtype == PKV_FP8_E4M3;
+    if (e4m3 && !(v_scale > 0.0f && v_scale < INFINITY))
+        return fail(PKV_ERR_INVALID, "cache_write_v: v_scale must be finite and > 0");
     if (num_kv_heads == 0 || head_dim_v == 0 || block_size == 0 || num_blocks == 0)
         return fail(PKV_ERR_INVALID, "cache_write_v: zero dimension");
     const uint64_t row_elems = (uint64_t)num_kv_heads * head_dim_v;
-    const uint64_t row_bytes = row_elems * dtype_size(dtype);
+    const uint64_t row_bytes = row_elems * dtype_size(in_dtype);
+    const uint64_t cache_row_bytes = row_elems * dtype_size(cache_dtype);
     if (in_token_stride < row_elems)
         return fail(PKV_ERR_INVALID, "cache_write_v: in_token_stride %llu < row of %llu elements",
                     (unsigned long long)in_token_stride, (unsigned long long)row_elems);
-    const uint64_t stride_bytes = in_token_stride * dtype_size(dtype);
-    if (row_bytes % 16 || stride_bytes % 16 || !aligned16(v) || !aligned16(v_cache))
+    const uint64_t stride_bytes = in_token_stride * dtype_size(in_dtype);
+    if (row_bytes % 16 || cache_row_bytes % 16 || stride_bytes % 16 || !aligned16(v) ||
+        !aligned16(v_cache))
         return fail(PKV_ERR_UNSUPPORTED,
                     "cache_write_v: rows, strides and pointers must be 16-byte aligned");
-    const uint64_t cols64 = row_bytes / 16;
+    const uint64_t cols64 = cache_row_bytes / 16;   // 16-byte columns of the cache row
     if (cols64 > (1u << 24))
         return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: row too long");
     const uint32_t cols = (uint32_t)cols64;
     const uint32_t tpb = cols <= (uint32_t)kVThreads ? (uint32_t)kVThreads / cols : 1u;
     const uint64_t per_block = (uint64_t)tpb * kVRun;
     const uint64_t blocks = (num_tokens + per_block - 1) / per_block;
-    hipLaunchKernelGGL(cache_write_v_kernel, dim3((uint32_t)blocks), dim3(kVThreads), 0,
-                       (hipStream_t)stream, (const u32x4*)v, stride_bytes / 16, slot_mapping,
-                       num_tokens, cols, tpb, (uint64_t)num_blocks * block_size,
-                       (u32x4*)v_cache);
+    const uint64_t num_slots = (uint64_t)num_blocks * block_size;
+    hipStream_t st = (hipStream_t)stream;
+    if (!e4m3)
+        hipLaunchKernelGGL(cache_write_v_kernel, dim3((uint32_t)blocks), dim3(kVThreads), 0, st,
+                           (const u32x4*)v, stride_bytes / 16, slot_mapping, num_tokens, cols,
+                           tpb, num_slots, (u32x4*)v_cache);
+    else if (in_dtype == PKV_BF16)
+        hipLaunchKernelGGL(cache_write_v_e4m3_kernel<0>, dim3((uint32_t)blocks), dim3(kVThreads),
+                           0, st, (const u32x4*)v, stride_bytes / 16, slot_mapping, num_tokens,
+                           cols, tpb, num_slots, v_scale, (u32x4*)v_cache);
+    else
+        hipLaunchKernelGGL(cache_write_v_e4m3_kernel<2>, dim3((uint32_t)blocks), dim3(kVThreads),
+                           0, st, (const u32x4*)v, stride_bytes / 16, slot_mapping, num_tokens,
+                           cols, tpb, num_slots, v_scale, (u32x4*)v_cache);
     return check_launch("cache_write_v");
 }

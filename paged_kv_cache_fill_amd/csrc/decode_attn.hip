@@ -2,7 +2,11 @@
 // attention with GQA, split-K over the token range and a log-sum-exp merge
 // (page 1, kv_cache.rs, paged_decode_attn_fp8 and its BF16 sibling: Q, K/V
 // pools, block_tables i32, seq_lens i32, num_q_heads / num_kv_heads,
-// inv_sqrt_d, k_scale; page 3, mla_cuda.rs: RoPE on q then SDPA + gate).
+// inv_sqrt_d, k_scale, v_scale; the sliding_window of its decode launchers
+// and the sinks of mla_paged_decode_fp8; page 3, mla_cuda.rs: RoPE on q
+// then SDPA + gate).  The attended range of a sequence of n tokens is
+// [n - W, n) for a window of W tokens (W = 0: all of it); a sink adds
+// exp(sink) to the softmax denominator of its query head.
 //
 // Work decomposition.  A work-group handles one (sequence, split) pair for
 // a group of kv heads, one wavefront per kv head; a split is `chunk_blocks`
@@ -21,7 +25,9 @@
 // loads 16 contiguous bytes; V's columns are permuted so that a lane's 16-byte
 // load feeds all eight N-tiles.  P is split into hi + lo BF16 parts (two PV
 // MFMAs), which keeps the weights to ~16 bits; BF16 q x BF16 (or E4M3) K
-// products are exact in FP32.  Online softmax runs in the log2 domain.
+// products are exact in FP32.  E4M3 V codes are widened exactly to BF16 for
+// the PV product and v_scale is applied with the final normalisation.
+// Online softmax runs in the log2 domain.
 //
 // FP32 caches (VALU path).  Four tokens per wave step (16 lanes per token
 // row, 16-byte loads), one online-softmax stream per row, merged at the end.
@@ -48,6 +54,7 @@ struct DecodeArgs {
     const int32_t* bt;
     const int32_t* seq_lens;
     const float* gate;
+    const float* sinks;     // [Hq] logits, or NULL
     float* out;
     float* part_o;          // [S][max_splits][Hq][Dv]
     float* part_ml;         // [S][max_splits][Hq][2]  (max in log2 units, sum)
@@ -58,6 +65,8 @@ struct DecodeArgs {
     uint32_t chunk_blocks;
     uint32_t max_splits;
     float qk_scale;         // scale * log2(e) (* k_scale for E4M3 K)
+    float out_scale;        // v_scale for E4M3 V, else 1
+    uint32_t window;        // sliding window in tokens, 0 = none
     // query rotation (FP32 path)
     uint32_t q_rope;
     float q_rope_theta;
@@ -73,6 +82,40 @@ __device__ __forceinline__ uint32_t seq_blocks(int32_t n, uint32_t M)
 {
     const uint32_t nb = n > 0 ? ((uint32_t)n + kBS - 1) / kBS : 0;
     return nb < M ? nb : M;
+}
+
+// Attended tokens [lo, n) of a sequence and the cache blocks [blo, nblk)
+// that hold them; split i covers blocks blo + i * chunk_blocks onwards.
+struct SeqRange {
+    int32_t n, lo;
+    uint32_t blo, nblk, nsplit;
+};
+__device__ __forceinline__ SeqRange seq_range(const DecodeArgs& a, uint32_t s)
+{
+    SeqRange r;
+    r.n = a.seq_lens[s];
+    r.nblk = seq_blocks(r.n, a.M);
+    r.lo = (a.window > 0 && r.n > (int32_t)a.window) ? r.n - (int32_t)a.window : 0;
+    r.blo = (uint32_t)r.lo / kBS;
+    r.nsplit = r.nblk > r.blo ? (r.nblk - r.blo + a.chunk_blocks - 1) / a.chunk_blocks : 0;
+    return r;
+}
+
+// Normalisation factor of a finished row: out = o * norm_factor(...).  With
+// a sink (log2 units sk2) the denominator l 2^m gains 2^sk2; a row with no
+// attended token (l = 0) stays zero.
+__device__ __forceinline__ float norm_factor(float m, float l, const float* sinks, uint32_t h,
+                                             float out_scale)
+{
+    if (!(l > 0.f))
+        return 0.f;
+    if (sinks) {
+        const float sk2 = sinks[h] * kLog2e;
+        const float mm = fmaxf(m, sk2);
+        const float f = __builtin_amdgcn_exp2f(m - mm);
+        return f * out_scale / (l * f + __builtin_amdgcn_exp2f(sk2 - mm));
+    }
+    return out_scale / l;
 }
 
 __device__ __forceinline__ float wave_max_xor16_32(float v)
@@ -119,7 +162,7 @@ __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint3
         const uint32_t h = kvh * a.G + g;
         float vals[NT];
         if (nsplit == 1) {
-            const float inv = lg > 0.f ? 1.0f / lg : 0.f;
+            const float inv = norm_factor(mg, lg, a.sinks, h, a.out_scale);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
                 vals[nt] = o[nt][r] * inv;
@@ -146,7 +189,8 @@ __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint3
 
 // ------------------------------------------------------------------ MFMA path
 
-// KT: 0 = BF16 K, 1 = E4M3 K.  D: head dim of q, K and V (64 or 128).
+// KT, VT: 0 = BF16, 1 = E4M3 (K and V caches).  D: head dim of q, K and V
+// (64 or 128).
 //
 // K reaches the MFMA in two steps.  (1) Coalesced loads: a K row of one head
 // is CPR 16-byte chunks; load j of a lane covers row j * (64 / CPR) + lane /
@@ -196,7 +240,7 @@ struct KFrag {
     }
 };
 
-template <int KT, int D, int PF>
+template <int KT, int VT, int D, int PF>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t kv_groups)
 {
     using KF = KFrag<KT, D>;
@@ -204,7 +248,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     __shared__ u32x4 s_k[8][16 * KF::CPR];          // one K tile per wave
     constexpr int NT = D / 16;                 // PV N-tiles
     constexpr int DPL = D / 16;                // V dims per lane
-    constexpr int VW = DPL / 2;                // V words per lane per token (4 or 2)
+    constexpr uint32_t VES = VT == 0 ? 2 : 1;  // V element bytes
+    constexpr int VW = DPL * VES / 4;          // V words per lane per token (4, 2 or 1)
     constexpr uint32_t KES = KT == 0 ? 2 : 1;  // K element bytes
 
     const int lane = threadIdx.x & 63;
@@ -223,19 +268,19 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     if (kvh >= a.Hkv)
         return;
 
-    const int32_t n = a.seq_lens[s];
-    const uint32_t nblk = seq_blocks(n, a.M);
-    const uint32_t b0 = split * a.chunk_blocks;
-    if (b0 >= nblk) {
-        if (n <= 0 && split == 0) {
-            // empty sequence: zero output rows of this kv head's group
+    const SeqRange R = seq_range(a, s);
+    const int32_t n = R.n;
+    const uint32_t nsplit = R.nsplit;
+    const uint32_t b0 = R.blo + split * a.chunk_blocks;
+    if (split >= nsplit) {
+        if (nsplit == 0 && split == 0) {
+            // nothing attended: zero output rows of this kv head's group
             for (uint32_t idx = lane; idx < a.G * D; idx += 64)
                 a.out[((uint64_t)s * a.Hq + kvh * a.G) * D + idx] = 0.f;
         }
         return;
     }
-    const uint32_t b1 = min(b0 + a.chunk_blocks, nblk);
-    const uint32_t nsplit = (nblk + a.chunk_blocks - 1) / a.chunk_blocks;
+    const uint32_t b1 = min(b0 + a.chunk_blocks, R.nblk);
 
     // q fragments: B operand of S^T = K q^T; lane (g = ln, kg)
     bf16x8 qf[NI];
@@ -267,7 +312,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     };
 
     const uint8_t* kbase = (const uint8_t*)a.k_cache;
-    const uint16_t* vbase = (const uint16_t*)a.v_cache;
+    const uint8_t* vbase = (const uint8_t*)a.v_cache;
     const uint64_t krow_stride = (uint64_t)a.Hkv * D * KES;   // bytes per cache row
     const uint64_t vrow_stride = (uint64_t)a.Hkv * D;         // elements per cache row
 
@@ -287,7 +332,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     // to that block); each lane's byte offsets inside a block are
     // loop-invariant 32-bit values.
     const uint32_t kblk_bytes = (uint32_t)(kBS * krow_stride);
-    const uint32_t vblk_bytes = (uint32_t)(kBS * vrow_stride * 2);
+    const uint32_t vblk_bytes = (uint32_t)(kBS * vrow_stride * VES);
     const uint32_t koff = (uint32_t)((lane / KF::CPR) * krow_stride + (uint64_t)kvh * D * KES +
                                      16 * (lane % KF::CPR));
     const uint32_t kstep = (uint32_t)(KF::RPL * krow_stride);     // next load: RPL rows down
@@ -299,8 +344,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         lds_r[j] = KF::lds_off(ln, KF::op_chunk(j, kg));
     }
     uint8_t* ktile = (uint8_t*)&s_k[wave][0];
-    const uint32_t voff = (uint32_t)((4 * kg) * vrow_stride * 2 + ((uint64_t)kvh * D + DPL * ln) * 2);
-    const uint32_t vrow_bytes = (uint32_t)(vrow_stride * 2);
+    const uint32_t voff = (uint32_t)((4 * kg) * vrow_stride * VES + ((uint64_t)kvh * D + DPL * ln) * VES);
+    const uint32_t vrow_bytes = (uint32_t)(vrow_stride * VES);
 
     // An unmapped block is read from block 0 instead (always inside the pool):
     // compute_block masks all of its tokens, so what it holds never counts.
@@ -310,7 +355,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(kbase + (uint64_t)pb * kblk_bytes), 0, (int)kblk_bytes, kBufferFlags);
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)((const uint8_t*)vbase + (uint64_t)pb * vblk_bytes), 0, (int)vblk_bytes, kBufferFlags);
+            (void*)(vbase + (uint64_t)pb * vblk_bytes), 0, (int)vblk_bytes, kBufferFlags);
 #pragma unroll
         for (int j = 0; j < NL; ++j) {                                    // K: token t = ln
             const u32x4 w = __builtin_bit_cast(
@@ -323,10 +368,12 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
                 const u32x4 t4 = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, r * vrow_bytes, kNT));
                 st.v[r][0] = t4[0]; st.v[r][1] = t4[1]; st.v[r][2] = t4[2]; st.v[r][3] = t4[3];
-            } else {
+            } else if constexpr (VW == 2) {
                 const u32x2 t2 = __builtin_bit_cast(
                     u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr, voff, r * vrow_bytes, kNT));
                 st.v[r][0] = t2[0]; st.v[r][1] = t2[1];
+            } else {
+                st.v[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, voff, r * vrow_bytes, kNT);
             }
         }
     };
@@ -336,6 +383,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         const bool blk_ok = pb >= 0 && (uint32_t)pb < a.num_blocks;
         const int32_t rem = n - (int32_t)(bi * kBS);
         const int ntok = blk_ok ? (rem < kBS ? rem : kBS) : 0;
+        const int tlo = R.lo - (int32_t)(bi * kBS);   // tokens below it are outside the window
 
         // K rows -> MFMA operand layout through the wave's LDS tile (lanes
         // exchange data: order the writes after the previous block's reads
@@ -364,7 +412,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = 4 * kg + r;
-            sv[r] = t < ntok ? sacc[r] * a.qk_scale : -INFINITY;
+            sv[r] = (t < ntok && t >= tlo) ? sacc[r] * a.qk_scale : -INFINITY;
             mx = fmaxf(mx, sv[r]);
         }
         mx = wave_max_xor16_32(mx);
@@ -401,26 +449,48 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         const i16x4 a_hi = __builtin_bit_cast(i16x4, u32x2{ph[0], ph[1]});
         const i16x4 a_lo = __builtin_bit_cast(i16x4, u32x2{pl[0], pl[1]});
 
-        // tokens past the sequence end must not bring NaN/Inf into 0 * V
-        if (ntok < kBS) {
+        // masked tokens must not bring NaN/Inf into 0 * V
+        if (ntok < kBS || tlo > 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (4 * kg + r >= ntok)
+                if (4 * kg + r >= ntok || 4 * kg + r < tlo)
 #pragma unroll
                     for (int w = 0; w < VW; ++w)
                         st.v[r][w] = 0u;
         }
 
+        // B operand of N-tile nt: element nt of the lane's DPL columns, rows
+        // t = 4kg + 0..3; E4M3 codes are widened to FP32 (exact) and their
+        // upper halves are the BF16 values
+        [[maybe_unused]] float vf[4][DPL];
+        if constexpr (VT == 1) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int w = 0; w < VW; ++w) {
+                    const f32x2 lo = unpack_e4m3x2(st.v[r][w], false);
+                    const f32x2 hi = unpack_e4m3x2(st.v[r][w], true);
+                    vf[r][4 * w] = lo.x;
+                    vf[r][4 * w + 1] = lo.y;
+                    vf[r][4 * w + 2] = hi.x;
+                    vf[r][4 * w + 3] = hi.y;
+                }
+        }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const int w = nt >> 1;
             uint32_t b01, b23;
-            if (nt & 1) {
-                b01 = hi16_pair(st.v[0][w], st.v[1][w]);
-                b23 = hi16_pair(st.v[2][w], st.v[3][w]);
+            if constexpr (VT == 1) {
+                b01 = hi16_pair(__float_as_uint(vf[0][nt]), __float_as_uint(vf[1][nt]));
+                b23 = hi16_pair(__float_as_uint(vf[2][nt]), __float_as_uint(vf[3][nt]));
             } else {
-                b01 = lo16_pair(st.v[0][w], st.v[1][w]);
-                b23 = lo16_pair(st.v[2][w], st.v[3][w]);
+                const int w = nt >> 1;
+                if (nt & 1) {
+                    b01 = hi16_pair(st.v[0][w], st.v[1][w]);
+                    b23 = hi16_pair(st.v[2][w], st.v[3][w]);
+                } else {
+                    b01 = lo16_pair(st.v[0][w], st.v[1][w]);
+                    b23 = lo16_pair(st.v[2][w], st.v[3][w]);
+                }
             }
             const i16x4 bv = __builtin_bit_cast(i16x4, u32x2{b01, b23});
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bv, o[nt], 0, 0, 0);
@@ -477,17 +547,17 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
     const uint32_t s = blockIdx.y;
     const uint32_t split = blockIdx.z;
 
-    const int32_t n = a.seq_lens[s];
-    const uint32_t nblk = seq_blocks(n, a.M);
-    const uint32_t b0 = split * a.chunk_blocks;
-    if (b0 >= nblk) {
-        if (n <= 0 && split == 0)
+    const SeqRange R = seq_range(a, s);
+    const int32_t n = R.n;
+    const uint32_t nsplit = R.nsplit;
+    const uint32_t b0 = R.blo + split * a.chunk_blocks;
+    if (split >= nsplit) {
+        if (nsplit == 0 && split == 0)
             for (uint32_t idx = lane; idx < (uint32_t)G * DV; idx += 64)
                 a.out[((uint64_t)s * a.Hq + kvh * G) * DV + idx] = 0.f;
         return;
     }
-    const uint32_t b1 = min(b0 + a.chunk_blocks, nblk);
-    const uint32_t nsplit = (nblk + a.chunk_blocks - 1) / a.chunk_blocks;
+    const uint32_t b1 = min(b0 + a.chunk_blocks, R.nblk);
 
     // q rows of the group into LDS, rotated at position n - 1 if asked
     const float* qsrc = (const float*)a.q + (uint64_t)s * a.q_stride + (uint64_t)kvh * G * DQK;
@@ -535,7 +605,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
     for (uint32_t t0 = b0 * kBS; t0 < t_end; t0 += 4) {
         const uint32_t t = t0 + row;
         const int32_t pb = a.bt[(uint64_t)s * a.M + t / kBS];
-        const bool ok = t < t_end && pb >= 0 && (uint32_t)pb < a.num_blocks;
+        const bool ok = t < t_end && (int32_t)t >= R.lo && pb >= 0 && (uint32_t)pb < a.num_blocks;
         f32x4 kv[JK], vv[JV];
         if (ok) {
             const uint64_t r = (uint64_t)pb * kBS + t % kBS;
@@ -594,7 +664,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
             continue;
         const uint32_t h = kvh * G + g;
         if (nsplit == 1) {
-            const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+            const float inv = norm_factor(mt, lt, a.sinks, h, a.out_scale);
             const uint64_t base = ((uint64_t)s * a.Hq + h) * DV;
 #pragma unroll
             for (int j = 0; j < JV; ++j) {
@@ -621,9 +691,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
 __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, uint32_t Dv)
 {
     const uint32_t s = blockIdx.x, h = blockIdx.y;
-    const int32_t n = a.seq_lens[s];
-    const uint32_t nblk = seq_blocks(n, a.M);
-    const uint32_t nsplit = (nblk + a.chunk_blocks - 1) / a.chunk_blocks;
+    const uint32_t nsplit = seq_range(a, s).nsplit;
     if (nsplit <= 1)
         return;
     const uint64_t prow0 = ((uint64_t)s * a.max_splits) * a.Hq + h;
@@ -640,7 +708,7 @@ __global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, uint32_
                 acc += w * a.part_o[prow * Dv + d];
             }
         }
-        float v = L > 0.f ? acc / L : 0.f;
+        float v = acc * norm_factor(M, L, a.sinks, h, a.out_scale);
         const uint64_t oi = ((uint64_t)s * a.Hq + h) * Dv + d;
         if (a.gate)
             v *= a.gate[oi];
@@ -658,12 +726,19 @@ struct Plan {
 
 // Split plan: enough (sequence, split) work-groups to cover the chip several
 // times over, each split a whole number of blocks, at most 128 blocks (so a
-// split's block-table entries fit two per lane).
+// split's block-table entries fit two per lane).  A window of W tokens
+// touches at most floor((W + 2B - 2) / B) blocks of size B, which bounds the
+// attended blocks of every sequence.
 static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads,
                       uint32_t head_dim_v, uint32_t max_blocks_per_seq, uint32_t block_size,
-                      uint32_t split_tokens)
+                      uint32_t sliding_window, uint32_t split_tokens)
 {
     Plan p{};
+    if (sliding_window > 0) {
+        const uint64_t wb = ((uint64_t)sliding_window + 2ull * block_size - 2) / block_size;
+        if (wb < max_blocks_per_seq)
+            max_blocks_per_seq = (uint32_t)wb;
+    }
     uint32_t cb;
     if (split_tokens) {
         cb = ceil_div(split_tokens, block_size);
@@ -688,24 +763,25 @@ static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_h
 extern "C" size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
                                              uint32_t num_kv_heads, uint32_t head_dim_v,
                                              uint32_t max_blocks_per_seq, uint32_t block_size,
-                                             uint32_t split_tokens)
+                                             uint32_t sliding_window, uint32_t split_tokens)
 {
     if (!num_seqs || !num_q_heads || !num_kv_heads || !head_dim_v || !max_blocks_per_seq ||
         !block_size)
         return 0;
     return pkv::make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim_v, max_blocks_per_seq,
-                          block_size, split_tokens)
+                          block_size, sliding_window, split_tokens)
         .workspace;
 }
 
 extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
                                      const void* k_cache, pkv_dtype k_dtype, float k_scale,
-                                     const void* v_cache, pkv_dtype v_dtype,
+                                     const void* v_cache, pkv_dtype v_dtype, float v_scale,
                                      const int32_t* block_tables, uint32_t max_blocks_per_seq,
                                      const int32_t* seq_lens, uint32_t num_seqs,
                                      uint32_t num_blocks, uint32_t num_q_heads,
                                      uint32_t num_kv_heads, uint32_t head_dim_qk,
                                      uint32_t head_dim_v, uint32_t block_size, float scale,
+                                     uint32_t sliding_window, const float* sinks,
                                      int q_rope, float q_rope_theta, uint32_t q_rope_offset,
                                      uint32_t q_rope_dim, const float* gate, float* out,
                                      uint32_t split_tokens, void* workspace,
@@ -729,16 +805,19 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     if (q_seq_stride < (uint64_t)num_q_heads * head_dim_qk)
         return fail(PKV_ERR_INVALID, "paged_decode_attn: q_seq_stride smaller than a query row");
     const uint32_t G = num_q_heads / num_kv_heads;
-    const bool mfma_path = q_dtype == PKV_BF16 && v_dtype == PKV_BF16 &&
-                           (k_dtype == PKV_BF16 || k_dtype == PKV_FP8_E4M3);
+    const bool mfma_path = q_dtype == PKV_BF16 &&
+                           (k_dtype == PKV_BF16 || k_dtype == PKV_FP8_E4M3) &&
+                           (v_dtype == PKV_BF16 || v_dtype == PKV_FP8_E4M3);
     const bool f32_path = q_dtype == PKV_FP32 && k_dtype == PKV_FP32 && v_dtype == PKV_FP32;
     if (!mfma_path && !f32_path)
-        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: dtypes (q,K,V) must be (BF16,BF16,BF16), (BF16,E4M3,BF16) or (FP32,FP32,FP32)");
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: dtypes (q,K,V) must be (BF16, BF16|E4M3, BF16|E4M3) or (FP32,FP32,FP32)");
     if ((q_seq_stride * dtype_size(q_dtype)) % 16 || !aligned16(q) || !aligned16(k_cache) ||
         !aligned16(v_cache) || !aligned16(out) || (gate && !aligned16(gate)))
         return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: pointers and q stride must be 16-byte aligned");
     if (k_dtype == PKV_FP8_E4M3 && !(k_scale > 0.0f && k_scale < INFINITY))
         return fail(PKV_ERR_INVALID, "paged_decode_attn: k_scale must be finite and > 0");
+    if (v_dtype == PKV_FP8_E4M3 && !(v_scale > 0.0f && v_scale < INFINITY))
+        return fail(PKV_ERR_INVALID, "paged_decode_attn: v_scale must be finite and > 0");
     if (q_rope && q_rope_dim > 0) {
         if (!f32_path)
             return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: query rotation is supported for FP32 q/K/V");
@@ -758,7 +837,7 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
             return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: FP32 path needs a GQA group of 1, 2, 4 or 8");
     }
     const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim_v,
-                                max_blocks_per_seq, block_size, split_tokens);
+                                max_blocks_per_seq, block_size, sliding_window, split_tokens);
     if (plan.workspace > 0 && (workspace_bytes < plan.workspace || !workspace))
         return fail(PKV_ERR_WORKSPACE, "paged_decode_attn: workspace of %zu bytes needed, %zu given",
                     plan.workspace, workspace_bytes);
@@ -772,6 +851,7 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     a.bt = block_tables;
     a.seq_lens = seq_lens;
     a.gate = gate;
+    a.sinks = sinks;
     a.out = out;
     a.part_o = (float*)workspace;
     a.part_ml = plan.workspace
@@ -786,6 +866,8 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     a.chunk_blocks = plan.chunk_blocks;
     a.max_splits = plan.max_splits;
     a.qk_scale = scale * kLog2e * (k_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f);
+    a.out_scale = v_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    a.window = sliding_window;
     a.q_rope = (q_rope && q_rope_dim > 0) ? 1u : 0u;
     a.q_rope_theta = q_rope_theta;
     a.q_rope_offset = q_rope_offset;
@@ -799,17 +881,13 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
         const uint32_t kvg = num_kv_heads / kvpb;
         const dim3 grid(num_seqs * kvg, plan.max_splits);
         const dim3 block(64 * kvpb);
-        if (k_dtype == PKV_BF16) {
-            if (head_dim_qk == 128)
-                hipLaunchKernelGGL((decode_mfma_kernel<0, 128, kPrefetch>), grid, block, 0, st, a, kvg);
-            else
-                hipLaunchKernelGGL((decode_mfma_kernel<0, 64, kPrefetch>), grid, block, 0, st, a, kvg);
-        } else {
-            if (head_dim_qk == 128)
-                hipLaunchKernelGGL((decode_mfma_kernel<1, 128, kPrefetch>), grid, block, 0, st, a, kvg);
-            else
-                hipLaunchKernelGGL((decode_mfma_kernel<1, 64, kPrefetch>), grid, block, 0, st, a, kvg);
-        }
+        const int kt = k_dtype == PKV_FP8_E4M3, vt = v_dtype == PKV_FP8_E4M3;
+#define PKV_MFMA(KT, VT, D)                                                                     \
+    if (kt == KT && vt == VT && head_dim_qk == D)                                              \
+        hipLaunchKernelGGL((decode_mfma_kernel<KT, VT, D, kPrefetch>), grid, block, 0, st, a, kvg);
+        PKV_MFMA(0, 0, 128) PKV_MFMA(0, 0, 64) PKV_MFMA(1, 0, 128) PKV_MFMA(1, 0, 64)
+        PKV_MFMA(0, 1, 128) PKV_MFMA(0, 1, 64) PKV_MFMA(1, 1, 128) PKV_MFMA(1, 1, 64)
+#undef PKV_MFMA
     } else {
         const dim3 grid(num_kv_heads, num_seqs, plan.max_splits);
 #define PKV_F32(DQK, DV, GG)                                                              \

@@ -66,6 +66,28 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return (uint32_t)w;
 }
 
+// Four FP32 -> four saturating E4M3FN codes: magnitudes above 448, infinite
+// ones included, become +-448 (v_med3 clamp, then round to nearest even);
+// NaN becomes the NaN code S.1111.111 with its sign.
+__device__ __forceinline__ uint32_t e4m3_sat_x4(float a, float b, float c, float d)
+{
+    uint32_t w = pack_e4m3x4(__builtin_amdgcn_fmed3f(a, -448.0f, 448.0f),
+                             __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f),
+                             __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f),
+                             __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f));
+    if ((a != a) | (b != b) | (c != c) | (d != d)) {
+        const float y[4] = {a, b, c, d};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (y[i] != y[i]) {
+                const uint32_t code = 0x7Fu | ((__float_as_uint(y[i]) >> 24) & 0x80u);
+                w = (w & ~(0xFFu << (8 * i))) | (code << (8 * i));
+            }
+        }
+    }
+    return w;
+}
+
 // Two E4M3FN bytes (selected by `hi`) -> two FP32, exact.
 __device__ __forceinline__ f32x2 unpack_e4m3x2(uint32_t w, bool hi)
 {

@@ -44,6 +44,16 @@ def test_binding_signatures_cover_the_header(lib):
     assert sorted(_SIGNATURES) == declared_functions()
 
 
+def test_binding_argument_counts_match_the_prototypes():
+    from paged_kv_cache_fill_amd import _SIGNATURES
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name, (args, _) in _SIGNATURES.items():
+        m = re.search(r"\b" + name + r"\s*\(([^)]*)\)", text)
+        params = m.group(1).strip()
+        n = 0 if params in ("", "void") else params.count(",") + 1
+        assert n == len(args), name
+
+
 def test_version(lib):
     assert re.fullmatch(r"\d+\.\d+\.\d+", lib.pkv_version().decode())
 
@@ -54,12 +64,12 @@ def _err(lib):
 
 def test_zero_work_returns_ok_without_pointers(lib):
     assert lib.pkv_fill_slots(None, None, 0, None, None, 0, 0, 16, None) == 0
-    assert lib.pkv_cache_write_v(None, 0, 0, None, 0, 8, 128, 16, 1, None, None) == 0
+    assert lib.pkv_cache_write_v(None, 0, 0, None, 0, 8, 128, 16, 1, None, 0, 1.0, None) == 0
     assert lib.pkv_cache_write_k_fused(None, 0, 0, None, 1e-6, None, None, None, 1e4, 0, 128, 0,
                                        None, 0, 8, 128, 16, 1, None, 0, 1.0, None) == 0
-    assert lib.pkv_paged_decode_attn(None, 0, 0, None, 0, 1.0, None, 0, None, 1, None, 0, 1, 8,
-                                     8, 128, 128, 16, 0.1, 0, 1e4, 0, 0, None, None, 0, None, 0,
-                                     None) == 0
+    assert lib.pkv_paged_decode_attn(None, 0, 0, None, 0, 1.0, None, 0, 1.0, None, 1, None, 0,
+                                     1, 8, 8, 128, 128, 16, 0.1, 0, None, 0, 1e4, 0, 0, None,
+                                     None, 0, None, 0, None) == 0
     assert _err(lib) == ""
 
 
@@ -69,14 +79,20 @@ FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails va
 def test_null_pointers_are_invalid(lib):
     assert lib.pkv_fill_slots(None, FAKE, 4, FAKE, FAKE, 1, 10, 16, None) == -1
     assert "non-NULL" in _err(lib)
-    assert lib.pkv_cache_write_v(FAKE, 0, 1024, None, 10, 8, 128, 16, 4, FAKE, None) == -1
+    assert lib.pkv_cache_write_v(FAKE, 0, 1024, None, 10, 8, 128, 16, 4, FAKE, 0, 1.0,
+                                 None) == -1
 
 
 def test_bad_dtypes_and_shapes(lib):
-    # FP8 V input is not a supported V write dtype
-    assert lib.pkv_cache_write_v(FAKE, 1, 1024, FAKE, 10, 8, 128, 16, 4, FAKE, None) == -2
-    # bad enum
-    assert lib.pkv_cache_write_v(FAKE, 7, 1024, FAKE, 10, 8, 128, 16, 4, FAKE, None) == -1
+    def vw(ind, cd, vs=1.0, stride=1024):
+        return lib.pkv_cache_write_v(FAKE, ind, stride, FAKE, 10, 8, 128, 16, 4, FAKE, cd, vs,
+                                     None)
+    assert vw(1, 1) == -2                         # FP8 V input is not a V write input dtype
+    assert vw(0, 2) == -2                         # BF16 -> FP32 is not a V store
+    assert vw(7, 7) == -1                         # bad enum
+    assert vw(0, 1, 0.0) == -1                    # E4M3 store needs a positive finite v_scale
+    assert vw(2, 1, float("inf")) == -1
+    assert vw(0, 1, 0.5, stride=512) == -1        # token stride smaller than a row
     # head_dim 96 unsupported by the K write
     assert lib.pkv_cache_write_k_fused(FAKE, 0, 768, None, 1e-6, FAKE, None, None, 1e4, 0, 96,
                                        0, FAKE, 10, 8, 96, 16, 4, FAKE, 0, 1.0, None) == -2
@@ -96,15 +112,18 @@ def test_bad_dtypes_and_shapes(lib):
 
 def test_decode_validation(lib):
     def call(**kw):
-        a = dict(q=FAKE, qd=0, qs=32 * 128, k=FAKE, kd=0, ks=1.0, v=FAKE, vd=0, bt=FAKE, M=4,
-                 sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1, qr=0,
-                 qt=1e4, qo=0, qdim=0, gate=None, out=FAKE, split=0, ws=FAKE, wsb=1 << 30)
+        a = dict(q=FAKE, qd=0, qs=32 * 128, k=FAKE, kd=0, ks=1.0, v=FAKE, vd=0, vs=1.0, bt=FAKE,
+                 M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1, win=0,
+                 sinks=None, qr=0, qt=1e4, qo=0, qdim=0, gate=None, out=FAKE, split=0, ws=FAKE,
+                 wsb=1 << 30)
         a.update(kw)
         return lib.pkv_paged_decode_attn(*a.values(), None)
     assert call(Hq=30) == -1                      # Hq % Hkv
     assert call(B=32) == -2                       # block size 16 only
     assert call(kd=2) == -2                       # (BF16, FP32, BF16) not a supported set
     assert call(kd=1, ks=0.0) == -1               # FP8 K needs a scale
+    assert call(vd=1, vs=-1.0) == -1              # FP8 V needs a scale
+    assert call(vd=2) == -2                       # (BF16, BF16, FP32) not a supported set
     assert call(Dqk=192, qs=32 * 192) == -2       # BF16 caches need Dqk == Dv
     assert call(qr=1, qdim=64) == -2              # query rotation: FP32 path only
     assert call(M=512, wsb=16) == -3              # workspace too small
@@ -113,9 +132,15 @@ def test_decode_validation(lib):
 
 
 def test_workspace_query(lib):
-    assert lib.pkv_decode_workspace_bytes(1, 4, 2, 64, 4, 16, 0) == 0        # one split
-    n = lib.pkv_decode_workspace_bytes(256, 32, 8, 128, 512, 16, 0)
+    assert lib.pkv_decode_workspace_bytes(1, 4, 2, 64, 4, 16, 0, 0) == 0     # one split
+    n = lib.pkv_decode_workspace_bytes(256, 32, 8, 128, 512, 16, 0, 0)
     assert n > 0 and n % 16 == 0
     # explicit split size: 1024 tokens = 64 blocks -> 2 splits of a 128-block table
-    assert lib.pkv_decode_workspace_bytes(2, 4, 1, 64, 128, 16, 1024) == 2 * 2 * 4 * 66 * 4
-    assert lib.pkv_decode_workspace_bytes(2, 4, 1, 64, 64, 16, 1024) == 0
+    assert lib.pkv_decode_workspace_bytes(2, 4, 1, 64, 128, 16, 0, 1024) == 2 * 2 * 4 * 66 * 4
+    assert lib.pkv_decode_workspace_bytes(2, 4, 1, 64, 64, 16, 0, 1024) == 0
+    # a window of W tokens touches at most ceil((W - 1) / 16) + 1 blocks of 16:
+    # 64 for W = 1009 (one 64-block split), 65 for W = 1010 (two)
+    assert lib.pkv_decode_workspace_bytes(2, 4, 1, 64, 128, 16, 1009, 1024) == 0
+    assert lib.pkv_decode_workspace_bytes(2, 4, 1, 64, 128, 16, 1010, 1024) == 2 * 2 * 4 * 66 * 4
+    # a window never asks for more than no window
+    assert lib.pkv_decode_workspace_bytes(256, 32, 8, 128, 512, 16, 100000, 0) == n
