@@ -11,7 +11,11 @@ timed on its own and reported as the cache-write throughput.
 Workloads (seeded, synthetic): ``decode_bf16_256seq`` (default; 256 sequences,
 lengths U[512, 8192], Hq 32 / Hkv 8, D 128, BF16 K and V) and
 ``decode_fp8k_64seq_long`` (64 sequences, U[16384, 32768], Hq 64 / Hkv 8,
-FP8 E4M3 K with k_scale = max|stored K| / 448, BF16 V).
+FP8 E4M3 K with k_scale = max|stored K| / 448, BF16 V).  Variants of the
+latter: ``decode_fp8kv_64seq_long`` (E4M3 V too, v_scale = max|V| / 448) and
+``decode_fp8k_64seq_long_window4096_sinks`` (a 4096-token sliding window and
+one sink logit per query head; only the window's tokens are read and
+counted).
 
 Prints one JSON line.  ``value`` is the algorithmic HBM bytes of one step
 divided by the step time (GB/s); the decode attention's KV read is >99.9% of
@@ -34,7 +38,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-WORKLOAD_INDEX = {"decode_bf16_256seq": 2, "decode_fp8k_64seq_long": 3}
+# name -> (workload index, E4M3 V cache, sliding window, sinks)
+WORKLOADS = {
+    "decode_bf16_256seq": (2, False, 0, False),
+    "decode_fp8k_64seq_long": (3, False, 0, False),
+    "decode_fp8kv_64seq_long": (3, True, 0, False),
+    "decode_fp8k_64seq_long_window4096_sinks": (3, False, 4096, True),
+}
 
 
 def parse():
@@ -42,7 +52,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode_bf16_256seq", choices=sorted(WORKLOAD_INDEX))
+    p.add_argument("--workload", default="decode_bf16_256seq", choices=sorted(WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--split-tokens", type=int, default=0)
     p.add_argument("--copy-probe", action="store_true",
@@ -58,13 +68,17 @@ def log(*a):
 # algorithmic bytes (what the method must move)
 # --------------------------------------------------------------------------
 
-def decode_bytes(lens, Hq, Hkv, D, Dv, kb, vb, qb, B=16):
-    """KV rows read + block-table entries + seq_len + q read + FP32 out written."""
+def decode_bytes(lens, Hq, Hkv, D, Dv, kb, vb, qb, B=16, window=0, sinks=False):
+    """KV rows read + block-table entries + seq_len + q read + FP32 out written
+    (+ sink logits); with a window only the attended tokens [n - W, n) and the
+    blocks that hold them count."""
     n = np.asarray(lens, np.int64)
-    kv = int(n.sum()) * Hkv * (D * kb + Dv * vb)
-    bt = int(((n + B - 1) // B).sum()) * 4
+    lo = np.where((window > 0) & (n > window), n - window, 0)
+    kv = int((n - lo).sum()) * Hkv * (D * kb + Dv * vb)
+    bt = int(((n + B - 1) // B - lo // B).sum()) * 4
     S = n.size
-    return kv + bt + 4 * S + S * Hq * D * qb + S * Hq * Dv * 4
+    return (kv + bt + 4 * S + S * Hq * D * qb + S * Hq * Dv * 4
+            + (Hq * 4 if sinks else 0))
 
 
 def kwrite_bytes(T, Hkv, D, in_b, out_b):
@@ -72,8 +86,9 @@ def kwrite_bytes(T, Hkv, D, in_b, out_b):
     return T * (Hkv * D * (in_b + out_b) + 8 + 4)
 
 
-def vwrite_bytes(T, Hkv, Dv, b):
-    return T * (Hkv * Dv * 2 * b + 8)
+def vwrite_bytes(T, Hkv, Dv, in_b, out_b):
+    """V rows read and written, slot (8 B) per token."""
+    return T * (Hkv * Dv * (in_b + out_b) + 8)
 
 
 def slots_bytes(T, S, B=16):
@@ -131,7 +146,7 @@ def main():
     import pkv_workloads as W
 
     pkv.load()
-    idx = WORKLOAD_INDEX[args.workload]
+    idx, v_fp8, window, use_sinks = WORKLOADS[args.workload]
     lay = W.layout(idx)
     cfg = lay.cfg
     S, Hq, Hkv, D, B = lay.num_seqs, cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], 16
@@ -147,7 +162,8 @@ def main():
     Th = int(hist_lens.sum())
     kdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
     k_pool = torch.empty((lay.num_blocks, B, Hkv, D), dtype=kdt, device=dev)
-    v_pool = torch.empty((lay.num_blocks, B, Hkv, Dv), dtype=torch.bfloat16, device=dev)
+    vdt = torch.float8_e4m3fn if v_fp8 else torch.bfloat16
+    v_pool = torch.empty((lay.num_blocks, B, Hkv, Dv), dtype=vdt, device=dev)
     bt = torch.from_numpy(lay.block_tables).to(dev)
     seq_lens = torch.from_numpy(lay.seq_lens).to(dev)
     w = torch.from_numpy(W.norm_weight(idx).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -176,13 +192,18 @@ def main():
         k_scale = float(amax.item()) / 448.0
         del tmp
         log(f"k_scale = {k_scale:.6g}")
+    v_scale = 1.0
+    if v_fp8:
+        v_scale = float(v_hist.abs().max().float().item()) / 448.0
+        log(f"v_scale = {v_scale:.6g}")
+    sinks = (torch.from_numpy(W.normal(idx, W.S_SINKS, (Hq,))).to(dev) if use_sinks else None)
 
     def populate():
         pkv.cache_write_k_fused(k_hist, slots_h, k_pool, norm_weight=w, eps=cfg["eps"],
                                 pos_t=pos_h_t, theta=cfg["theta"], k_scale=k_scale)
 
     def populate_v():
-        pkv.cache_write_v(v_hist, slots_h, v_pool)
+        pkv.cache_write_v(v_hist, slots_h, v_pool, v_scale=v_scale)
 
     def time_call(fn, reps):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -202,7 +223,7 @@ def main():
     del k_hist, v_hist
     torch.cuda.empty_cache()
     kw_bytes = kwrite_bytes(Th, Hkv, D, 2, 1 if fp8 else 2)
-    vw_bytes = vwrite_bytes(Th, Hkv, Dv, 2)
+    vw_bytes = vwrite_bytes(Th, Hkv, Dv, 2, 1 if v_fp8 else 2)
     log(f"population write: K {kw_ms:.3f} ms ({kw_bytes / kw_ms / 1e6:.0f} GB/s), "
         f"V {vw_ms:.3f} ms ({vw_bytes / vw_ms / 1e6:.0f} GB/s)")
 
@@ -216,7 +237,8 @@ def main():
     pos_d_t = torch.from_numpy(pos_d).to(dev)
     slots_d = torch.empty(S, dtype=torch.int64, device=dev)
     out = torch.empty((S, Hq, Dv), dtype=torch.float32, device=dev)
-    ws_n = pkv.decode_workspace_bytes(S, Hq, Hkv, Dv, lay.max_blocks_per_seq, B, args.split_tokens)
+    ws_n = pkv.decode_workspace_bytes(S, Hq, Hkv, Dv, lay.max_blocks_per_seq, B, args.split_tokens,
+                                      window)
     ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
     scale = D ** -0.5
 
@@ -224,11 +246,12 @@ def main():
         pkv.fill_slots(slots_d, bt, start_d_t, cu_d_t, B)
         pkv.cache_write_k_fused(k_new, slots_d, k_pool, norm_weight=w, eps=cfg["eps"],
                                 pos_t=pos_d_t, theta=cfg["theta"], k_scale=k_scale)
-        pkv.cache_write_v(v_new, slots_d, v_pool)
+        pkv.cache_write_v(v_new, slots_d, v_pool, v_scale=v_scale)
 
     def step_attn():
         pkv.paged_decode_attn(q, k_pool, v_pool, bt, seq_lens, scale=scale, k_scale=k_scale,
-                              out=out, split_tokens=args.split_tokens, workspace=ws)
+                              v_scale=v_scale, sliding_window=window, sinks=sinks, out=out,
+                              split_tokens=args.split_tokens, workspace=ws)
 
     def step():
         step_writes()
@@ -249,9 +272,10 @@ def main():
     write_ms = float(np.mean(time_call(step_writes, args.steps)))
     log(f"step {ms_per_step:.3f} ms (decode call {attn_ms:.3f} ms, step writes {write_ms * 1e3:.1f} us)")
 
-    dec_b = decode_bytes(lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 2, 2)
-    step_b = (dec_b + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2) + vwrite_bytes(S, Hkv, Dv, 2)
-              + slots_bytes(S, S))
+    dec_b = decode_bytes(lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 1 if v_fp8 else 2, 2,
+                         window=window, sinks=use_sinks)
+    step_b = (dec_b + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2)
+              + vwrite_bytes(S, Hkv, Dv, 2, 1 if v_fp8 else 2) + slots_bytes(S, S))
     value = step_b / (ms_per_step * 1e-3) / 1e9
     achieved = dec_b / (attn_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(kernel_source_hash(), args.workload)
@@ -267,11 +291,13 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 K / bf16 V, f32 accumulate" if fp8 else "bf16 K/V, f32 accumulate",
+        "dtype": (("fp8_e4m3 K" if fp8 else "bf16 K") + (" / fp8_e4m3 V" if v_fp8 else " / bf16 V")
+                  + ", f32 accumulate"),
         "data": "synthetic (seeded)",
         "config": {"workload": args.workload, "num_seqs": S, "seq_len_range": [cfg["len_lo"], cfg["len_hi"]],
                    "total_tokens": int(lens.sum()), "num_q_heads": Hq, "num_kv_heads": Hkv,
-                   "head_dim": D, "block_size": B, "parallelism": "single GPU"},
+                   "head_dim": D, "block_size": B, "sliding_window": window,
+                   "sinks": use_sinks, "parallelism": "single GPU"},
         "decode_attn": {"ms": round(attn_ms, 4), "algorithmic_bytes": dec_b,
                         "GB_per_s": round(achieved, 1), "frac_of_hbm_peak": round(achieved / HBM_PEAK_GBS, 4)},
         "cache_write": {
@@ -290,11 +316,12 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(idx, lay, k_scale)
+        result["cpu_baseline"] = cpu_baseline(idx, lay, k_scale, v_fp8, v_scale, window,
+                                              None if sinks is None else sinks.cpu().numpy())
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(idx, lay, k_scale):
+def cpu_baseline(idx, lay, k_scale, v_fp8=False, v_scale=1.0, window=0, sinks=None):
     """The oracle, as it stands, timed on this host on the decode step of the
     whole workload (slots, K write, V write, attention over every sequence).
     Pools are drawn on the device by the seeded generator and copied to the
@@ -318,8 +345,18 @@ def cpu_baseline(idx, lay, k_scale):
     else:
         kp = W.device_normal(idx, W.S_POOLK, shape, torch.bfloat16, "cuda").view(torch.int16) \
             .cpu().numpy().view(np.uint16)
-    vp = W.device_normal(idx, W.S_POOLV, (lay.num_blocks, 16, Hkv, Dv), torch.bfloat16, "cuda") \
-        .view(torch.int16).cpu().numpy().view(np.uint16)
+    vshape = (lay.num_blocks, 16, Hkv, Dv)
+    if v_fp8:
+        g = torch.Generator(device="cuda")
+        g.manual_seed(W.seed_of(idx) * 1000 + W.S_POOLV)
+        mag = torch.randint(0, 0x50, vshape, dtype=torch.uint8, device="cuda", generator=g)
+        sign = torch.randint(0, 2, vshape, dtype=torch.uint8, device="cuda", generator=g) << 7
+        vp = (mag | sign).cpu().numpy()
+        del mag, sign
+    else:
+        vp = W.device_normal(idx, W.S_POOLV, vshape, torch.bfloat16, "cuda") \
+            .view(torch.int16).cpu().numpy().view(np.uint16)
+    vdt = "fp8" if v_fp8 else "bf16"
     torch.cuda.empty_cache()
     S = lay.num_seqs
     q = W.queries(idx, S)
@@ -332,15 +369,17 @@ def cpu_baseline(idx, lay, k_scale):
     oracle.cache_write_k(k_new, "bf16", slots, kp, cfg["k_cache_dtype"], num_kv_heads=Hkv,
                          head_dim=D, block_size=16, norm_weight=w, eps=cfg["eps"], pos_t=pos,
                          theta=cfg["theta"], k_scale=k_scale, nthreads=cores)
-    oracle.cache_write_v(v_new, "bf16", slots, vp, num_kv_heads=Hkv, head_dim_v=Dv, block_size=16)
-    oracle.paged_decode(q, "bf16", kp, cfg["k_cache_dtype"], vp, "bf16", lay.block_tables,
+    oracle.cache_write_v(v_new, "bf16", slots, vp, num_kv_heads=Hkv, head_dim_v=Dv, block_size=16,
+                         cache_dtype=vdt, v_scale=v_scale)
+    oracle.paged_decode(q, "bf16", kp, cfg["k_cache_dtype"], vp, vdt, lay.block_tables,
                         lay.seq_lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D,
                         head_dim_v=Dv, block_size=16, scale=D ** -0.5, k_scale=k_scale,
-                        nthreads=cores)
+                        v_scale=v_scale, sliding_window=window, sinks=sinks, nthreads=cores)
     dt = time.perf_counter() - t0
-    b = (decode_bytes(lay.seq_lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 2, 2)
-         + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2) + vwrite_bytes(S, Hkv, Dv, 2)
-         + slots_bytes(S, S))
+    b = (decode_bytes(lay.seq_lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 1 if v_fp8 else 2, 2,
+                      window=window, sinks=sinks is not None)
+         + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2)
+         + vwrite_bytes(S, Hkv, Dv, 2, 1 if v_fp8 else 2) + slots_bytes(S, S))
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole decode step of all {S} sequences "
                       f"({int(lay.seq_lens.astype(np.int64).sum())} tokens), {dt:.2f} s"}

@@ -63,7 +63,8 @@ def rng(index: int, stream: int) -> np.random.Generator:
 
 
 # streams (fixed numbers so that each array is independent of draw order)
-S_LENS, S_BLOCKS, S_K, S_V, S_Q, S_W, S_GATE, S_KNEW, S_VNEW, S_POOLK, S_POOLV, S_OUTL = range(12)
+S_LENS, S_BLOCKS, S_K, S_V, S_Q, S_W, S_GATE, S_KNEW, S_VNEW, S_POOLK, S_POOLV, S_OUTL, S_SINKS = \
+    range(13)
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
