@@ -73,6 +73,12 @@ def lib():
                                         U32, U32, U32, U32, U32, U32, F32, U32, P, I32, F32,
                                         U32, U32, P, P, I32]
         L.pkvo_paged_decode.restype = None
+        L.pkvo_paged_prefill.argtypes = [P, I32, U64, P, P, I32, F32, P, I32, F32, P, U32, P, U32,
+                                         U32, U32, U32, U32, U32, U32, F32, U32, P, P, I32]
+        L.pkvo_paged_prefill.restype = None
+        L.pkvo_mla_cache_assemble.argtypes = [P, P, I32, U64, U64, P, U32, U32, U32, U32, U32,
+                                              U32, P, P]
+        L.pkvo_mla_cache_assemble.restype = None
         _lib = L
     return _lib
 
@@ -224,3 +230,53 @@ def paged_decode(q, q_dtype, k_cache, k_dtype, v_cache, v_dtype, block_tables, s
                             q_rope_theta, q_rope_offset,
                             q_rope_dim, _ptr(g), _ptr(out), nthreads)
     return out
+
+
+def paged_prefill(q, q_dtype, cu_q, k_cache, k_dtype, v_cache, v_dtype, block_tables, seq_lens, *,
+                  num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, block_size, scale,
+                  k_scale=1.0, v_scale=1.0, sliding_window=0, sinks=None, q_token_stride=None,
+                  nthreads=1):
+    """Causal attention of the last q_len tokens of every sequence over the
+    paged cache.  q [total_q, Hq, Dqk]; cu_q int32 [S+1].  Returns FP32
+    [total_q, num_q_heads, head_dim_v]."""
+    q = _c(q, NP_TYPES[q_dtype])
+    cq = _c(cu_q, np.int32)
+    bt = _c(block_tables, np.int32)
+    if bt.ndim == 1:
+        bt = bt.reshape(1, -1)
+    sl = _c(seq_lens, np.int32)
+    S = sl.size
+    kc = _c(k_cache, NP_TYPES[k_dtype])
+    vc = _c(v_cache, NP_TYPES[v_dtype])
+    num_blocks = kc.size // (block_size * num_kv_heads * head_dim_qk)
+    qs = q_token_stride if q_token_stride is not None else num_q_heads * head_dim_qk
+    total = int(cq[S]) if S else 0
+    sk = _c(sinks, np.float32)
+    out = np.empty((total, num_q_heads, head_dim_v), np.float32)
+    lib().pkvo_paged_prefill(_ptr(q), DTYPES[q_dtype], qs, _ptr(cq), _ptr(kc), DTYPES[k_dtype],
+                             k_scale, _ptr(vc), DTYPES[v_dtype], v_scale, _ptr(bt), bt.shape[1],
+                             _ptr(sl), S, num_blocks, num_q_heads, num_kv_heads, head_dim_qk,
+                             head_dim_v, block_size, scale, sliding_window, _ptr(sk), _ptr(out),
+                             nthreads)
+    return out
+
+
+def mla_cache_assemble(kv_latent, k_rope, dtype, slots, k_cache, v_cache, *, kv_lora, rope,
+                            block_size, latent_stride=None, rope_stride=None):
+    """K row [latent | k_rope | 0], V row [latent | 0] at every slot (caches
+    [num_blocks, block_size, 1, cache_dim], modified in place).  kv_latent
+    [T, >= kv_lora] and k_rope [T, >= rope] with token strides."""
+    lat = _c(kv_latent, NP_TYPES[dtype])
+    rp = _c(k_rope, NP_TYPES[dtype])
+    T = int(slots.size)
+    ls = latent_stride if latent_stride is not None else lat.shape[-1]
+    rs = rope_stride if rope_stride is not None else rp.shape[-1]
+    assert k_cache.flags.c_contiguous and v_cache.flags.c_contiguous
+    assert k_cache.dtype == NP_TYPES[dtype] and v_cache.dtype == NP_TYPES[dtype]
+    cache_dim = k_cache.shape[-1]
+    num_blocks = k_cache.size // (block_size * cache_dim)
+    sl = _c(slots, np.int64)
+    lib().pkvo_mla_cache_assemble(_ptr(lat), _ptr(rp), DTYPES[dtype], ls, rs, _ptr(sl), T,
+                                  kv_lora, rope, cache_dim, block_size, num_blocks,
+                                  _ptr(k_cache), _ptr(v_cache))
+    return k_cache, v_cache

@@ -401,6 +401,89 @@ static double cache_elem(const void* base, int dtype, float scl, uint64_t idx)
     return dtype == O_E4M3 ? x * (double)scl : x;
 }
 
+/* Attention of one query vector q (kv head g, query head h) of sequence s
+ * over the positions [lo, end) of its cache, written to dst[Dv]:
+ *   softmax over s_t = scale * <q, k_t> (t attended), times v_t, summed.
+ * Tokens of an unmapped block or past the table are excluded; with no
+ * attended token the row is zero. */
+static void attend(const decode_ctx* c, uint32_t s, uint32_t g, uint32_t h, int32_t end,
+                   int32_t lo, const double* q, double* o, const float* gate_row, float* dst)
+{
+    for (uint32_t d = 0; d < c->Dv; ++d)
+        o[d] = 0.0;
+    if (end <= 0) {
+        for (uint32_t d = 0; d < c->Dv; ++d)
+            dst[d] = 0.0f;
+        return;
+    }
+    /* pass 1: scores and their maximum */
+    double* sc = (double*)malloc(sizeof(double) * (size_t)end);
+    unsigned char* ok = (unsigned char*)malloc((size_t)end);
+    double m = -INFINITY;
+    for (int32_t t = 0; t < end; ++t) {
+        uint32_t b = (uint32_t)t / c->B;
+        ok[t] = 0;
+        if (t < lo)
+            continue;                        /* outside the window */
+        if (b >= c->max_blocks_per_seq)
+            continue;
+        int32_t blk = c->block_tables[(uint64_t)s * c->max_blocks_per_seq + b];
+        if (blk < 0 || (uint32_t)blk >= c->num_blocks)
+            continue;                        /* unmapped block: token excluded */
+        uint64_t row = (uint64_t)blk * c->B + (uint32_t)t % c->B;
+        uint64_t koff = (row * c->Hkv + g) * c->Dqk;
+        double dot = 0.0;
+        for (uint32_t j = 0; j < c->Dqk; ++j)
+            dot += q[j] * cache_elem(c->k_cache, c->k_dtype, c->k_scale, koff + j);
+        sc[t] = (double)c->scale * dot;
+        ok[t] = 1;
+        if (sc[t] > m) m = sc[t];
+    }
+    /* pass 2: softmax weights and the weighted sum of V rows */
+    double l = 0.0;
+    for (int32_t t = 0; t < end; ++t) {
+        if (!ok[t]) continue;
+        uint32_t b = (uint32_t)t / c->B;
+        int32_t blk = c->block_tables[(uint64_t)s * c->max_blocks_per_seq + b];
+        uint64_t row = (uint64_t)blk * c->B + (uint32_t)t % c->B;
+        uint64_t voff = (row * c->Hkv + g) * c->Dv;
+        double pt = exp(sc[t] - m);
+        l += pt;
+        for (uint32_t d = 0; d < c->Dv; ++d)
+            o[d] += pt * cache_elem(c->v_cache, c->v_dtype, c->v_scale, voff + d);
+    }
+    /* Attention sink (p1 mla_paged_decode_fp8 takes a `sinks` pointer,
+     * semantics unstated; our reading): one logit per query head, in the
+     * units of the scaled scores, that joins the softmax normalisation
+     * and carries no value, i.e. the denominator gains exp(sink - m).
+     * With no attended token the output stays zero. */
+    if (c->sinks && l > 0.0) {
+        double sk = (double)c->sinks[h];
+        double mm = sk > m ? sk : m;
+        double f = exp(m - mm);
+        l = l * f + exp(sk - mm);
+        for (uint32_t d = 0; d < c->Dv; ++d)
+            o[d] *= f;
+    }
+    for (uint32_t d = 0; d < c->Dv; ++d) {
+        double val = l > 0.0 ? o[d] / l : 0.0;
+        /* optional elementwise output gate (p3 module doc: SDPA + gate) */
+        if (gate_row)
+            val *= (double)gate_row[d];
+        dst[d] = (float)val;
+    }
+    free(sc);
+    free(ok);
+}
+
+/* Sliding window of W tokens (p1/p3 decode launchers take a sliding_window
+ * argument, semantics unstated; our reading): a query at position p sees the
+ * W most recent positions, [p + 1 - W, p + 1); W = 0 means no window. */
+static int32_t window_start(uint32_t window, int32_t end)
+{
+    return (window > 0 && (int64_t)end > (int64_t)window) ? end - (int32_t)window : 0;
+}
+
 static void decode_range(void* p, uint64_t u0, uint64_t u1)
 {
     const decode_ctx* c = (const decode_ctx*)p;
@@ -410,85 +493,17 @@ static void decode_range(void* p, uint64_t u0, uint64_t u1)
     for (uint64_t u = u0; u < u1; ++u) {
         uint32_t s = (uint32_t)(u / c->Hq), h = (uint32_t)(u % c->Hq);
         uint32_t g = h / G;                      /* GQA: contiguous groups */
-        float* dst = c->out + ((uint64_t)s * c->Hq + h) * c->Dv;
-        int32_t n = c->seq_lens[s];
-        for (uint32_t d = 0; d < c->Dv; ++d)
-            o[d] = 0.0;
-        if (n <= 0) {
-            for (uint32_t d = 0; d < c->Dv; ++d)
-                dst[d] = 0.0f;
-            continue;
-        }
+        uint64_t orow = ((uint64_t)s * c->Hq + h) * c->Dv;
+        int32_t n = c->seq_lens[s];              /* the query is the token at n - 1 */
         uint64_t qoff = (uint64_t)s * c->q_seq_stride + (uint64_t)h * c->Dqk;
         for (uint32_t j = 0; j < c->Dqk; ++j)
-            q[j] = load_elem(c->q, c->q_dtype, qoff + j);
-        if (c->q_rope && c->q_rope_dim > 0) {
-            int32_t pos3[3] = {n - 1, n - 1, n - 1};   /* the query is the last token */
+            q[j] = n > 0 ? load_elem(c->q, c->q_dtype, qoff + j) : 0.0;
+        if (n > 0 && c->q_rope && c->q_rope_dim > 0) {
+            int32_t pos3[3] = {n - 1, n - 1, n - 1};
             rope_rotate(q, c->q_rope_offset, c->q_rope_dim, c->q_rope_theta, pos3);
         }
-        /* pass 1: scores and their maximum */
-        double* sc = (double*)malloc(sizeof(double) * (size_t)n);
-        unsigned char* ok = (unsigned char*)malloc((size_t)n);
-        double m = -INFINITY;
-        /* Sliding window of W tokens (p1/p3 decode launchers take a
-         * sliding_window argument, semantics unstated; our reading): the query
-         * at position n-1 sees the W most recent tokens, positions
-         * [n - W, n); W = 0 means no window. */
-        int32_t lo = (c->window > 0 && (int64_t)n > (int64_t)c->window) ? n - (int32_t)c->window : 0;
-        for (int32_t t = 0; t < n; ++t) {
-            uint32_t b = (uint32_t)t / c->B;
-            ok[t] = 0;
-            if (t < lo)
-                continue;                        /* outside the window */
-            if (b >= c->max_blocks_per_seq)
-                continue;
-            int32_t blk = c->block_tables[(uint64_t)s * c->max_blocks_per_seq + b];
-            if (blk < 0 || (uint32_t)blk >= c->num_blocks)
-                continue;                        /* unmapped block: token excluded */
-            uint64_t row = (uint64_t)blk * c->B + (uint32_t)t % c->B;
-            uint64_t koff = (row * c->Hkv + g) * c->Dqk;
-            double dot = 0.0;
-            for (uint32_t j = 0; j < c->Dqk; ++j)
-                dot += q[j] * cache_elem(c->k_cache, c->k_dtype, c->k_scale, koff + j);
-            sc[t] = (double)c->scale * dot;
-            ok[t] = 1;
-            if (sc[t] > m) m = sc[t];
-        }
-        /* pass 2: softmax weights and the weighted sum of V rows */
-        double l = 0.0;
-        for (int32_t t = 0; t < n; ++t) {
-            if (!ok[t]) continue;
-            uint32_t b = (uint32_t)t / c->B;
-            int32_t blk = c->block_tables[(uint64_t)s * c->max_blocks_per_seq + b];
-            uint64_t row = (uint64_t)blk * c->B + (uint32_t)t % c->B;
-            uint64_t voff = (row * c->Hkv + g) * c->Dv;
-            double pt = exp(sc[t] - m);
-            l += pt;
-            for (uint32_t d = 0; d < c->Dv; ++d)
-                o[d] += pt * cache_elem(c->v_cache, c->v_dtype, c->v_scale, voff + d);
-        }
-        /* Attention sink (p1 mla_paged_decode_fp8 takes a `sinks` pointer,
-         * semantics unstated; our reading): one logit per query head, in the
-         * units of the scaled scores, that joins the softmax normalisation
-         * and carries no value, i.e. the denominator gains exp(sink - m).
-         * With no attended token the output stays zero. */
-        if (c->sinks && l > 0.0) {
-            double sk = (double)c->sinks[h];
-            double mm = sk > m ? sk : m;
-            double f = exp(m - mm);
-            l = l * f + exp(sk - mm);
-            for (uint32_t d = 0; d < c->Dv; ++d)
-                o[d] *= f;
-        }
-        for (uint32_t d = 0; d < c->Dv; ++d) {
-            double val = l > 0.0 ? o[d] / l : 0.0;
-            /* optional elementwise output gate (p3 module doc: SDPA + gate) */
-            if (c->gate)
-                val *= (double)c->gate[((uint64_t)s * c->Hq + h) * c->Dv + d];
-            dst[d] = (float)val;
-        }
-        free(sc);
-        free(ok);
+        attend(c, s, g, h, n, window_start(c->window, n), q, o, c->gate ? c->gate + orow : NULL,
+               c->out + orow);
     }
     free(q);
     free(o);
@@ -510,6 +525,104 @@ void pkvo_paged_decode(const void* q, int q_dtype, uint64_t q_seq_stride,
                     num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, block_size, scale,
                     sliding_window, sinks, q_rope, q_rope_theta, q_rope_offset, q_rope_dim, gate, out};
     parallel_for((uint64_t)num_seqs * num_q_heads, nthreads, decode_range, &c);
+}
+
+/* ------------------------------------------------------------------ */
+/* (6) Paged prefill attention (N new tokens per sequence)             */
+/* ------------------------------------------------------------------ */
+
+typedef struct {
+    decode_ctx d;                 /* cache, tables, heads, scale, window, sinks */
+    uint64_t q_token_stride;
+    const int32_t* cu_q;          /* [S + 1] */
+    uint32_t num_seqs;
+} prefill_ctx;
+
+/* Page 1 names batched prefill variants (N tokens) of the paged kernels and
+ * gives no more; the reading taken is causal attention over the same cache:
+ * the q_len = cu_q[s+1] - cu_q[s] queries of sequence s are its last q_len
+ * tokens (their K/V rows already written), query i at position
+ * p = seq_len - q_len + i, and it attends to positions [lo, p] (lo from the
+ * sliding window, as for decode).  A query with p < 0 gives a zero row. */
+static void prefill_range(void* pp, uint64_t u0, uint64_t u1)
+{
+    const prefill_ctx* c = (const prefill_ctx*)pp;
+    const decode_ctx* d = &c->d;
+    const uint32_t G = d->Hq / d->Hkv;
+    double* q = (double*)malloc(sizeof(double) * d->Dqk);
+    double* o = (double*)malloc(sizeof(double) * d->Dv);
+    for (uint64_t u = u0; u < u1; ++u) {
+        uint64_t t = u / d->Hq;
+        uint32_t h = (uint32_t)(u % d->Hq);
+        uint32_t s = 0;                          /* sequence holding query token t */
+        while (s + 1 < c->num_seqs && (uint64_t)c->cu_q[s + 1] <= t)
+            ++s;
+        int32_t qlen = c->cu_q[s + 1] - c->cu_q[s];
+        int32_t i = (int32_t)(t - (uint64_t)c->cu_q[s]);
+        int32_t end = d->seq_lens[s] - qlen + i + 1;   /* attends to [lo, end) */
+        uint64_t qoff = t * c->q_token_stride + (uint64_t)h * d->Dqk;
+        for (uint32_t j = 0; j < d->Dqk; ++j)
+            q[j] = load_elem(d->q, d->q_dtype, qoff + j);
+        attend(d, s, h / G, h, end, window_start(d->window, end), q, o, NULL,
+               d->out + (t * d->Hq + h) * d->Dv);
+    }
+    free(q);
+    free(o);
+}
+
+void pkvo_paged_prefill(const void* q, int q_dtype, uint64_t q_token_stride, const int32_t* cu_q,
+                        const void* k_cache, int k_dtype, float k_scale,
+                        const void* v_cache, int v_dtype, float v_scale,
+                        const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
+                        uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
+                        uint32_t head_dim_v, uint32_t block_size, float scale,
+                        uint32_t sliding_window, const float* sinks, float* out, int nthreads)
+{
+    prefill_ctx c;
+    memset(&c, 0, sizeof c);
+    decode_ctx d = {q, q_dtype, 0, k_cache, k_dtype, k_scale, v_cache, v_dtype, v_scale,
+                    block_tables, max_blocks_per_seq, seq_lens, num_blocks, num_q_heads,
+                    num_kv_heads, head_dim_qk, head_dim_v, block_size, scale, sliding_window,
+                    sinks, 0, 0.0f, 0, 0, NULL, out};
+    c.d = d;
+    c.q_token_stride = q_token_stride;
+    c.cu_q = cu_q;
+    c.num_seqs = num_seqs;
+    uint64_t total = num_seqs ? (uint64_t)cu_q[num_seqs] : 0;
+    parallel_for(total * num_q_heads, nthreads, prefill_range, &c);
+}
+
+/* ------------------------------------------------------------------ */
+/* (7) MLA cache assembly                                              */
+/* ------------------------------------------------------------------ */
+
+/* Page 1, mla_cache_assemble: [kv_latent | k_rope] becomes the K row and
+ * [kv_latent | zeros] the V row of the single-head MLA cache.  Batched here
+ * over tokens through a slot mapping (padding slots skipped); a cache row
+ * longer than kv_lora + rope is zero past the copied parts.  Byte copies in
+ * the input dtype. */
+void pkvo_mla_cache_assemble(const void* kv_latent, const void* k_rope, int dtype,
+                             uint64_t latent_stride, uint64_t rope_stride,
+                             const int64_t* slots, uint32_t num_tokens, uint32_t kv_lora,
+                             uint32_t rope, uint32_t cache_dim, uint32_t block_size,
+                             uint32_t num_blocks, void* k_cache, void* v_cache)
+{
+    size_t es = elem_size(dtype);
+    uint64_t num_slots = (uint64_t)num_blocks * block_size;
+    for (uint64_t t = 0; t < num_tokens; ++t) {
+        int64_t slot = slots[t];
+        if (slot < 0 || (uint64_t)slot >= num_slots)
+            continue;
+        char* krow = (char*)k_cache + (uint64_t)slot * cache_dim * es;
+        char* vrow = (char*)v_cache + (uint64_t)slot * cache_dim * es;
+        memset(krow, 0, cache_dim * es);
+        memset(vrow, 0, cache_dim * es);
+        memcpy(krow, (const char*)kv_latent + t * latent_stride * es, (size_t)kv_lora * es);
+        memcpy(krow + (size_t)kv_lora * es, (const char*)k_rope + t * rope_stride * es,
+               (size_t)rope * es);
+        memcpy(vrow, (const char*)kv_latent + t * latent_stride * es, (size_t)kv_lora * es);
+    }
 }
 
 /* ------------------------------------------------------------------ */
