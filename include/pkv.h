@@ -8,6 +8,8 @@
  *   pkv_cache_write_k_fused RMSNorm -> RoPE -> one rounding, into the K pool
  *   pkv_cache_write_v       V reshape-and-cache copy (or E4M3 store) into the V pool
  *   pkv_paged_decode_attn   one-query-token GQA attention through the tables
+ *   pkv_paged_prefill_attn  causal attention of N new tokens per sequence
+ *   pkv_mla_cache_assemble  MLA cache rows [latent | k_rope] -> K, [latent | 0] -> V
  *
  * Sources (the pages this library implements):
  *   [p1] docs.atlasinference.io, spark_model/layers/ops/kv_cache.rs
@@ -254,6 +256,68 @@ int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_strid
                           uint32_t q_rope_dim, const float* gate, float* out,
                           uint32_t split_tokens, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * pkv_paged_prefill_attn -- [p1] "batched prefill variants (N tokens)" of
+ * the paged kernels (the page names them and gives no more): causal
+ * attention of the new tokens of every sequence over the same paged cache,
+ * after their K/V rows have been written (pkv_cache_write_k_fused /
+ * pkv_cache_write_v).  Reading taken: the q_len = cu_q[s+1] - cu_q[s]
+ * queries of sequence s are its last q_len tokens; query i sits at position
+ * p = seq_lens[s] - q_len + i and attends to positions [lo, p], lo = p + 1 -
+ * sliding_window when 0 < sliding_window < p + 1, else 0; scores, E4M3
+ * scales, the sink rule and the exclusion of unmapped blocks are those of
+ * pkv_paged_decode_attn.  q_len = 1 is the decode call.
+ *
+ *   q             in  [total_q, num_q_heads, head_dim_qk] BF16, token t at
+ *                     element t * q_token_stride (heads packed)
+ *   cu_q          in  int32 [num_seqs + 1], non-decreasing, cu_q[0] = 0,
+ *                     cu_q[num_seqs] <= total_q
+ *   max_q_len         an upper bound of every q_len (host value: sizes the
+ *                     grid); rows of a sequence past max_q_len are undefined
+ *   total_q           rows of q and out; rows >= total_q are never touched
+ *   seq_lens      in  int32 [num_seqs], including the new tokens; a query
+ *                     with p < 0 gets an all-zero row
+ *   sinks         in  FP32 [num_q_heads] or NULL
+ *   out           out FP32 [total_q, num_q_heads, head_dim_v]; rows of the
+ *                     queries only
+ *   (other arguments as for pkv_paged_decode_attn)
+ * Supported: q BF16; K and V BF16 or FP8_E4M3; head_dim_qk == head_dim_v in
+ *   {64, 128}; GQA group 1, 2, 4, 8 or 16; block_size 16.  No workspace.
+ */
+int pkv_paged_prefill_attn(const void* q, pkv_dtype q_dtype, uint64_t q_token_stride,
+                           const int32_t* cu_q, uint32_t max_q_len, uint32_t total_q,
+                           const void* k_cache, pkv_dtype k_dtype, float k_scale,
+                           const void* v_cache, pkv_dtype v_dtype, float v_scale,
+                           const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                           const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
+                           uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
+                           uint32_t head_dim_v, uint32_t block_size, float scale,
+                           uint32_t sliding_window, const float* sinks, float* out,
+                           void* stream);
+
+/*
+ * pkv_mla_cache_assemble -- [p1] mla_cache_assemble: the single-head MLA
+ * cache rows of a token, K = [kv_latent | k_rope] and V = [kv_latent |
+ * zeros], in one kernel.  Batched here over tokens through a slot mapping:
+ * for each token t with 0 <= slot_mapping[t] < num_blocks * block_size,
+ *   k_cache[slot, 0, :] = [kv_latent[t, :kv_lora], k_rope[t, :rope], 0 ...]
+ *   v_cache[slot, 0, :] = [kv_latent[t, :kv_lora], 0 ...]
+ * byte for byte in dtype; cache_dim >= kv_lora + rope (the rest is zero).
+ *
+ *   kv_latent     in  [num_tokens, >= kv_lora] of dtype, token stride latent_stride
+ *   k_rope        in  [num_tokens, >= rope] of dtype, token stride rope_stride
+ *                     (may be NULL when rope == 0)
+ *   slot_mapping  in  int64 [num_tokens]
+ *   k_cache, v_cache  out [num_blocks, block_size, 1, cache_dim] of dtype
+ * Supported: dtype BF16 or FP32; kv_lora, rope, cache_dim and both strides
+ *   multiples of 16 bytes.
+ */
+int pkv_mla_cache_assemble(const void* kv_latent, const void* k_rope, pkv_dtype dtype,
+                           uint64_t latent_stride, uint64_t rope_stride,
+                           const int64_t* slot_mapping, uint32_t num_tokens, uint32_t kv_lora,
+                           uint32_t rope, uint32_t cache_dim, uint32_t block_size,
+                           uint32_t num_blocks, void* k_cache, void* v_cache, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,7 +9,7 @@ every call raises ``RuntimeError``.
 
 Functions (same names as the C calls without the ``pkv_`` prefix):
   fill_slots, cache_write_k_fused, cache_write_v, decode_workspace_bytes,
-  paged_decode_attn
+  paged_decode_attn, paged_prefill_attn, mla_cache_assemble
 """
 from __future__ import annotations
 
@@ -19,7 +19,8 @@ import os
 import torch
 
 __all__ = ["fill_slots", "cache_write_k_fused", "cache_write_v", "decode_workspace_bytes",
-           "paged_decode_attn", "library_path", "load", "PkvError"]
+           "paged_decode_attn", "paged_prefill_attn", "mla_cache_assemble", "library_path", "load",
+           "PkvError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpkv.so")
@@ -42,6 +43,11 @@ _SIGNATURES = {
     "pkv_paged_decode_attn": ([_P, _I32, _U64, _P, _I32, _F32, _P, _I32, _F32, _P, _U32, _P,
                                _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32, _U32, _P, _I32,
                                _F32, _U32, _U32, _P, _P, _U32, _P, _SZ, _P], _I32),
+    "pkv_paged_prefill_attn": ([_P, _I32, _U64, _P, _U32, _U32, _P, _I32, _F32, _P, _I32, _F32,
+                                _P, _U32, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32,
+                                _U32, _P, _P, _P], _I32),
+    "pkv_mla_cache_assemble": ([_P, _P, _I32, _U64, _U64, _P, _U32, _U32, _U32, _U32, _U32, _U32,
+                                _P, _P, _P], _I32),
 }
 
 
@@ -244,3 +250,70 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: flo
         q_rope_dim, _ptr(gate), _ptr(out),
         split_tokens, _ptr(workspace), ws_bytes, _stream()))
     return out
+
+
+def paged_prefill_attn(q, cu_q, k_cache, v_cache, block_tables, seq_lens, *, max_q_len: int,
+                       scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                       sliding_window: int = 0, sinks=None, out=None):
+    """Causal attention of the last q_len tokens of every sequence over the
+    paged cache (pkv_paged_prefill_attn).
+
+    q [total_q, Hq, D] BF16 (token stride free, heads packed); cu_q int32
+    [S+1]; k_cache / v_cache [nb, B, Hkv, D]; block_tables int32 [S, M];
+    seq_lens int32 [S] (including the new tokens); ``max_q_len`` >= every
+    q_len (host value).  Returns out FP32 [total_q, Hq, D].
+    """
+    _dev(q, cu_q, k_cache, v_cache, block_tables, seq_lens, sinks, out)
+    nb, B, Hkv, Dqk = _pool(k_cache, "k_cache")
+    nb2, B2, Hkv2, Dv = _pool(v_cache, "v_cache")
+    if (nb2, B2, Hkv2) != (nb, B, Hkv):
+        raise ValueError("K and V pools must have the same blocks and heads")
+    stride = _token_stride(q, "q")
+    T, Hq = q.shape[0], q.shape[1]
+    S = seq_lens.numel()
+    if cu_q.dtype != torch.int32 or cu_q.numel() != S + 1 or not cu_q.is_contiguous():
+        raise ValueError("cu_q must be int32 [S+1] contiguous")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or \
+            block_tables.shape[0] != S or not block_tables.is_contiguous():
+        raise ValueError("block_tables must be int32 [S, M] contiguous")
+    if seq_lens.dtype != torch.int32 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be int32 [S] contiguous")
+    if sinks is not None and (sinks.dtype != torch.float32 or sinks.numel() != Hq or
+                              not sinks.is_contiguous()):
+        raise ValueError("sinks must be FP32 [Hq] contiguous")
+    if out is None:
+        out = torch.zeros((T, Hq, Dv), dtype=torch.float32, device=q.device)
+    elif out.dtype != torch.float32 or out.shape != (T, Hq, Dv) or not out.is_contiguous():
+        raise ValueError("out must be FP32 [total_q, Hq, Dv] contiguous")
+    _check(load().pkv_paged_prefill_attn(
+        _ptr(q), _dtype(q), stride, _ptr(cu_q), max_q_len, T, _ptr(k_cache), _dtype(k_cache),
+        k_scale, _ptr(v_cache), _dtype(v_cache), v_scale, _ptr(block_tables),
+        block_tables.shape[1], _ptr(seq_lens), S, nb, Hq, Hkv, Dqk, Dv, B, scale, sliding_window,
+        _ptr(sinks), _ptr(out), _stream()))
+    return out
+
+
+def mla_cache_assemble(kv_latent, k_rope, slot_mapping, k_cache, v_cache, *, kv_lora: int,
+                       rope: int):
+    """MLA cache rows at their slots (pkv_mla_cache_assemble): K = [latent |
+    k_rope | 0], V = [latent | 0].  kv_latent [T, >= kv_lora] and k_rope
+    [T, >= rope] (row stride free); caches [nb, B, 1, cache_dim]."""
+    _dev(kv_latent, k_rope, slot_mapping, k_cache, v_cache)
+    nb, B, H, dim = _pool(k_cache, "k_cache")
+    if tuple(v_cache.shape) != (nb, B, H, dim) or not v_cache.is_contiguous() or H != 1:
+        raise ValueError("caches must be [num_blocks, block_size, 1, cache_dim], alike")
+    if kv_latent.dim() != 2 or kv_latent.stride(1) != 1 or k_rope.dim() != 2 or \
+            k_rope.stride(1) != 1:
+        raise ValueError("kv_latent and k_rope must be [T, width] with unit element stride")
+    T = kv_latent.shape[0]
+    if k_rope.shape[0] != T or slot_mapping.numel() != T or slot_mapping.dtype != torch.int64:
+        raise ValueError("k_rope [T, rope] and slot_mapping int64 [T] must match kv_latent")
+    dt = _dtype(kv_latent)
+    if _dtype(k_rope) != dt or _dtype(k_cache) != dt or _dtype(v_cache) != dt:
+        raise ValueError("kv_latent, k_rope and the caches must share one dtype")
+    ls = kv_latent.stride(0) if T > 1 else kv_latent.shape[1]
+    rs = k_rope.stride(0) if T > 1 else k_rope.shape[1]
+    _check(load().pkv_mla_cache_assemble(
+        _ptr(kv_latent), _ptr(k_rope), dt, ls, rs, _ptr(slot_mapping), T, kv_lora, rope, dim, B, nb,
+        _ptr(k_cache), _ptr(v_cache), _stream()))
+    return k_cache, v_cache

@@ -16,7 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["abi.cpp", "slots.hip", "cache_write_v.hip", "cache_write_k.hip", "decode_attn.hip"]
+SOURCES = ["abi.cpp", "slots.hip", "cache_write_v.hip", "cache_write_k.hip", "decode_attn.hip",
+           "prefill_attn.hip", "mla_cache.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,449 @@
+// prefill_attn.hip -- pkv_paged_prefill_attn: causal attention of the N new
+// tokens of every sequence over its paged KV cache (page 1, kv_cache.rs,
+// "batched prefill variants (N tokens)" of the paged kernels; the reading:
+// the q_len queries of a sequence are its last q_len tokens, already written
+// to the cache, and query i at position p = seq_len - q_len + i attends to
+// [lo, p], lo from the sliding window as in decode; sinks as in decode).
+//
+// Work decomposition.  Rows of the score matrix are (query token, query
+// head) pairs of one kv head's GQA group, token-major (row = i * G + g).  A
+// work-group takes 64 consecutive rows of one (sequence, kv head), one
+// wavefront per 16 rows, and walks the keys [lo_min, end_max) of its rows in
+// steps of two cache blocks.  Each step's K and V blocks are loaded once per
+// work-group (one 16-byte chunk of each per thread and block), written to
+// LDS -- K in the swizzled MFMA operand layout of KFrag, V row-major with a
+// 16-byte pad per row -- and read by all four waves; the next step's loads
+// are in flight while the current one is computed (two LDS buffers, one
+// barrier per step).  Per wave and cache block:
+//   S^T[t, row] = K[t, :] . q[row, :]   v_mfma_f32_16x16x32_bf16 (M=t, N=row)
+//   O[row, d]  += P[row, t] V[t, d]     v_mfma_f32_16x16x32_bf16 with the
+//                                       hi and lo BF16 halves of P along k
+// with the causal / window mask per row and online softmax in the log2
+// domain, as in decode.  All query tiles of one (sequence, kv head) are
+// dealt to the same XCD (work-group id % 8), so their repeated K/V reads
+// are served by that XCD's L2.
+#include "attn_common.h"
+
+namespace pkv {
+
+constexpr int kPWaves = 4;                   // waves per work-group
+constexpr int kPRows = 16 * kPWaves;         // query rows per work-group
+constexpr int kPThreads = 64 * kPWaves;
+constexpr int kPStep = 2;                    // cache blocks per step
+constexpr int kXcds = 8;                     // XCDs work-groups are dealt to
+
+struct PrefillArgs {
+    const void* q;
+    const void* k_cache;
+    const void* v_cache;
+    const int32_t* cu_q;
+    const int32_t* bt;
+    const int32_t* seq_lens;
+    const float* sinks;
+    float* out;
+    uint64_t q_stride;      // elements between query tokens
+    uint32_t total_q;       // rows of q and out
+    uint32_t M;             // max_blocks_per_seq
+    uint32_t num_blocks;
+    uint32_t Hq, Hkv, G;
+    uint32_t tiles;         // query tiles per (sequence, kv head) in the grid
+    uint32_t units;         // num_seqs * Hkv
+    float qk_scale;         // scale * log2(e) (* k_scale for E4M3 K)
+    float out_scale;        // v_scale for E4M3 V, else 1
+    uint32_t window;
+};
+
+__device__ __forceinline__ int32_t window_lo(uint32_t window, int32_t end)
+{
+    return (window > 0 && end > (int32_t)window) ? end - (int32_t)window : 0;
+}
+
+template <int KT, int VT, int D>
+__global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
+{
+    using KF = KFrag<KT, D>;
+    constexpr int NI = KF::NI, NL = KF::NL;
+    constexpr int CPR = KF::CPR;                       // K chunks per row
+    constexpr uint32_t KES = KT == 0 ? 2 : 1;
+    constexpr uint32_t VES = VT == 0 ? 2 : 1;
+    constexpr int NT = D / 16;                         // PV N-tiles
+    constexpr int DPL = D / 16;                        // V columns per lane
+    constexpr int VW = DPL * VES / 4;                  // V words per lane per row
+    constexpr int VCPR = D * VES / 16;                 // V chunks per row
+    constexpr int KTILE = 16 * CPR * 16;               // bytes of a K tile
+    constexpr int VROW = D * VES + 16;                 // padded V row in LDS
+    constexpr int VTILE = 16 * VROW;
+    constexpr int BLK = KTILE + VTILE;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][kPStep][BLK];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int kg = lane >> 4;
+    const int ln = lane & 15;
+
+    // work-group -> (unit, tile): the tiles of a unit share id % 8 (one XCD)
+    const uint32_t xcd = blockIdx.x % kXcds, k = blockIdx.x / kXcds;
+    const uint32_t unit = xcd + kXcds * (k / a.tiles);
+    const uint32_t tile = k % a.tiles;
+    if (unit >= a.units)
+        return;
+    const uint32_t s = unit / a.Hkv, kvh = unit % a.Hkv;
+    const int32_t q0 = a.cu_q[s];
+    const int32_t qlen = a.cu_q[s + 1] - q0;
+    const uint32_t G = a.G;
+    const uint32_t row0 = tile * kPRows;
+    if (qlen <= 0 || (uint64_t)row0 >= (uint64_t)qlen * G)
+        return;
+    const int32_t n = a.seq_lens[s];
+    const int32_t first_pos = n - qlen;                // position of query 0
+
+    // this lane's row (S^T column): query token i, head g
+    const uint32_t row = row0 + 16 * wave + ln;
+    const int32_t qi = (int32_t)(row / G);
+    const uint32_t g = row % G;
+    const bool row_ok = qi < qlen && (uint32_t)(q0 + qi) < a.total_q;
+    const int32_t end_r = row_ok ? first_pos + qi + 1 : 0;     // keys [lo_r, end_r)
+    const int32_t lo_r = window_lo(a.window, end_r);
+
+    // key range of the work-group and of this wave (rows are token-major)
+    const int32_t i_lo = (int32_t)(row0 / G);
+    const int32_t i_hi = min(qlen, (int32_t)((row0 + kPRows + G - 1) / G)) - 1;
+    const int32_t end_max = first_pos + i_hi + 1;
+    const int32_t lo_min = window_lo(a.window, first_pos + i_lo + 1);
+    const int32_t wi_lo = (int32_t)((row0 + 16 * wave) / G);
+    const int32_t wi_hi = min(qlen, (int32_t)((row0 + 16 * wave + 16 + G - 1) / G)) - 1;
+    const bool wave_live = wi_lo <= wi_hi;
+    const int32_t w_end = first_pos + wi_hi + 1;
+    const int32_t w_lo = window_lo(a.window, first_pos + wi_lo + 1);
+
+    uint32_t nblk = 0, blo = 0;
+    if (end_max > 0) {
+        nblk = min(((uint32_t)end_max + kBS - 1) / kBS, a.M);
+        blo = (uint32_t)max(lo_min, 0) / kBS;
+    }
+
+    // q fragments (B operand of S^T = K q^T): lane (row ln, kg)
+    bf16x8 qf[NI];
+    {
+        const uint16_t* qrow = (const uint16_t*)a.q + (uint64_t)(q0 + qi) * a.q_stride +
+                               (uint64_t)(kvh * G + g) * D;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            u32x4 w = u32x4{0u, 0u, 0u, 0u};
+            if (row_ok)
+                w = *(const u32x4*)(qrow + KF::phys(i, kg));
+            qf[i] = __builtin_bit_cast(bf16x8, w);
+        }
+    }
+
+    f32x4 o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+        o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = -INFINITY, l = 0.f;
+
+    // cooperative loads: thread tid owns K chunk tid and V chunk tid of each
+    // block of a step (16 rows x CPR / VCPR chunks)
+    const uint8_t* kbase = (const uint8_t*)a.k_cache;
+    const uint8_t* vbase = (const uint8_t*)a.v_cache;
+    const uint64_t krow_bytes = (uint64_t)a.Hkv * D * KES;
+    const uint64_t vrow_bytes = (uint64_t)a.Hkv * D * VES;
+    const bool k_loader = tid < 16 * CPR, v_loader = tid < 16 * VCPR;
+    const uint32_t k_r = tid / CPR, k_c = tid % CPR;
+    const uint32_t v_r = tid / VCPR, v_c = tid % VCPR;
+    const uint64_t k_off = k_r * krow_bytes + (uint64_t)kvh * D * KES + 16u * k_c;
+    const uint64_t v_off = v_r * vrow_bytes + (uint64_t)kvh * D * VES + 16u * v_c;
+    const uint32_t k_lds = KF::lds_off(k_r, k_c);
+    const uint32_t v_lds = KTILE + v_r * VROW + 16u * v_c;
+
+    struct Stage {
+        u32x4 k[kPStep], v[kPStep];
+    };
+    auto block_id = [&](uint32_t b) -> int32_t {
+        const int32_t pb = b < nblk ? a.bt[(uint64_t)s * a.M + b] : -1;
+        return pb;
+    };
+    // an unmapped block (or one past the range) is read from block 0 and masked
+    auto load_step = [&](uint32_t b0, Stage& st) {
+#pragma unroll
+        for (int j = 0; j < kPStep; ++j) {
+            int32_t pb = block_id(b0 + j);
+            pb = (pb >= 0 && (uint32_t)pb < a.num_blocks) ? pb : 0;
+            const uint64_t blk = (uint64_t)pb * kBS;
+            if (k_loader)
+                st.k[j] = load_nt((const u32x4*)(kbase + blk * krow_bytes + k_off));
+            if (v_loader)
+                st.v[j] = load_nt((const u32x4*)(vbase + blk * vrow_bytes + v_off));
+        }
+    };
+    auto store_step = [&](int buf, const Stage& st) {
+#pragma unroll
+        for (int j = 0; j < kPStep; ++j) {
+            if (k_loader)
+                *(u32x4*)&lds[buf][j][k_lds] = st.k[j];
+            if (v_loader)
+                *(u32x4*)&lds[buf][j][v_lds] = st.v[j];
+        }
+    };
+
+    // LDS read positions: K operand chunk of MFMA group jj; V rows 4kg + r
+    uint32_t lds_r[NL];
+#pragma unroll
+    for (int jj = 0; jj < NL; ++jj)
+        lds_r[jj] = KF::lds_off(ln, KF::op_chunk(jj, kg));
+    const uint32_t v_rd = KTILE + (4 * kg) * VROW + DPL * ln * VES;
+
+    auto compute_step = [&](int buf, uint32_t b0) {
+        if (!wave_live)
+            return;
+        f32x4 sacc[kPStep];
+        bool blk_ok[kPStep];
+#pragma unroll
+        for (int j = 0; j < kPStep; ++j) {
+            const uint32_t b = b0 + j;
+            const int32_t pb = block_id(b);
+            blk_ok[j] = b < nblk && pb >= 0 && (uint32_t)pb < a.num_blocks &&
+                        (int32_t)(b * kBS) < w_end && (int32_t)(b * kBS + kBS) > w_lo;
+            sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (blk_ok[j]) {
+                const uint8_t* kt = &lds[buf][j][0];
+                u32x4 kop[NL];
+#pragma unroll
+                for (int jj = 0; jj < NL; ++jj)
+                    kop[jj] = *(const u32x4*)(kt + lds_r[jj]);
+#pragma unroll
+                for (int i = 0; i < NI; ++i)
+                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KF::operand(kop, i), qf[i],
+                                                                      sacc[j], 0, 0, 0);
+            }
+        }
+        // scores of this lane's row (ln) at keys (b0 + j) * 16 + 4kg + r
+        float sv[kPStep][4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kPStep; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int32_t t = (int32_t)((b0 + j) * kBS) + 4 * kg + r;
+                const bool ok = blk_ok[j] && t >= lo_r && t < end_r;
+                sv[j][r] = ok ? sacc[j][r] * a.qk_scale : -INFINITY;
+                mx = fmaxf(mx, sv[j][r]);
+            }
+        mx = wave_max_xor16_32(mx);
+        const float m_new = fmaxf(m, mx);
+        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+        float p[kPStep][4];
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < kPStep; ++j) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                p[j][r] = __builtin_amdgcn_exp2f(sv[j][r] - m_ref);
+            psum += (p[j][0] + p[j][1]) + (p[j][2] + p[j][3]);
+        }
+        l = l * alpha + psum;
+        m = m_new;
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * kg + r, 64);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    o[nt][r] *= ar;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < kPStep; ++j) {
+            if (!blk_ok[j])
+                continue;
+            // A operand: k = 8kg + 0..3 -> P_hi of keys 4kg + 0..3, k = 8kg + 4..7 -> P_lo
+            uint32_t ph[2], pl[2];
+#pragma unroll
+            for (int r2 = 0; r2 < 2; ++r2) {
+                const uint32_t hw = pack_bf16(p[j][2 * r2], p[j][2 * r2 + 1]);
+                ph[r2] = hw;
+                pl[r2] = pack_bf16(p[j][2 * r2] - bf16_lo(hw), p[j][2 * r2 + 1] - bf16_hi(hw));
+            }
+            const bf16x8 a_p = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], pl[0], pl[1]});
+            // V rows 4kg + r of the block; keys outside [w_lo, w_end) read as
+            // zero (they may lie past the sequence end)
+            const uint8_t* vt = &lds[buf][j][0] + v_rd;
+            uint32_t vr[4][VW];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int32_t t = (int32_t)((b0 + j) * kBS) + 4 * kg + r;
+                const bool keep = t >= w_lo && t < w_end;
+                if constexpr (VW == 4) {
+                    const u32x4 x = *(const u32x4*)(vt + r * VROW);
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) vr[r][w] = keep ? x[w] : 0u;
+                } else if constexpr (VW == 2) {
+                    const u32x2 x = *(const u32x2*)(vt + r * VROW);
+#pragma unroll
+                    for (int w = 0; w < 2; ++w) vr[r][w] = keep ? x[w] : 0u;
+                } else {
+                    const uint32_t x = *(const uint32_t*)(vt + r * VROW);
+                    vr[r][0] = keep ? x : 0u;
+                }
+            }
+            [[maybe_unused]] float vf[4][DPL];
+            if constexpr (VT == 1) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int w = 0; w < VW; ++w) {
+                        const f32x2 lo = unpack_e4m3x2(vr[r][w], false);
+                        const f32x2 hi = unpack_e4m3x2(vr[r][w], true);
+                        vf[r][4 * w] = lo.x;
+                        vf[r][4 * w + 1] = lo.y;
+                        vf[r][4 * w + 2] = hi.x;
+                        vf[r][4 * w + 3] = hi.y;
+                    }
+            }
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                uint32_t b01, b23;
+                if constexpr (VT == 1) {
+                    b01 = hi16_pair(__float_as_uint(vf[0][nt]), __float_as_uint(vf[1][nt]));
+                    b23 = hi16_pair(__float_as_uint(vf[2][nt]), __float_as_uint(vf[3][nt]));
+                } else {
+                    const int w = nt >> 1;
+                    if (nt & 1) {
+                        b01 = hi16_pair(vr[0][w], vr[1][w]);
+                        b23 = hi16_pair(vr[2][w], vr[3][w]);
+                    } else {
+                        b01 = lo16_pair(vr[0][w], vr[1][w]);
+                        b23 = lo16_pair(vr[2][w], vr[3][w]);
+                    }
+                }
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{b01, b23, b01, b23});
+                o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p, bv, o[nt], 0, 0, 0);
+            }
+        }
+    };
+
+    if (nblk > blo) {
+        const uint32_t nsteps = (nblk - blo + kPStep - 1) / kPStep;
+        Stage st;
+        load_step(blo, st);
+        store_step(0, st);
+        __syncthreads();
+        for (uint32_t j = 0; j < nsteps; ++j) {
+            const uint32_t b0 = blo + j * kPStep;
+            const bool more = j + 1 < nsteps;
+            if (more)
+                load_step(b0 + kPStep, st);
+            compute_step(j & 1, b0);
+            if (more)
+                store_step((j + 1) & 1, st);
+            __syncthreads();
+        }
+    }
+
+    // finished rows: o[nt][r] is row 4kg + r of the wave, column DPL * ln + nt
+    l = wave_sum_xor16_32(l);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t wr = 4 * kg + r;                  // row within the wave
+        const float lr = __shfl(l, (int)wr, 64);
+        const float mr = __shfl(m, (int)wr, 64);
+        const uint32_t orow = row0 + 16 * wave + wr;
+        const int32_t oi = (int32_t)(orow / G);
+        if (oi >= qlen || (uint32_t)(q0 + oi) >= a.total_q)
+            continue;
+        const uint32_t h = kvh * G + orow % G;
+        const float inv = norm_factor(mr, lr, a.sinks, h, a.out_scale);
+        float* dst = a.out + ((uint64_t)(q0 + oi) * a.Hq + h) * D + (uint64_t)DPL * ln;
+#pragma unroll
+        for (int nt = 0; nt < NT; nt += 4)
+            *(f32x4*)(dst + nt) = f32x4{o[nt][r] * inv, o[nt + 1][r] * inv, o[nt + 2][r] * inv,
+                                        o[nt + 3][r] * inv};
+    }
+}
+
+}  // namespace pkv
+
+extern "C" int pkv_paged_prefill_attn(const void* q, pkv_dtype q_dtype, uint64_t q_token_stride,
+                                      const int32_t* cu_q, uint32_t max_q_len, uint32_t total_q,
+                                      const void* k_cache, pkv_dtype k_dtype, float k_scale,
+                                      const void* v_cache, pkv_dtype v_dtype, float v_scale,
+                                      const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                                      const int32_t* seq_lens, uint32_t num_seqs,
+                                      uint32_t num_blocks, uint32_t num_q_heads,
+                                      uint32_t num_kv_heads, uint32_t head_dim_qk,
+                                      uint32_t head_dim_v, uint32_t block_size, float scale,
+                                      uint32_t sliding_window, const float* sinks, float* out,
+                                      void* stream)
+{
+    using namespace pkv;
+    clear_error();
+    if (num_seqs == 0 || max_q_len == 0 || total_q == 0)
+        return PKV_OK;
+    if (!q || !cu_q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
+        return fail(PKV_ERR_INVALID, "paged_prefill_attn: q, cu_q, caches, block_tables, seq_lens and out must be non-NULL");
+    if (!valid_dtype(q_dtype) || !valid_dtype(k_dtype) || !valid_dtype(v_dtype))
+        return fail(PKV_ERR_INVALID, "paged_prefill_attn: bad dtype");
+    if (!num_q_heads || !num_kv_heads || !head_dim_qk || !head_dim_v || !max_blocks_per_seq ||
+        !num_blocks || !block_size)
+        return fail(PKV_ERR_INVALID, "paged_prefill_attn: zero dimension");
+    if (num_q_heads % num_kv_heads)
+        return fail(PKV_ERR_INVALID, "paged_prefill_attn: num_q_heads %% num_kv_heads != 0");
+    if (block_size != (uint32_t)kBS)
+        return fail(PKV_ERR_UNSUPPORTED, "paged_prefill_attn: block_size must be 16");
+    if (q_token_stride < (uint64_t)num_q_heads * head_dim_qk)
+        return fail(PKV_ERR_INVALID, "paged_prefill_attn: q_token_stride smaller than a query row");
+    const uint32_t G = num_q_heads / num_kv_heads;
+    if (q_dtype != PKV_BF16 || (k_dtype != PKV_BF16 && k_dtype != PKV_FP8_E4M3) ||
+        (v_dtype != PKV_BF16 && v_dtype != PKV_FP8_E4M3))
+        return fail(PKV_ERR_UNSUPPORTED, "paged_prefill_attn: dtypes (q,K,V) must be (BF16, BF16|E4M3, BF16|E4M3)");
+    if (head_dim_qk != head_dim_v || (head_dim_qk != 64 && head_dim_qk != 128))
+        return fail(PKV_ERR_UNSUPPORTED, "paged_prefill_attn: head_dim_qk == head_dim_v in {64,128}");
+    if (16 % G)
+        return fail(PKV_ERR_UNSUPPORTED, "paged_prefill_attn: GQA group must be 1, 2, 4, 8 or 16");
+    if ((q_token_stride * 2) % 16 || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(out))
+        return fail(PKV_ERR_UNSUPPORTED, "paged_prefill_attn: pointers and q stride must be 16-byte aligned");
+    if (k_dtype == PKV_FP8_E4M3 && !(k_scale > 0.0f && k_scale < INFINITY))
+        return fail(PKV_ERR_INVALID, "paged_prefill_attn: k_scale must be finite and > 0");
+    if (v_dtype == PKV_FP8_E4M3 && !(v_scale > 0.0f && v_scale < INFINITY))
+        return fail(PKV_ERR_INVALID, "paged_prefill_attn: v_scale must be finite and > 0");
+    const uint64_t tiles = ((uint64_t)max_q_len * G + kPRows - 1) / kPRows;
+    const uint64_t units = (uint64_t)num_seqs * num_kv_heads;
+    const uint64_t groups = (units + kXcds - 1) / kXcds * kXcds * tiles;
+    if (groups >= (1ull << 31))
+        return fail(PKV_ERR_UNSUPPORTED, "paged_prefill_attn: grid too large");
+
+    PrefillArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.cu_q = cu_q;
+    a.bt = block_tables;
+    a.seq_lens = seq_lens;
+    a.sinks = sinks;
+    a.out = out;
+    a.q_stride = q_token_stride;
+    a.total_q = total_q;
+    a.M = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.Hq = num_q_heads;
+    a.Hkv = num_kv_heads;
+    a.G = G;
+    a.tiles = (uint32_t)tiles;
+    a.units = (uint32_t)units;
+    a.qk_scale = scale * kLog2e * (k_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f);
+    a.out_scale = v_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    a.window = sliding_window;
+    hipStream_t st = (hipStream_t)stream;
+    const int kt = k_dtype == PKV_FP8_E4M3, vt = v_dtype == PKV_FP8_E4M3;
+    const dim3 grid((uint32_t)groups), block(kPThreads);
+#define PKV_PREFILL(KT, VT, D)                                                                  \
+    if (kt == KT && vt == VT && head_dim_qk == D)                                              \
+        hipLaunchKernelGGL((prefill_mfma_kernel<KT, VT, D>), grid, block, 0, st, a);
+    PKV_PREFILL(0, 0, 128) PKV_PREFILL(0, 0, 64) PKV_PREFILL(1, 0, 128) PKV_PREFILL(1, 0, 64)
+    PKV_PREFILL(0, 1, 128) PKV_PREFILL(0, 1, 64) PKV_PREFILL(1, 1, 128) PKV_PREFILL(1, 1, 64)
+#undef PKV_PREFILL
+    return check_launch("paged_prefill_attn");
+}

@@ -144,3 +144,35 @@ def test_workspace_query(lib):
     assert lib.pkv_decode_workspace_bytes(2, 4, 1, 64, 128, 16, 1010, 1024) == 2 * 2 * 4 * 66 * 4
     # a window never asks for more than no window
     assert lib.pkv_decode_workspace_bytes(256, 32, 8, 128, 512, 16, 100000, 0) == n
+
+
+def test_prefill_and_mla_validation(lib):
+    def pre(**kw):
+        a = dict(q=FAKE, qd=0, qs=32 * 128, cu=FAKE, mql=8, tq=64, k=FAKE, kd=0, ks=1.0, v=FAKE,
+                 vd=0, vs=1.0, bt=FAKE, M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128,
+                 B=16, scale=0.1, win=0, sinks=None, out=FAKE)
+        a.update(kw)
+        return lib.pkv_paged_prefill_attn(*a.values(), None)
+    assert pre(S=0) == 0 and pre(mql=0) == 0       # no work
+    assert pre(out=None) == -1
+    assert pre(Hq=30) == -1                       # Hq % Hkv
+    assert pre(Hq=24) == -2                       # group of 3 does not divide 16
+    assert pre(Dqk=192, Dv=192, qs=32 * 192) == -2
+    assert pre(qd=2) == -2                        # FP32 q not supported here
+    assert pre(kd=1, ks=0.0) == -1
+    assert pre(vd=1, vs=float("nan")) == -1
+    assert pre(qs=100) == -1
+    assert pre(B=32) == -2
+    assert _err(lib) != ""
+
+    def mla(**kw):
+        a = dict(lat=FAKE, rope_p=FAKE, dt=0, ls=512, rs=64, slots=FAKE, T=4, lora=512, rope=64,
+                 dim=576, B=16, nb=4, kc=FAKE, vc=FAKE)
+        a.update(kw)
+        return lib.pkv_mla_cache_assemble(*a.values(), None)
+    assert mla(T=0) == 0
+    assert mla(slots=None) == -1
+    assert mla(dim=512) == -1                     # kv_lora + rope > cache_dim
+    assert mla(ls=500) == -1                      # latent stride below the row
+    assert mla(lora=500, ls=500, dim=576) == -2   # 1000 bytes: not a 16-byte multiple
+    assert mla(dt=1) == -2                        # E4M3 not an MLA cache dtype here
