@@ -15,7 +15,11 @@ FP8 E4M3 K with k_scale = max|stored K| / 448, BF16 V).  Variants of the
 latter: ``decode_fp8kv_64seq_long`` (E4M3 V too, v_scale = max|V| / 448) and
 ``decode_fp8k_64seq_long_window4096_sinks`` (a 4096-token sliding window and
 one sink logit per query head; only the window's tokens are read and
-counted).
+counted).  ``prefill_bf16_256seq_chunk256`` is chunked prefill on the first
+workload's pool: the last min(256, n) tokens of every sequence are the new
+chunk (slots, K write, V write, then causal prefill attention over the whole
+cache); its metric is the attention's algorithmic TFLOP/s and its roofline
+is the dense BF16 MFMA peak.
 
 Prints one JSON line.  ``value`` is the algorithmic HBM bytes of one step
 divided by the step time (GB/s); the decode attention's KV read is >99.9% of
@@ -45,6 +49,8 @@ WORKLOADS = {
     "decode_fp8kv_64seq_long": (3, True, 0, False),
     "decode_fp8k_64seq_long_window4096_sinks": (3, False, 4096, True),
 }
+PREFILL_WORKLOADS = {"prefill_bf16_256seq_chunk256": (2, 256)}
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def parse():
@@ -52,7 +58,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode_bf16_256seq", choices=sorted(WORKLOADS))
+    p.add_argument("--workload", default="decode_bf16_256seq",
+                   choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--split-tokens", type=int, default=0)
     p.add_argument("--copy-probe", action="store_true",
@@ -109,11 +116,11 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
 
 
-def traffic_from_profile(kernel_src_hash: str, workload: str):
-    """HBM bytes per decode call measured with rocprofv3 --pmc (FETCH_SIZE and
+def traffic_from_profile(kernel_src_hash: str, workload: str, kernel: str = "decode_attn"):
+    """HBM bytes per call measured with rocprofv3 --pmc (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain copy's counters), stored in profiles/ with the
     hash of the kernel source they were taken on; None when stale or absent."""
-    path = os.path.join(ROOT, "profiles", f"decode_attn_{workload}_pmc.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -124,10 +131,13 @@ def traffic_from_profile(kernel_src_hash: str, workload: str):
     return float(t.group(1))
 
 
-def kernel_source_hash():
+def kernel_source_hash(source: str = "decode_attn.hip"):
+    """Hash of a kernel's source file and the attention header it includes."""
     import hashlib
-    src = os.path.join(ROOT, "paged_kv_cache_fill_amd", "csrc", "decode_attn.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in (source, "attn_common.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_fill_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def main():
@@ -138,6 +148,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.workload in PREFILL_WORKLOADS:
+        run_prefill(args)
         return
 
     import torch
@@ -318,6 +331,136 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(idx, lay, k_scale, v_fp8, v_scale, window,
                                               None if sinks is None else sinks.cpu().numpy())
+    print(json.dumps(result), flush=True)
+
+
+def prefill_flops(lens, qlens, Hq, D, Dv):
+    """Algorithmic FLOPs of causal prefill attention: query i of a sequence
+    of n tokens with q_len new ones attends to n - q_len + i + 1 keys, each
+    costing 2 D (q.k) + 2 Dv (p v) per query head."""
+    keys = 0
+    for n, c in zip(np.asarray(lens, np.int64), np.asarray(qlens, np.int64)):
+        keys += int(c * (n - c) + c * (c + 1) // 2)
+    return keys * Hq * (2 * D + 2 * Dv)
+
+
+def run_prefill(args):
+    import torch
+
+    import paged_kv_cache_fill_amd as pkv
+    import pkv_workloads as W
+
+    pkv.load()
+    idx, chunk = PREFILL_WORKLOADS[args.workload]
+    lay = W.layout(idx)
+    cfg = lay.cfg
+    S, Hq, Hkv, D, B = lay.num_seqs, cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], 16
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    lens = lay.seq_lens.astype(np.int64)
+    qlens = np.minimum(lens, chunk)
+    hist = lens - qlens
+    Th, Tc = int(hist.sum()), int(qlens.sum())
+    log(f"workload {args.workload}: {S} seqs, {int(lens.sum())} tokens, chunk {chunk} "
+        f"({Tc} new tokens), pool {lay.num_blocks} blocks")
+    k_pool = torch.empty((lay.num_blocks, B, Hkv, D), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.empty_like(k_pool)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    seq_lens = torch.from_numpy(lay.seq_lens).to(dev)
+    w = torch.from_numpy(W.norm_weight(idx).view(np.int16)).to(dev).view(torch.bfloat16)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.int32)).to(dev)
+
+    def positions(start, count):
+        cu = np.zeros(S + 1, np.int64)
+        cu[1:] = np.cumsum(count)
+        pos = np.concatenate([np.arange(a, a + c, dtype=np.int32) for a, c in zip(start, count)])
+        return i32(start), i32(cu), i32(pos), int(cu[-1])
+
+    # history: the first n - q_len tokens of every sequence, written once
+    hs, hcu, hpos, _ = positions(np.zeros(S, np.int64), hist)
+    k_hist = W.device_normal(idx, W.S_K, (Th, Hkv, D), torch.bfloat16, dev)
+    v_hist = W.device_normal(idx, W.S_V, (Th, Hkv, D), torch.bfloat16, dev)
+    slots_h = torch.empty(Th, dtype=torch.int64, device=dev)
+    pkv.fill_slots(slots_h, bt, hs, hcu, B)
+    pkv.cache_write_k_fused(k_hist, slots_h, k_pool, norm_weight=w, eps=cfg["eps"], pos_t=hpos,
+                            theta=cfg["theta"])
+    pkv.cache_write_v(v_hist, slots_h, v_pool)
+    del k_hist, v_hist
+    # the chunk: slots, K write, V write, prefill attention
+    cs, ccu, cpos, _ = positions(hist, qlens)
+    k_new = W.device_normal(idx, W.S_KNEW, (Tc, Hkv, D), torch.bfloat16, dev)
+    v_new = W.device_normal(idx, W.S_VNEW, (Tc, Hkv, D), torch.bfloat16, dev)
+    q = W.device_normal(idx, W.S_Q, (Tc, Hq, D), torch.bfloat16, dev)
+    slots_c = torch.empty(Tc, dtype=torch.int64, device=dev)
+    out = torch.empty((Tc, Hq, D), dtype=torch.float32, device=dev)
+    scale = D ** -0.5
+
+    def step_writes():
+        pkv.fill_slots(slots_c, bt, cs, ccu, B)
+        pkv.cache_write_k_fused(k_new, slots_c, k_pool, norm_weight=w, eps=cfg["eps"], pos_t=cpos,
+                                theta=cfg["theta"])
+        pkv.cache_write_v(v_new, slots_c, v_pool)
+
+    def step_attn():
+        pkv.paged_prefill_attn(q, ccu, k_pool, v_pool, bt, seq_lens, max_q_len=chunk,
+                               scale=scale, out=out)
+
+    def step():
+        step_writes()
+        step_attn()
+
+    def time_call(fn, reps):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    attn_ms = float(np.mean(time_call(step_attn, args.steps)))
+    write_ms = float(np.mean(time_call(step_writes, args.steps)))
+    flops = prefill_flops(lens, qlens, Hq, D, D)
+    tflops = flops / (attn_ms * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms (prefill attention {attn_ms:.3f} ms = {tflops:.1f} TFLOP/s, "
+        f"chunk writes {write_ms * 1e3:.1f} us)")
+    result = {
+        "metric": "paged prefill attention TFLOP/s (chunked prefill over the paged cache)",
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 q/K/V, f32 accumulate",
+        "data": "synthetic (seeded)",
+        "config": {"workload": args.workload, "num_seqs": S, "chunk": chunk,
+                   "new_tokens": Tc, "total_tokens": int(lens.sum()), "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": B,
+                   "parallelism": "single GPU"},
+        "prefill_attn": {"ms": round(attn_ms, 4), "algorithmic_flops": flops,
+                         "TFLOP_per_s": round(tflops, 1)},
+        "chunk_writes_us": round(write_ms * 1e3, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic_from_profile(kernel_source_hash("prefill_attn.hip"),
+                                                     args.workload, "prefill_attn"),
+                     "kernel": "paged_prefill_attn"},
+        "cpu_baseline": None,
+    }
     print(json.dumps(result), flush=True)
 
 

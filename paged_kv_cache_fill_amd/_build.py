@@ -19,6 +19,11 @@ LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = ["abi.cpp", "slots.hip", "cache_write_v.hip", "cache_write_k.hip", "decode_attn.hip",
            "prefill_attn.hip", "mla_cache.hip"]
 
+# Per-source flags: the prefill kernel keeps its MFMA accumulators in VGPRs
+# (the accumulator-register form made the compiler copy them back and forth
+# around every online-softmax rescale).
+EXTRA = {"prefill_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
@@ -34,7 +39,7 @@ def build(verbose: bool = False) -> str:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

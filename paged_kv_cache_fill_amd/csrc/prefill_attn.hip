@@ -27,10 +27,14 @@
 namespace pkv {
 
 constexpr int kPWaves = 4;                   // waves per work-group
-constexpr int kPRows = 16 * kPWaves;         // query rows per work-group
-constexpr int kPThreads = 64 * kPWaves;
 constexpr int kPStep = 2;                    // cache blocks per step
+constexpr int kPPre = 1;                     // steps whose loads are in flight
+constexpr int kPTiles = 2;                   // 16-row tiles per wave
 constexpr int kXcds = 8;                     // XCDs work-groups are dealt to
+// A row's exponent reference moves only when its running max passes it by
+// more than this (log2 units): weights stay below 2^8, exact in the BF16
+// hi + lo split and in FP32, and the O rescale becomes rare.
+constexpr float kLazyRescale = 8.0f;
 
 struct PrefillArgs {
     const void* q;
@@ -58,10 +62,23 @@ __device__ __forceinline__ int32_t window_lo(uint32_t window, int32_t end)
     return (window > 0 && end > (int32_t)window) ? end - (int32_t)window : 0;
 }
 
-template <int KT, int VT, int D>
-__global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
+// NW waves of RT x 16 query rows, STEP cache blocks per step, PF steps of
+// loads in flight (a ring of register stages; loads are unconditional --
+// steps past the range re-read block 0 -- so the compiler's wait before a
+// stage's LDS write covers that stage only).  A wave's RT row tiles share
+// every K operand read from LDS and every V operand built from it.
+// The block table is a restrict parameter of its own: its wave-uniform
+// entries are then read through the scalar cache, and waiting for them does
+// not drain the vector loads in flight.
+template <int KT, int VT, int D, int NW, int STEP, int PF, int RT>
+__global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
+                                                               const int32_t* __restrict__ bt)
 {
     using KF = KFrag<KT, D>;
+    constexpr int kWRows = 16 * RT;                    // query rows per wave
+    constexpr int kPRows = kWRows * NW;                // ... per work-group
+    constexpr int kPThreads = 64 * NW;
+    constexpr int kPStep = STEP;
     constexpr int NI = KF::NI, NL = KF::NL;
     constexpr int CPR = KF::CPR;                       // K chunks per row
     constexpr uint32_t KES = KT == 0 ? 2 : 1;
@@ -78,7 +95,9 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform (scalar) so that every wave-level bound and block test
+    // below is a scalar value and its branches are uniform
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int kg = lane >> 4;
     const int ln = lane & 15;
 
@@ -98,24 +117,31 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
     const int32_t n = a.seq_lens[s];
     const int32_t first_pos = n - qlen;                // position of query 0
 
-    // this lane's row (S^T column): query token i, head g
-    const uint32_t row = row0 + 16 * wave + ln;
-    const int32_t qi = (int32_t)(row / G);
-    const uint32_t g = row % G;
-    const bool row_ok = qi < qlen && (uint32_t)(q0 + qi) < a.total_q;
-    const int32_t end_r = row_ok ? first_pos + qi + 1 : 0;     // keys [lo_r, end_r)
-    const int32_t lo_r = window_lo(a.window, end_r);
+    // this lane's rows (S^T columns), one per row tile: query token, head
+    const uint32_t wrow0 = row0 + kWRows * wave;
+    int32_t end_r[RT], lo_r[RT];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const uint32_t row = wrow0 + 16 * t + ln;
+        const int32_t qi = (int32_t)(row / G);
+        const bool ok = qi < qlen && (uint32_t)(q0 + qi) < a.total_q;
+        end_r[t] = ok ? first_pos + qi + 1 : 0;      // keys [lo_r, end_r)
+        lo_r[t] = window_lo(a.window, end_r[t]);
+    }
 
     // key range of the work-group and of this wave (rows are token-major)
     const int32_t i_lo = (int32_t)(row0 / G);
     const int32_t i_hi = min(qlen, (int32_t)((row0 + kPRows + G - 1) / G)) - 1;
     const int32_t end_max = first_pos + i_hi + 1;
     const int32_t lo_min = window_lo(a.window, first_pos + i_lo + 1);
-    const int32_t wi_lo = (int32_t)((row0 + 16 * wave) / G);
-    const int32_t wi_hi = min(qlen, (int32_t)((row0 + 16 * wave + 16 + G - 1) / G)) - 1;
+    const int32_t wi_lo = (int32_t)(wrow0 / G);
+    const int32_t wi_hi = min(qlen, (int32_t)((wrow0 + kWRows + G - 1) / G)) - 1;
     const bool wave_live = wi_lo <= wi_hi;
     const int32_t w_end = first_pos + wi_hi + 1;
     const int32_t w_lo = window_lo(a.window, first_pos + wi_lo + 1);
+    // keys every row of the wave attends to: [in_lo, in_end)
+    const int32_t in_end = first_pos + wi_lo + 1;
+    const int32_t in_lo = window_lo(a.window, w_end);
 
     uint32_t nblk = 0, blo = 0;
     if (end_max > 0) {
@@ -123,25 +149,33 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
         blo = (uint32_t)max(lo_min, 0) / kBS;
     }
 
-    // q fragments (B operand of S^T = K q^T): lane (row ln, kg)
-    bf16x8 qf[NI];
-    {
+    // q fragments (B operand of S^T = K q^T): lane (row ln, kg), per row tile
+    bf16x8 qf[RT][NI];
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+        const uint32_t row = wrow0 + 16 * t + ln;
+        const int32_t qi = (int32_t)(row / G);
         const uint16_t* qrow = (const uint16_t*)a.q + (uint64_t)(q0 + qi) * a.q_stride +
-                               (uint64_t)(kvh * G + g) * D;
+                               (uint64_t)(kvh * G + row % G) * D;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             u32x4 w = u32x4{0u, 0u, 0u, 0u};
-            if (row_ok)
+            if (qi < qlen && (uint32_t)(q0 + qi) < a.total_q)
                 w = *(const u32x4*)(qrow + KF::phys(i, kg));
-            qf[i] = __builtin_bit_cast(bf16x8, w);
+            qf[t][i] = __builtin_bit_cast(bf16x8, w);
         }
     }
 
-    f32x4 o[NT];
+    f32x4 o[RT][NT];
+    float m[RT], l[RT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-        o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY, l = 0.f;
+    for (int t = 0; t < RT; ++t) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m[t] = -INFINITY;
+        l[t] = 0.f;
+    }
 
     // cooperative loads: thread tid owns K chunk tid and V chunk tid of each
     // block of a step (16 rows x CPR / VCPR chunks)
@@ -149,9 +183,17 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
     const uint8_t* vbase = (const uint8_t*)a.v_cache;
     const uint64_t krow_bytes = (uint64_t)a.Hkv * D * KES;
     const uint64_t vrow_bytes = (uint64_t)a.Hkv * D * VES;
-    const bool k_loader = tid < 16 * CPR, v_loader = tid < 16 * VCPR;
-    const uint32_t k_r = tid / CPR, k_c = tid % CPR;
-    const uint32_t v_r = tid / VCPR, v_c = tid % VCPR;
+    // K chunks on threads [0, 16 CPR), V chunks on the next 16 VCPR threads
+    // when the work-group has that many, else on threads [0, 16 VCPR) too
+    // (every thread loads -- threads past the chunk count re-load a chunk and
+    // do not store it -- so the loads are not behind an exec-mask branch)
+    constexpr int V_FIRST = 16 * CPR + 16 * VCPR <= kPThreads ? 16 * CPR : 0;
+    const int vtid = tid - V_FIRST;
+    const bool k_loader = tid < 16 * CPR, v_loader = vtid >= 0 && vtid < 16 * VCPR;
+    const uint32_t kt_ = (uint32_t)tid % (16 * CPR);
+    const uint32_t vt_ = (uint32_t)(vtid + kPThreads) % (16 * VCPR);
+    const uint32_t k_r = kt_ / CPR, k_c = kt_ % CPR;
+    const uint32_t v_r = vt_ / VCPR, v_c = vt_ % VCPR;
     const uint64_t k_off = k_r * krow_bytes + (uint64_t)kvh * D * KES + 16u * k_c;
     const uint64_t v_off = v_r * vrow_bytes + (uint64_t)kvh * D * VES + 16u * v_c;
     const uint32_t k_lds = KF::lds_off(k_r, k_c);
@@ -161,7 +203,7 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
         u32x4 k[kPStep], v[kPStep];
     };
     auto block_id = [&](uint32_t b) -> int32_t {
-        const int32_t pb = b < nblk ? a.bt[(uint64_t)s * a.M + b] : -1;
+        const int32_t pb = b < nblk ? bt[(uint64_t)s * a.M + b] : -1;
         return pb;
     };
     // an unmapped block (or one past the range) is read from block 0 and masked
@@ -171,10 +213,10 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
             int32_t pb = block_id(b0 + j);
             pb = (pb >= 0 && (uint32_t)pb < a.num_blocks) ? pb : 0;
             const uint64_t blk = (uint64_t)pb * kBS;
-            if (k_loader)
-                st.k[j] = load_nt((const u32x4*)(kbase + blk * krow_bytes + k_off));
-            if (v_loader)
-                st.v[j] = load_nt((const u32x4*)(vbase + blk * vrow_bytes + v_off));
+            // ordinary (cached) loads: the other query tiles of this (sequence,
+            // kv head), on the same XCD, read the same blocks from its L2
+            st.k[j] = *(const u32x4*)(kbase + blk * krow_bytes + k_off);
+            st.v[j] = *(const u32x4*)(vbase + blk * vrow_bytes + v_off);
         }
     };
     auto store_step = [&](int buf, const Stage& st) {
@@ -197,15 +239,20 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
     auto compute_step = [&](int buf, uint32_t b0) {
         if (!wave_live)
             return;
-        f32x4 sacc[kPStep];
-        bool blk_ok[kPStep];
+        f32x4 sacc[RT][kPStep];
+        bool blk_ok[kPStep], inner[kPStep];
 #pragma unroll
         for (int j = 0; j < kPStep; ++j) {
             const uint32_t b = b0 + j;
+            const int32_t t0 = (int32_t)(b * kBS);
             const int32_t pb = block_id(b);
-            blk_ok[j] = b < nblk && pb >= 0 && (uint32_t)pb < a.num_blocks &&
-                        (int32_t)(b * kBS) < w_end && (int32_t)(b * kBS + kBS) > w_lo;
-            sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            blk_ok[j] = b < nblk && pb >= 0 && (uint32_t)pb < a.num_blocks && t0 < w_end &&
+                        t0 + kBS > w_lo;
+            // a block wholly inside every row's [lo, end) needs no mask
+            inner[j] = blk_ok[j] && t0 >= in_lo && t0 + kBS <= in_end;
+#pragma unroll
+            for (int t = 0; t < RT; ++t)
+                sacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (blk_ok[j]) {
                 const uint8_t* kt = &lds[buf][j][0];
                 u32x4 kop[NL];
@@ -213,68 +260,93 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
                 for (int jj = 0; jj < NL; ++jj)
                     kop[jj] = *(const u32x4*)(kt + lds_r[jj]);
 #pragma unroll
-                for (int i = 0; i < NI; ++i)
-                    sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KF::operand(kop, i), qf[i],
-                                                                      sacc[j], 0, 0, 0);
+                for (int i = 0; i < NI; ++i) {
+                    const bf16x8 kf = KF::operand(kop, i);
+#pragma unroll
+                    for (int t = 0; t < RT; ++t)
+                        sacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][i],
+                                                                             sacc[t][j], 0, 0, 0);
+                }
             }
         }
-        // scores of this lane's row (ln) at keys (b0 + j) * 16 + 4kg + r
-        float sv[kPStep][4];
-        float mx = -INFINITY;
+        // online softmax per row tile; lane's row ln of tile t, keys
+        // (b0 + j) * 16 + 4kg + r
+        bf16x8 a_p[RT][kPStep];
 #pragma unroll
-        for (int j = 0; j < kPStep; ++j)
+        for (int t = 0; t < RT; ++t) {
+            float sv[kPStep][4];
+            float mx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int32_t t = (int32_t)((b0 + j) * kBS) + 4 * kg + r;
-                const bool ok = blk_ok[j] && t >= lo_r && t < end_r;
-                sv[j][r] = ok ? sacc[j][r] * a.qk_scale : -INFINITY;
-                mx = fmaxf(mx, sv[j][r]);
+            for (int j = 0; j < kPStep; ++j) {
+                if (inner[j]) {                          // wave-uniform
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        sv[j][r] = sacc[t][j][r] * a.qk_scale;
+                } else {
+                    const int32_t tk = (int32_t)((b0 + j) * kBS) + 4 * kg;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        // bitwise &: no short-circuit control flow per element
+                        const bool ok = blk_ok[j] & (tk + r >= lo_r[t]) & (tk + r < end_r[t]);
+                        sv[j][r] = ok ? sacc[t][j][r] * a.qk_scale : -INFINITY;
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    mx = fmaxf(mx, sv[j][r]);
             }
-        mx = wave_max_xor16_32(mx);
-        const float m_new = fmaxf(m, mx);
-        const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
-        float p[kPStep][4];
-        float psum = 0.f;
+            mx = wave_max_xor16_32(mx);
+            // m is the row's exponent reference (-inf until a key counts)
+            if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyRescale)) {
+                // rows whose reference stays keep alpha = 1 (also when it is
+                // -inf: -inf - -inf would be NaN); a first reference gives 0
+                const bool move = mx > m[t] + kLazyRescale;
+                const float m_new = move ? mx : m[t];
+                const float alpha = move ? __builtin_amdgcn_exp2f(m[t] - m_new) : 1.f;
+                l[t] *= alpha;
+                m[t] = m_new;
 #pragma unroll
-        for (int j = 0; j < kPStep; ++j) {
+                for (int r = 0; r < 4; ++r) {
+                    const float ar = __shfl(alpha, 4 * kg + r, 64);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                p[j][r] = __builtin_amdgcn_exp2f(sv[j][r] - m_ref);
-            psum += (p[j][0] + p[j][1]) + (p[j][2] + p[j][3]);
-        }
-        l = l * alpha + psum;
-        m = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float ar = __shfl(alpha, 4 * kg + r, 64);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    o[nt][r] *= ar;
+                    for (int nt = 0; nt < NT; ++nt)
+                        o[t][nt][r] *= ar;
+                }
             }
+            const float m_ref = m[t] == -INFINITY ? 0.f : m[t];
+            float psum = 0.f;
+#pragma unroll
+            for (int j = 0; j < kPStep; ++j) {
+                float p[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p[r] = __builtin_amdgcn_exp2f(sv[j][r] - m_ref);
+                psum += (p[0] + p[1]) + (p[2] + p[3]);
+                // A operand: k = 8kg + 0..3 -> P_hi of keys 4kg + 0..3,
+                // k = 8kg + 4..7 -> P_lo
+                uint32_t ph[2], pl[2];
+#pragma unroll
+                for (int r2 = 0; r2 < 2; ++r2) {
+                    const uint32_t hw = pack_bf16(p[2 * r2], p[2 * r2 + 1]);
+                    ph[r2] = hw;
+                    pl[r2] = pack_bf16(p[2 * r2] - bf16_lo(hw), p[2 * r2 + 1] - bf16_hi(hw));
+                }
+                a_p[t][j] = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], pl[0], pl[1]});
+            }
+            l[t] += psum;
         }
 #pragma unroll
         for (int j = 0; j < kPStep; ++j) {
             if (!blk_ok[j])
                 continue;
-            // A operand: k = 8kg + 0..3 -> P_hi of keys 4kg + 0..3, k = 8kg + 4..7 -> P_lo
-            uint32_t ph[2], pl[2];
-#pragma unroll
-            for (int r2 = 0; r2 < 2; ++r2) {
-                const uint32_t hw = pack_bf16(p[j][2 * r2], p[j][2 * r2 + 1]);
-                ph[r2] = hw;
-                pl[r2] = pack_bf16(p[j][2 * r2] - bf16_lo(hw), p[j][2 * r2 + 1] - bf16_hi(hw));
-            }
-            const bf16x8 a_p = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], pl[0], pl[1]});
             // V rows 4kg + r of the block; keys outside [w_lo, w_end) read as
             // zero (they may lie past the sequence end)
             const uint8_t* vt = &lds[buf][j][0] + v_rd;
             uint32_t vr[4][VW];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int32_t t = (int32_t)((b0 + j) * kBS) + 4 * kg + r;
-                const bool keep = t >= w_lo && t < w_end;
+                const int32_t tk = (int32_t)((b0 + j) * kBS) + 4 * kg + r;
+                const bool keep = inner[j] | ((tk >= w_lo) & (tk < w_end));
                 if constexpr (VW == 4) {
                     const u32x4 x = *(const u32x4*)(vt + r * VROW);
 #pragma unroll
@@ -319,47 +391,59 @@ __global__ __launch_bounds__(kPThreads) void prefill_mfma_kernel(PrefillArgs a)
                     }
                 }
                 const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{b01, b23, b01, b23});
-                o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p, bv, o[nt], 0, 0, 0);
+#pragma unroll
+                for (int t = 0; t < RT; ++t)
+                    o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p[t][j], bv, o[t][nt], 0,
+                                                                       0, 0);
             }
         }
     };
 
     if (nblk > blo) {
         const uint32_t nsteps = (nblk - blo + kPStep - 1) / kPStep;
-        Stage st;
-        load_step(blo, st);
-        store_step(0, st);
+        // step j lives in register stage j % PF until it is written to LDS
+        // buffer j % 2 at the end of step j - 1
+        Stage st[PF];
+#pragma unroll
+        for (int u = 0; u < PF; ++u)
+            load_step(blo + u * kPStep, st[u]);
+        store_step(0, st[0]);
         __syncthreads();
-        for (uint32_t j = 0; j < nsteps; ++j) {
-            const uint32_t b0 = blo + j * kPStep;
-            const bool more = j + 1 < nsteps;
-            if (more)
-                load_step(b0 + kPStep, st);
-            compute_step(j & 1, b0);
-            if (more)
-                store_step((j + 1) & 1, st);
-            __syncthreads();
+        for (uint32_t j0 = 0; j0 < nsteps; j0 += PF) {
+#pragma unroll
+            for (int u = 0; u < PF; ++u) {
+                const uint32_t j = j0 + u;
+                if (j >= nsteps)
+                    break;
+                load_step(blo + (j + PF) * kPStep, st[u]);
+                compute_step(j & 1, blo + j * kPStep);
+                store_step((j + 1) & 1, st[(u + 1) % PF]);
+                __syncthreads();
+            }
         }
     }
 
-    // finished rows: o[nt][r] is row 4kg + r of the wave, column DPL * ln + nt
-    l = wave_sum_xor16_32(l);
+    // finished rows: o[t][nt][r] is row 4kg + r of tile t, column DPL * ln + nt
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const uint32_t wr = 4 * kg + r;                  // row within the wave
-        const float lr = __shfl(l, (int)wr, 64);
-        const float mr = __shfl(m, (int)wr, 64);
-        const uint32_t orow = row0 + 16 * wave + wr;
-        const int32_t oi = (int32_t)(orow / G);
-        if (oi >= qlen || (uint32_t)(q0 + oi) >= a.total_q)
-            continue;
-        const uint32_t h = kvh * G + orow % G;
-        const float inv = norm_factor(mr, lr, a.sinks, h, a.out_scale);
-        float* dst = a.out + ((uint64_t)(q0 + oi) * a.Hq + h) * D + (uint64_t)DPL * ln;
+    for (int t = 0; t < RT; ++t) {
+        const float lt = wave_sum_xor16_32(l[t]);
 #pragma unroll
-        for (int nt = 0; nt < NT; nt += 4)
-            *(f32x4*)(dst + nt) = f32x4{o[nt][r] * inv, o[nt + 1][r] * inv, o[nt + 2][r] * inv,
-                                        o[nt + 3][r] * inv};
+        for (int r = 0; r < 4; ++r) {
+            const uint32_t wr = 4 * kg + r;              // row within the tile
+            const float lr = __shfl(lt, (int)wr, 64);
+            const float mr = __shfl(m[t], (int)wr, 64);
+            const uint32_t orow = wrow0 + 16 * t + wr;
+            const int32_t oi = (int32_t)(orow / G);
+            if (oi >= qlen || (uint32_t)(q0 + oi) >= a.total_q)
+                continue;
+            const uint32_t h = kvh * G + orow % G;
+            const float inv = norm_factor(mr, lr, a.sinks, h, a.out_scale);
+            float* dst = a.out + ((uint64_t)(q0 + oi) * a.Hq + h) * D + (uint64_t)DPL * ln;
+#pragma unroll
+            for (int nt = 0; nt < NT; nt += 4)
+                *(f32x4*)(dst + nt) = f32x4{o[t][nt][r] * inv, o[t][nt + 1][r] * inv,
+                                            o[t][nt + 2][r] * inv, o[t][nt + 3][r] * inv};
+        }
     }
 }
 
@@ -409,6 +493,7 @@ extern "C" int pkv_paged_prefill_attn(const void* q, pkv_dtype q_dtype, uint64_t
         return fail(PKV_ERR_INVALID, "paged_prefill_attn: k_scale must be finite and > 0");
     if (v_dtype == PKV_FP8_E4M3 && !(v_scale > 0.0f && v_scale < INFINITY))
         return fail(PKV_ERR_INVALID, "paged_prefill_attn: v_scale must be finite and > 0");
+    constexpr int kPRows = 16 * kPWaves * kPTiles;
     const uint64_t tiles = ((uint64_t)max_q_len * G + kPRows - 1) / kPRows;
     const uint64_t units = (uint64_t)num_seqs * num_kv_heads;
     const uint64_t groups = (units + kXcds - 1) / kXcds * kXcds * tiles;
@@ -438,10 +523,11 @@ extern "C" int pkv_paged_prefill_attn(const void* q, pkv_dtype q_dtype, uint64_t
     a.window = sliding_window;
     hipStream_t st = (hipStream_t)stream;
     const int kt = k_dtype == PKV_FP8_E4M3, vt = v_dtype == PKV_FP8_E4M3;
-    const dim3 grid((uint32_t)groups), block(kPThreads);
+    const dim3 grid((uint32_t)groups), block(64 * kPWaves);
 #define PKV_PREFILL(KT, VT, D)                                                                  \
     if (kt == KT && vt == VT && head_dim_qk == D)                                              \
-        hipLaunchKernelGGL((prefill_mfma_kernel<KT, VT, D>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((prefill_mfma_kernel<KT, VT, D, kPWaves, kPStep, kPPre, kPTiles>),  \
+                           grid, block, 0, st, a, block_tables);
     PKV_PREFILL(0, 0, 128) PKV_PREFILL(0, 0, 64) PKV_PREFILL(1, 0, 128) PKV_PREFILL(1, 0, 64)
     PKV_PREFILL(0, 1, 128) PKV_PREFILL(0, 1, 64) PKV_PREFILL(1, 1, 128) PKV_PREFILL(1, 1, 64)
 #undef PKV_PREFILL
