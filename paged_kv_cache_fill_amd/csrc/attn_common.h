@@ -29,6 +29,30 @@ __device__ __forceinline__ float wave_sum_xor16_32(float v)
     return v;
 }
 
+// The same reductions with gfx950's row swaps: v_permlane16_swap (v, v)
+// returns v's xor-16 partners across the two results, v_permlane32_swap the
+// xor-32 ones, so the max of the pair is the exchange-and-reduce step -- no
+// lane-address arithmetic and no LDS round trip.
+__device__ __forceinline__ float row_max_xor16_32(float v)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float row_sum_xor16_32(float v)
+{
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // bytes 2,3 of lo and 2,3 of hi -> one word (two BF16 from two FP32)
 __device__ __forceinline__ uint32_t hi16_pair(uint32_t lo, uint32_t hi)
 {

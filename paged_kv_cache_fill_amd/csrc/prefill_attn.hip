@@ -274,28 +274,30 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
         bf16x8 a_p[RT][kPStep];
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
-            float sv[kPStep][4];
+            // raw scores, masked ones -inf; the scale is applied inside the
+            // exponent's FMA (and to the row max: scale > 0 keeps the order)
+            float sr[kPStep][4];
             float mx = -INFINITY;
 #pragma unroll
             for (int j = 0; j < kPStep; ++j) {
                 if (inner[j]) {                          // wave-uniform
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        sv[j][r] = sacc[t][j][r] * a.qk_scale;
+                        sr[j][r] = sacc[t][j][r];
                 } else {
                     const int32_t tk = (int32_t)((b0 + j) * kBS) + 4 * kg;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         // bitwise &: no short-circuit control flow per element
                         const bool ok = blk_ok[j] & (tk + r >= lo_r[t]) & (tk + r < end_r[t]);
-                        sv[j][r] = ok ? sacc[t][j][r] * a.qk_scale : -INFINITY;
+                        sr[j][r] = ok ? sacc[t][j][r] : -INFINITY;
                     }
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    mx = fmaxf(mx, sv[j][r]);
+                    mx = fmaxf(mx, sr[j][r]);
             }
-            mx = wave_max_xor16_32(mx);
+            mx = row_max_xor16_32(mx) * a.qk_scale;
             // m is the row's exponent reference (-inf until a key counts)
             if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyRescale)) {
                 // rows whose reference stays keep alpha = 1 (also when it is
@@ -313,14 +315,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
                         o[t][nt][r] *= ar;
                 }
             }
-            const float m_ref = m[t] == -INFINITY ? 0.f : m[t];
+            const float neg_m = m[t] == -INFINITY ? 0.f : -m[t];
             float psum = 0.f;
 #pragma unroll
             for (int j = 0; j < kPStep; ++j) {
                 float p[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    p[r] = __builtin_amdgcn_exp2f(sv[j][r] - m_ref);
+                    p[r] = __builtin_amdgcn_exp2f(fmaf(sr[j][r], a.qk_scale, neg_m));
                 psum += (p[0] + p[1]) + (p[2] + p[3]);
                 // A operand: k = 8kg + 0..3 -> P_hi of keys 4kg + 0..3,
                 // k = 8kg + 4..7 -> P_lo
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
     // finished rows: o[t][nt][r] is row 4kg + r of tile t, column DPL * ln + nt
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
-        const float lt = wave_sum_xor16_32(l[t]);
+        const float lt = row_sum_xor16_32(l[t]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint32_t wr = 4 * kg + r;              // row within the tile
