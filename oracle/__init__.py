@@ -23,8 +23,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpkv_oracle.so")
 SRC_PATH = os.path.join(_HERE, "pkv_oracle.c")
 
-DTYPES = {"bf16": 0, "fp8": 1, "f32": 2}
-NP_TYPES = {"bf16": np.uint16, "fp8": np.uint8, "f32": np.float32}
+DTYPES = {"bf16": 0, "fp8": 1, "f32": 2, "tq2": 3, "tq3": 4, "tq4": 5}
+NP_TYPES = {"bf16": np.uint16, "fp8": np.uint8, "f32": np.float32, "tq2": np.uint8,
+            "tq3": np.uint8, "tq4": np.uint8}
 
 
 def build() -> str:
@@ -76,6 +77,12 @@ def lib():
         L.pkvo_paged_prefill.argtypes = [P, I32, U64, P, P, I32, F32, P, I32, F32, P, U32, P, U32,
                                          U32, U32, U32, U32, U32, U32, F32, U32, P, P, I32]
         L.pkvo_paged_prefill.restype = None
+        L.pkvo_tq_lloyd_max.argtypes = [I32, P]
+        L.pkvo_tq_lloyd_max.restype = None
+        L.pkvo_tq_codebook.argtypes = [I32, P]
+        L.pkvo_tq_codebook.restype = None
+        L.pkvo_tq_block_bytes.argtypes = [I32, U32, U32, U32]
+        L.pkvo_tq_block_bytes.restype = U64
         L.pkvo_mla_cache_assemble.argtypes = [P, P, I32, U64, U64, P, U32, U32, U32, U32, U32,
                                               U32, P, P]
         L.pkvo_mla_cache_assemble.restype = None
@@ -195,7 +202,11 @@ def cache_write_v(v, dtype, slots, v_cache, *, num_kv_heads, head_dim_v, block_s
     T = int(slots.size)
     stride = in_token_stride if in_token_stride is not None else num_kv_heads * head_dim_v
     assert v_cache.flags.c_contiguous and v_cache.dtype == NP_TYPES[cache_dtype]
-    num_blocks = v_cache.size // (block_size * num_kv_heads * head_dim_v)
+    if cache_dtype.startswith("tq"):
+        num_blocks = v_cache.size // tq_block_bytes(int(cache_dtype[2]), block_size, num_kv_heads,
+                                                    head_dim_v)
+    else:
+        num_blocks = v_cache.size // (block_size * num_kv_heads * head_dim_v)
     sl = _c(slots, np.int64)
     lib().pkvo_cache_write_v(_ptr(v), DTYPES[dtype], stride, _ptr(sl), T, num_kv_heads,
                              head_dim_v, block_size, num_blocks, _ptr(v_cache),
@@ -280,3 +291,21 @@ def mla_cache_assemble(kv_latent, k_rope, dtype, slots, k_cache, v_cache, *, kv_
                                   kv_lora, rope, cache_dim, block_size, num_blocks,
                                   _ptr(k_cache), _ptr(v_cache))
     return k_cache, v_cache
+
+
+def tq_lloyd_max(bits: int) -> np.ndarray:
+    """The 2^bits Lloyd-Max levels of N(0,1), ascending (FP64)."""
+    out = np.empty(1 << bits, np.float64)
+    lib().pkvo_tq_lloyd_max(bits, _ptr(out))
+    return out
+
+
+def tq_codebook(bits: int) -> np.ndarray:
+    """E4M3 codes of the positive codebook magnitudes, ascending."""
+    out = np.empty(1 << (bits - 1), np.uint8)
+    lib().pkvo_tq_codebook(bits, _ptr(out))
+    return out
+
+
+def tq_block_bytes(bits: int, block_size: int, num_kv_heads: int, head_dim_v: int) -> int:
+    return int(lib().pkvo_tq_block_bytes(bits, block_size, num_kv_heads, head_dim_v))

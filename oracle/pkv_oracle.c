@@ -35,7 +35,7 @@
 
 /* Element types.  Numbered like the product's enum only by convention; the
  * values are restated here, not included. */
-enum { O_BF16 = 0, O_E4M3 = 1, O_F32 = 2 };
+enum { O_BF16 = 0, O_E4M3 = 1, O_F32 = 2, O_TQ2 = 3, O_TQ3 = 4, O_TQ4 = 5 };
 
 /* ------------------------------------------------------------------ */
 /* Number formats                                                      */
@@ -342,6 +342,164 @@ void pkvo_cache_write_k(const void* k_in, int in_dtype, uint64_t in_token_stride
 }
 
 /* ------------------------------------------------------------------ */
+/* TurboQuant-style V (p1 and p2: V as b-bit Lloyd-Max codes plus one  */
+/* FP8 scale per group of 16 elements, with a norm correction)         */
+/* ------------------------------------------------------------------ */
+
+/* The pages name the ingredients (p1 reshape_and_cache_bf16k_turbo{2,3,4}v:
+ * b-bit Lloyd-Max codes, an FP8 per-group scale, a matched-norm
+ * correction; p2: one FP8 scale per 16 elements) and not their details.
+ * Readings taken here:
+ *  - codebook: the 2^b-level Lloyd-Max quantizer of the standard normal
+ *    distribution, its levels rounded to E4M3 (so that a decoded value,
+ *    scale x level, is a product of two E4M3 numbers); symmetric, code =
+ *    sign << (b-1) | magnitude index, magnitudes ascending;
+ *  - a group of 16 consecutive elements of a (token, kv head) row is coded
+ *    as the nearest level of x / rms(x) (ties to the smaller magnitude, -0
+ *    positive), and its scale is E4M3 of |x| / |levels of the codes| (the
+ *    norm correction: the decoded group has the input's L2 norm up to the
+ *    scale's rounding); an all-zero group stores scale 0 and code 0;
+ *  - layout of a cache block of B tokens: the codes of token t, head h at
+ *    byte (t * H + h) * D * b / 8, group q at 2 b bytes each, element i at
+ *    bits [b i, b i + b) of the group's little-endian bytes; then the scale
+ *    section, scale of (t, h, q) at data_bytes + (t * H + h) * D / 16 + q.
+ *  - no rotation and no sparse skip (the decode is exact). */
+
+static double std_normal_pdf(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846); }
+static double std_normal_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
+
+/* Lloyd's algorithm on N(0,1): alternate the nearest-neighbour cells
+ * (midpoints) and the centroid condition (conditional means), to a fixed
+ * point.  levels[2^bits], ascending. */
+void pkvo_tq_lloyd_max(int bits, double* levels)
+{
+    int L = 1 << bits;
+    for (int k = 0; k < L; ++k)
+        levels[k] = -3.0 + 6.0 * (k + 0.5) / L;
+    for (int it = 0; it < 100000; ++it) {
+        double change = 0.0;
+        double prev_t = -INFINITY;
+        double nl[16];
+        for (int k = 0; k < L; ++k) {
+            double t = k + 1 < L ? 0.5 * (levels[k] + levels[k + 1]) : INFINITY;
+            double pa = isinf(prev_t) ? 0.0 : std_normal_pdf(prev_t);
+            double pb = isinf(t) ? 0.0 : std_normal_pdf(t);
+            double mass = std_normal_cdf(t) - std_normal_cdf(prev_t);
+            nl[k] = (pa - pb) / mass;
+            prev_t = t;
+        }
+        for (int k = 0; k < L; ++k) {
+            double d = fabs(nl[k] - levels[k]);
+            if (d > change) change = d;
+            levels[k] = nl[k];
+        }
+        if (change < 1e-15)
+            break;
+    }
+}
+
+/* E4M3 codes of the 2^(bits-1) positive magnitudes, ascending. */
+void pkvo_tq_codebook(int bits, uint8_t* mag_codes)
+{
+    double lv[16];
+    pkvo_tq_lloyd_max(bits, lv);
+    int L = 1 << bits, M = L / 2;
+    for (int j = 0; j < M; ++j)
+        mag_codes[j] = pkvo_e4m3_from_f64(lv[M + j]);
+}
+
+static int tq_bits(int dtype) { return dtype - O_TQ2 + 2; }
+static int is_tq(int dtype) { return dtype >= O_TQ2 && dtype <= O_TQ4; }
+
+/* bytes of one cache block of B tokens x H heads x D elements */
+uint64_t pkvo_tq_block_bytes(int bits, uint32_t B, uint32_t H, uint32_t D)
+{
+    return (uint64_t)B * H * D * bits / 8 + (uint64_t)B * H * D / 16;
+}
+
+/* Decoded element (blk, t, h, d) of a TQ cache. */
+static double tq_elem(const void* cache, int bits, uint32_t B, uint32_t H, uint32_t D,
+                      const double* mags, uint64_t blk, uint32_t t, uint32_t h, uint32_t d)
+{
+    const uint8_t* base = (const uint8_t*)cache + blk * pkvo_tq_block_bytes(bits, B, H, D);
+    uint64_t data_bytes = (uint64_t)B * H * D * bits / 8;
+    const uint8_t* row = base + ((uint64_t)t * H + h) * D * bits / 8;
+    uint32_t q = d / 16, i = d % 16;
+    const uint8_t* grp = row + (uint64_t)q * 2 * bits;
+    uint32_t bit = (uint32_t)bits * i, code = 0;
+    for (int k = 0; k < bits; ++k, ++bit)
+        code |= (uint32_t)((grp[bit / 8] >> (bit % 8)) & 1u) << k;
+    uint8_t sc = base[data_bytes + ((uint64_t)t * H + h) * (D / 16) + q];
+    double mag = mags[code & ((1u << (bits - 1)) - 1)];
+    double v = (code >> (bits - 1)) ? -mag : mag;
+    return pkvo_f64_from_e4m3(sc) * v;
+}
+
+/* Writes V rows of the tokens with valid slots into a TQ cache. */
+void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride,
+                           const int64_t* slots, uint32_t num_tokens, uint32_t num_kv_heads,
+                           uint32_t head_dim_v, uint32_t block_size, uint32_t num_blocks,
+                           void* v_cache, int bits)
+{
+    const uint32_t H = num_kv_heads, D = head_dim_v, B = block_size;
+    const int M = 1 << (bits - 1);
+    uint8_t mc[8];
+    double mags[8], thr[8];
+    pkvo_tq_codebook(bits, mc);
+    for (int j = 0; j < M; ++j)
+        mags[j] = pkvo_f64_from_e4m3(mc[j]);
+    for (int j = 0; j + 1 < M; ++j)
+        thr[j] = 0.5 * (mags[j] + mags[j + 1]);
+    uint64_t blk_bytes = pkvo_tq_block_bytes(bits, B, H, D);
+    uint64_t data_bytes = (uint64_t)B * H * D * bits / 8;
+    uint64_t num_slots = (uint64_t)num_blocks * B;
+    for (uint64_t tok = 0; tok < num_tokens; ++tok) {
+        int64_t slot = slots[tok];
+        if (slot < 0 || (uint64_t)slot >= num_slots)
+            continue;
+        uint64_t blk = (uint64_t)slot / B;
+        uint32_t t = (uint32_t)((uint64_t)slot % B);
+        uint8_t* base = (uint8_t*)v_cache + blk * blk_bytes;
+        for (uint32_t h = 0; h < H; ++h) {
+            uint8_t* row = base + ((uint64_t)t * H + h) * D * bits / 8;
+            for (uint32_t q = 0; q < D / 16; ++q) {
+                double x[16], ss = 0.0;
+                for (int i = 0; i < 16; ++i) {
+                    x[i] = load_elem(v, in_dtype,
+                                     tok * in_token_stride + (uint64_t)h * D + q * 16 + i);
+                    ss += x[i] * x[i];
+                }
+                uint32_t codes[16];
+                uint8_t scale = 0;
+                if (ss > 0.0) {
+                    double r = sqrt(ss / 16.0), cn = 0.0;
+                    for (int i = 0; i < 16; ++i) {
+                        double u = x[i] / r, au = fabs(u);
+                        uint32_t m = 0;
+                        while ((int)m + 1 < M && au > thr[m])
+                            ++m;
+                        codes[i] = (signbit(u) && u != 0.0 ? 1u : 0u) << (bits - 1) | m;
+                        cn += mags[m] * mags[m];
+                    }
+                    scale = pkvo_e4m3_from_f64((double)(float)(sqrt(ss) / sqrt(cn)));
+                } else {
+                    for (int i = 0; i < 16; ++i)
+                        codes[i] = 0;
+                }
+                uint8_t* grp = row + (uint64_t)q * 2 * bits;
+                memset(grp, 0, 2 * (size_t)bits);
+                for (int i = 0; i < 16; ++i)
+                    for (int k = 0; k < bits; ++k) {
+                        uint32_t bit = (uint32_t)bits * i + k;
+                        grp[bit / 8] |= (uint8_t)(((codes[i] >> k) & 1u) << (bit % 8));
+                    }
+                base[data_bytes + ((uint64_t)t * H + h) * (D / 16) + q] = scale;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
 /* (4) V reshape-and-cache                                             */
 /* ------------------------------------------------------------------ */
 
@@ -357,6 +515,11 @@ void pkvo_cache_write_v(const void* v, int in_dtype, uint64_t in_token_stride,
                         uint32_t head_dim_v, uint32_t block_size, uint32_t num_blocks,
                         void* v_cache, int cache_dtype, float v_scale)
 {
+    if (is_tq(cache_dtype)) {
+        pkvo_cache_write_v_tq(v, in_dtype, in_token_stride, slots, num_tokens, num_kv_heads,
+                              head_dim_v, block_size, num_blocks, v_cache, tq_bits(cache_dtype));
+        return;
+    }
     size_t es = elem_size(in_dtype);
     uint64_t row_elems = (uint64_t)num_kv_heads * head_dim_v;
     uint64_t num_slots = (uint64_t)num_blocks * block_size;
@@ -391,6 +554,7 @@ typedef struct {
     uint32_t window; const float* sinks;
     int q_rope; float q_rope_theta; uint32_t q_rope_offset, q_rope_dim;
     const float* gate; float* out;
+    double tq_mags[8];          /* decoded codebook magnitudes of a TQ V cache */
 } decode_ctx;
 
 /* Dequantised cache element: BF16 and FP32 exactly, E4M3 exactly times its
@@ -399,6 +563,17 @@ static double cache_elem(const void* base, int dtype, float scl, uint64_t idx)
 {
     double x = load_elem(base, dtype, idx);
     return dtype == O_E4M3 ? x * (double)scl : x;
+}
+
+static void tq_fill_mags(decode_ctx* c)
+{
+    if (!is_tq(c->v_dtype))
+        return;
+    int bits = tq_bits(c->v_dtype);
+    uint8_t mc[8];
+    pkvo_tq_codebook(bits, mc);
+    for (int j = 0; j < (1 << (bits - 1)); ++j)
+        c->tq_mags[j] = pkvo_f64_from_e4m3(mc[j]);
 }
 
 /* Attention of one query vector q (kv head g, query head h) of sequence s
@@ -450,7 +625,10 @@ static void attend(const decode_ctx* c, uint32_t s, uint32_t g, uint32_t h, int3
         double pt = exp(sc[t] - m);
         l += pt;
         for (uint32_t d = 0; d < c->Dv; ++d)
-            o[d] += pt * cache_elem(c->v_cache, c->v_dtype, c->v_scale, voff + d);
+            o[d] += pt * (is_tq(c->v_dtype)
+                              ? tq_elem(c->v_cache, tq_bits(c->v_dtype), c->B, c->Hkv, c->Dv,
+                                        c->tq_mags, (uint64_t)blk, (uint32_t)t % c->B, g, d)
+                              : cache_elem(c->v_cache, c->v_dtype, c->v_scale, voff + d));
     }
     /* Attention sink (p1 mla_paged_decode_fp8 takes a `sinks` pointer,
      * semantics unstated; our reading): one logit per query head, in the
@@ -523,7 +701,9 @@ void pkvo_paged_decode(const void* q, int q_dtype, uint64_t q_seq_stride,
     decode_ctx c = {q, q_dtype, q_seq_stride, k_cache, k_dtype, k_scale, v_cache, v_dtype,
                     v_scale, block_tables, max_blocks_per_seq, seq_lens, num_blocks,
                     num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, block_size, scale,
-                    sliding_window, sinks, q_rope, q_rope_theta, q_rope_offset, q_rope_dim, gate, out};
+                    sliding_window, sinks, q_rope, q_rope_theta, q_rope_offset, q_rope_dim, gate, out,
+                    {0}};
+    tq_fill_mags(&c);
     parallel_for((uint64_t)num_seqs * num_q_heads, nthreads, decode_range, &c);
 }
 
@@ -584,7 +764,8 @@ void pkvo_paged_prefill(const void* q, int q_dtype, uint64_t q_token_stride, con
     decode_ctx d = {q, q_dtype, 0, k_cache, k_dtype, k_scale, v_cache, v_dtype, v_scale,
                     block_tables, max_blocks_per_seq, seq_lens, num_blocks, num_q_heads,
                     num_kv_heads, head_dim_qk, head_dim_v, block_size, scale, sliding_window,
-                    sinks, 0, 0.0f, 0, 0, NULL, out};
+                    sinks, 0, 0.0f, 0, 0, NULL, out, {0}};
+    tq_fill_mags(&d);
     c.d = d;
     c.q_token_stride = q_token_stride;
     c.cu_q = cu_q;
