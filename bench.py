@@ -15,7 +15,9 @@ FP8 E4M3 K with k_scale = max|stored K| / 448, BF16 V).  Variants of the
 latter: ``decode_fp8kv_64seq_long`` (E4M3 V too, v_scale = max|V| / 448) and
 ``decode_fp8k_64seq_long_window4096_sinks`` (a 4096-token sliding window and
 one sink logit per query head; only the window's tokens are read and
-counted).  ``prefill_bf16_256seq_chunk256`` is chunked prefill on the first
+counted).  ``decode_bf16k_tq3v_256seq`` is the first workload with its V
+cache in the 3-bit TurboQuant-style format (3-bit codes plus one E4M3 scale
+per 16 elements: 0.4375 bytes per element).  ``prefill_bf16_256seq_chunk256`` is chunked prefill on the first
 workload's pool: the last min(256, n) tokens of every sequence are the new
 chunk (slots, K write, V write, then causal prefill attention over the whole
 cache); its metric is the attention's algorithmic TFLOP/s and its roofline
@@ -42,13 +44,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# name -> (workload index, E4M3 V cache, sliding window, sinks)
+# name -> (workload index, V cache format, sliding window, sinks)
 WORKLOADS = {
-    "decode_bf16_256seq": (2, False, 0, False),
-    "decode_fp8k_64seq_long": (3, False, 0, False),
-    "decode_fp8kv_64seq_long": (3, True, 0, False),
-    "decode_fp8k_64seq_long_window4096_sinks": (3, False, 4096, True),
+    "decode_bf16_256seq": (2, "bf16", 0, False),
+    "decode_fp8k_64seq_long": (3, "bf16", 0, False),
+    "decode_fp8kv_64seq_long": (3, "fp8", 0, False),
+    "decode_fp8k_64seq_long_window4096_sinks": (3, "bf16", 4096, True),
+    "decode_bf16k_tq3v_256seq": (2, "tq3", 0, False),
 }
+
+
+def v_elem_bytes(v_kind):
+    """Bytes per V element: 2 (BF16), 1 (E4M3), b/8 + 1/16 (b-bit TQ codes
+    plus one E4M3 scale per 16 elements)."""
+    if v_kind.startswith("tq"):
+        return int(v_kind[2]) / 8 + 1 / 16
+    return 1 if v_kind == "fp8" else 2
 PREFILL_WORKLOADS = {"prefill_bf16_256seq_chunk256": (2, 256)}
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
@@ -81,7 +92,7 @@ def decode_bytes(lens, Hq, Hkv, D, Dv, kb, vb, qb, B=16, window=0, sinks=False):
     blocks that hold them count."""
     n = np.asarray(lens, np.int64)
     lo = np.where((window > 0) & (n > window), n - window, 0)
-    kv = int((n - lo).sum()) * Hkv * (D * kb + Dv * vb)
+    kv = int(round(int((n - lo).sum()) * Hkv * (D * kb + Dv * vb)))
     bt = int(((n + B - 1) // B - lo // B).sum()) * 4
     S = n.size
     return (kv + bt + 4 * S + S * Hq * D * qb + S * Hq * Dv * 4
@@ -95,7 +106,7 @@ def kwrite_bytes(T, Hkv, D, in_b, out_b):
 
 def vwrite_bytes(T, Hkv, Dv, in_b, out_b):
     """V rows read and written, slot (8 B) per token."""
-    return T * (Hkv * Dv * (in_b + out_b) + 8)
+    return int(round(T * (Hkv * Dv * (in_b + out_b) + 8)))
 
 
 def slots_bytes(T, S, B=16):
@@ -159,7 +170,10 @@ def main():
     import pkv_workloads as W
 
     pkv.load()
-    idx, v_fp8, window, use_sinks = WORKLOADS[args.workload]
+    idx, v_kind, window, use_sinks = WORKLOADS[args.workload]
+    v_fp8 = v_kind == "fp8"
+    tq = int(v_kind[2]) if v_kind.startswith("tq") else 0
+    vb = v_elem_bytes(v_kind)
     lay = W.layout(idx)
     cfg = lay.cfg
     S, Hq, Hkv, D, B = lay.num_seqs, cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], 16
@@ -175,8 +189,12 @@ def main():
     Th = int(hist_lens.sum())
     kdt = torch.float8_e4m3fn if fp8 else torch.bfloat16
     k_pool = torch.empty((lay.num_blocks, B, Hkv, D), dtype=kdt, device=dev)
-    vdt = torch.float8_e4m3fn if v_fp8 else torch.bfloat16
-    v_pool = torch.empty((lay.num_blocks, B, Hkv, Dv), dtype=vdt, device=dev)
+    if tq:
+        v_pool = torch.empty((lay.num_blocks, pkv.v_block_bytes(tq + 1, B, Hkv, Dv)),
+                             dtype=torch.uint8, device=dev)
+    else:
+        vdt = torch.float8_e4m3fn if v_fp8 else torch.bfloat16
+        v_pool = torch.empty((lay.num_blocks, B, Hkv, Dv), dtype=vdt, device=dev)
     bt = torch.from_numpy(lay.block_tables).to(dev)
     seq_lens = torch.from_numpy(lay.seq_lens).to(dev)
     w = torch.from_numpy(W.norm_weight(idx).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -216,7 +234,7 @@ def main():
                                 pos_t=pos_h_t, theta=cfg["theta"], k_scale=k_scale)
 
     def populate_v():
-        pkv.cache_write_v(v_hist, slots_h, v_pool, v_scale=v_scale)
+        pkv.cache_write_v(v_hist, slots_h, v_pool, v_scale=v_scale, tq_bits=tq)
 
     def time_call(fn, reps):
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -236,7 +254,7 @@ def main():
     del k_hist, v_hist
     torch.cuda.empty_cache()
     kw_bytes = kwrite_bytes(Th, Hkv, D, 2, 1 if fp8 else 2)
-    vw_bytes = vwrite_bytes(Th, Hkv, Dv, 2, 1 if v_fp8 else 2)
+    vw_bytes = vwrite_bytes(Th, Hkv, Dv, 2, vb)
     log(f"population write: K {kw_ms:.3f} ms ({kw_bytes / kw_ms / 1e6:.0f} GB/s), "
         f"V {vw_ms:.3f} ms ({vw_bytes / vw_ms / 1e6:.0f} GB/s)")
 
@@ -259,12 +277,12 @@ def main():
         pkv.fill_slots(slots_d, bt, start_d_t, cu_d_t, B)
         pkv.cache_write_k_fused(k_new, slots_d, k_pool, norm_weight=w, eps=cfg["eps"],
                                 pos_t=pos_d_t, theta=cfg["theta"], k_scale=k_scale)
-        pkv.cache_write_v(v_new, slots_d, v_pool, v_scale=v_scale)
+        pkv.cache_write_v(v_new, slots_d, v_pool, v_scale=v_scale, tq_bits=tq)
 
     def step_attn():
         pkv.paged_decode_attn(q, k_pool, v_pool, bt, seq_lens, scale=scale, k_scale=k_scale,
                               v_scale=v_scale, sliding_window=window, sinks=sinks, out=out,
-                              split_tokens=args.split_tokens, workspace=ws)
+                              split_tokens=args.split_tokens, workspace=ws, v_tq_bits=tq)
 
     def step():
         step_writes()
@@ -285,10 +303,10 @@ def main():
     write_ms = float(np.mean(time_call(step_writes, args.steps)))
     log(f"step {ms_per_step:.3f} ms (decode call {attn_ms:.3f} ms, step writes {write_ms * 1e3:.1f} us)")
 
-    dec_b = decode_bytes(lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 1 if v_fp8 else 2, 2,
+    dec_b = decode_bytes(lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, vb, 2,
                          window=window, sinks=use_sinks)
     step_b = (dec_b + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2)
-              + vwrite_bytes(S, Hkv, Dv, 2, 1 if v_fp8 else 2) + slots_bytes(S, S))
+              + vwrite_bytes(S, Hkv, Dv, 2, vb) + slots_bytes(S, S))
     value = step_b / (ms_per_step * 1e-3) / 1e9
     achieved = dec_b / (attn_ms * 1e-3) / 1e9
     traffic = traffic_from_profile(kernel_source_hash(), args.workload)
@@ -304,7 +322,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": (("fp8_e4m3 K" if fp8 else "bf16 K") + (" / fp8_e4m3 V" if v_fp8 else " / bf16 V")
+        "dtype": (("fp8_e4m3 K" if fp8 else "bf16 K")
+                  + {"fp8": " / fp8_e4m3 V", "bf16": " / bf16 V"}.get(
+                      v_kind, f" / {tq}-bit TQ V (e4m3 scale per 16)")
                   + ", f32 accumulate"),
         "data": "synthetic (seeded)",
         "config": {"workload": args.workload, "num_seqs": S, "seq_len_range": [cfg["len_lo"], cfg["len_hi"]],
@@ -329,7 +349,7 @@ def main():
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(idx, lay, k_scale, v_fp8, v_scale, window,
+        result["cpu_baseline"] = cpu_baseline(idx, lay, k_scale, v_kind, v_scale, window,
                                               None if sinks is None else sinks.cpu().numpy())
     print(json.dumps(result), flush=True)
 
@@ -464,7 +484,7 @@ def run_prefill(args):
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(idx, lay, k_scale, v_fp8=False, v_scale=1.0, window=0, sinks=None):
+def cpu_baseline(idx, lay, k_scale, v_kind="bf16", v_scale=1.0, window=0, sinks=None):
     """The oracle, as it stands, timed on this host on the decode step of the
     whole workload (slots, K write, V write, attention over every sequence).
     Pools are drawn on the device by the seeded generator and copied to the
@@ -489,7 +509,22 @@ def cpu_baseline(idx, lay, k_scale, v_fp8=False, v_scale=1.0, window=0, sinks=No
         kp = W.device_normal(idx, W.S_POOLK, shape, torch.bfloat16, "cuda").view(torch.int16) \
             .cpu().numpy().view(np.uint16)
     vshape = (lay.num_blocks, 16, Hkv, Dv)
-    if v_fp8:
+    v_fp8 = v_kind == "fp8"
+    vb = v_elem_bytes(v_kind)
+    if v_kind.startswith("tq"):
+        # random code bytes and random finite E4M3 scales
+        bits = int(v_kind[2])
+        data = 16 * Hkv * Dv * bits // 8
+        blk = data + 16 * Hkv * Dv // 16
+        g = torch.Generator(device="cuda")
+        g.manual_seed(W.seed_of(idx) * 1000 + W.S_POOLV)
+        codes = torch.randint(0, 256, (lay.num_blocks, data), dtype=torch.uint8, device="cuda",
+                              generator=g)
+        scales = torch.randint(0, 0x50, (lay.num_blocks, blk - data), dtype=torch.uint8,
+                               device="cuda", generator=g)
+        vp = torch.cat([codes, scales], dim=1).cpu().numpy()
+        del codes, scales
+    elif v_fp8:
         g = torch.Generator(device="cuda")
         g.manual_seed(W.seed_of(idx) * 1000 + W.S_POOLV)
         mag = torch.randint(0, 0x50, vshape, dtype=torch.uint8, device="cuda", generator=g)
@@ -499,7 +534,7 @@ def cpu_baseline(idx, lay, k_scale, v_fp8=False, v_scale=1.0, window=0, sinks=No
     else:
         vp = W.device_normal(idx, W.S_POOLV, vshape, torch.bfloat16, "cuda") \
             .view(torch.int16).cpu().numpy().view(np.uint16)
-    vdt = "fp8" if v_fp8 else "bf16"
+    vdt = v_kind
     torch.cuda.empty_cache()
     S = lay.num_seqs
     q = W.queries(idx, S)
@@ -519,10 +554,10 @@ def cpu_baseline(idx, lay, k_scale, v_fp8=False, v_scale=1.0, window=0, sinks=No
                         head_dim_v=Dv, block_size=16, scale=D ** -0.5, k_scale=k_scale,
                         v_scale=v_scale, sliding_window=window, sinks=sinks, nthreads=cores)
     dt = time.perf_counter() - t0
-    b = (decode_bytes(lay.seq_lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, 1 if v_fp8 else 2, 2,
+    b = (decode_bytes(lay.seq_lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, vb, 2,
                       window=window, sinks=sinks is not None)
          + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2)
-         + vwrite_bytes(S, Hkv, Dv, 2, 1 if v_fp8 else 2) + slots_bytes(S, S))
+         + vwrite_bytes(S, Hkv, Dv, 2, vb) + slots_bytes(S, S))
     return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"the whole decode step of all {S} sequences "
                       f"({int(lay.seq_lens.astype(np.int64).sum())} tokens), {dt:.2f} s"}

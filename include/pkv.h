@@ -58,11 +58,35 @@ extern "C" {
 #endif
 
 /* Element types.  PKV_FP8_E4M3 is OCP FP8 E4M3FN (bias 7, no infinities,
- * largest finite 448), the "FP8 E4M3" of [p1] and [p2]. */
+ * largest finite 448), the "FP8 E4M3" of [p1] and [p2].
+ * PKV_TQ2 / TQ3 / TQ4 are V cache formats only: the TurboQuant-style V of
+ * [p1] reshape_and_cache_bf16k_turbo{2,3,4}v and [p2] (b-bit Lloyd-Max codes
+ * plus one FP8 scale per 16 elements, with a norm correction).  The pages
+ * give no more; the format taken here:
+ *   - codebook: the 2^b Lloyd-Max levels of the standard normal
+ *     distribution, rounded to E4M3; code = sign << (b-1) | magnitude index
+ *     (pkv_tq_codebook returns the magnitudes);
+ *   - each group of 16 consecutive elements of a (token, kv head) V row is
+ *     coded as the nearest level of x / rms(group) (ties to the smaller
+ *     magnitude); its scale is the saturating E4M3 of |x| / |levels|, so the
+ *     decoded group (scale x level) keeps the input's L2 norm up to the
+ *     scale's rounding; an all-zero group has scale 0.  These decisions are
+ *     taken in FP32 in this order: ss = fused multiply-add sum of x_i^2,
+ *     i = 0..15; u_i = x_i * (1 / sqrt(ss * 1/16)); magnitude index = the
+ *     number of midpoints between adjacent magnitudes that |u_i| exceeds;
+ *     sign = u_i < 0; scale = E4M3(sqrt(ss) / sqrt(sum of chosen m^2));
+ *   - a cache block of B tokens is B * H * D * b / 8 bytes of codes -- token
+ *     t, head h at byte (t * H + h) * D * b / 8, group q at 2 b bytes each,
+ *     element i at bits [b i, b i + b) of the group's little-endian bytes --
+ *     followed by B * H * D / 16 scale bytes, (t, h, q) at offset
+ *     (t * H + h) * D / 16 + q (pkv_v_block_bytes gives the block size). */
 typedef enum pkv_dtype {
     PKV_BF16 = 0,
     PKV_FP8_E4M3 = 1,
-    PKV_FP32 = 2
+    PKV_FP32 = 2,
+    PKV_TQ2 = 3,
+    PKV_TQ3 = 4,
+    PKV_TQ4 = 5
 } pkv_dtype;
 
 enum {
@@ -78,6 +102,17 @@ const char* pkv_last_error(void);
 
 /* Library version as "major.minor.patch". */
 const char* pkv_version(void);
+
+/* Bytes of one V cache block of block_size tokens x num_kv_heads x
+ * head_dim_v elements in v_dtype (the pool is num_blocks such blocks); 0 for
+ * an unknown dtype or a TQ layout whose head_dim_v is not a multiple of 16. */
+size_t pkv_v_block_bytes(pkv_dtype v_dtype, uint32_t block_size, uint32_t num_kv_heads,
+                         uint32_t head_dim_v);
+
+/* The E4M3 codes of a TQ format's 2^(b-1) positive codebook magnitudes,
+ * ascending, into host memory mag_codes.  0, or PKV_ERR_INVALID for a
+ * non-TQ dtype or NULL. */
+int pkv_tq_codebook(pkv_dtype v_dtype, uint8_t* mag_codes);
 
 /*
  * pkv_fill_slots -- [p1] fill_slots_from_block_table: fill paged-KV slot
@@ -159,6 +194,8 @@ int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype, uint64_t in_to
  * For each token t with 0 <= slot_mapping[t] < num_blocks * block_size and
  * every kv head h:
  *   cache_dtype == in_dtype:  v_cache[slot, h, :] = v[t, h, :], byte for byte
+ *   cache_dtype == TQ2/3/4:   the row's 16-element groups coded as stated
+ *                             with pkv_dtype (finite inputs; v_scale unused)
  *   cache_dtype == FP8_E4M3:  v_cache[slot, h, d] = saturating E4M3 of
  *                             fl32(v[t, h, d] / v_scale) (correctly rounded
  *                             FP32 division, then round-to-nearest-even;
@@ -170,8 +207,11 @@ int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype, uint64_t in_to
  *   v_cache       out [num_blocks, block_size, num_kv_heads, head_dim_v] of cache_dtype
  *   v_scale           E4M3 cache only: per-tensor scale, finite and > 0
  * Supported: (in_dtype, cache_dtype) (BF16, BF16), (FP32, FP32),
- *   (BF16, FP8_E4M3), (FP32, FP8_E4M3); the cache row num_kv_heads *
- *   head_dim_v elements a multiple of 16 bytes in both dtypes.
+ *   (BF16, FP8_E4M3), (FP32, FP8_E4M3), (BF16 or FP32, TQ2/3/4); the cache
+ *   row num_kv_heads * head_dim_v elements a multiple of 16 bytes in both
+ *   dtypes; for TQ, head_dim_v a multiple of 16 and block_size *
+ *   num_kv_heads * head_dim_v / 16 a multiple of 8 (v_cache: num_blocks *
+ *   pkv_v_block_bytes bytes, 16-byte aligned).
  */
 int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_token_stride,
                       const int64_t* slot_mapping, uint32_t num_tokens, uint32_t num_kv_heads,
@@ -237,8 +277,10 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *                 does not depend on it beyond FP32 rounding.
  *   workspace     device scratch of at least
  *                 pkv_decode_workspace_bytes(...) bytes (may be NULL if that is 0)
- * Supported: (q, K, V) dtypes (BF16, BF16 or FP8_E4M3, BF16 or FP8_E4M3),
- *   (FP32, FP32, FP32); num_q_heads % num_kv_heads == 0; block_size 16;
+ * Supported: (q, K, V) dtypes (BF16, BF16 or FP8_E4M3, BF16 or FP8_E4M3 or
+ *   TQ2/3/4), (FP32, FP32, FP32); TQ V with head_dim 128; the decode of TQ V
+ *   is exact (no weight-threshold skipping); num_q_heads % num_kv_heads == 0;
+ *   block_size 16;
  *   head_dim_qk in {64, 128, 192, 256}, head_dim_v in {64, 128} (BF16/E4M3
  *   caches: head_dim_qk == head_dim_v in {64, 128}, GQA group <= 16; FP32:
  *   group 1, 2, 4 or 8); q_rope (FP32 only) with q_rope_dim even and

@@ -435,7 +435,15 @@ static double tq_elem(const void* cache, int bits, uint32_t B, uint32_t H, uint3
     return pkvo_f64_from_e4m3(sc) * v;
 }
 
-/* Writes V rows of the tokens with valid slots into a TQ cache. */
+/* Writes V rows of the tokens with valid slots into a TQ cache.
+ * The pages fix no precision for the encoder's decisions (the code of an
+ * element, the E4M3 scale byte); they are integers decided by floating point,
+ * so they are taken here in FP32 by this stated sequence:
+ *   ss  = FP32 fused multiply-add sum of x_i^2, i = 0..15 in order;
+ *   inv = 1 / sqrt(ss * (1/16))   (correctly rounded sqrt, then division);
+ *   u_i = x_i * inv;  code_i = sign(u_i) << (b-1) | the count of thresholds
+ *         (midpoints of adjacent magnitudes) that |u_i| exceeds;
+ *   scale = saturating E4M3 of sqrt(ss) / sqrt(sum of chosen magnitude^2). */
 void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride,
                            const int64_t* slots, uint32_t num_tokens, uint32_t num_kv_heads,
                            uint32_t head_dim_v, uint32_t block_size, uint32_t num_blocks,
@@ -463,25 +471,30 @@ void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride
         for (uint32_t h = 0; h < H; ++h) {
             uint8_t* row = base + ((uint64_t)t * H + h) * D * bits / 8;
             for (uint32_t q = 0; q < D / 16; ++q) {
-                double x[16], ss = 0.0;
+                float x[16], ss = 0.0f;
                 for (int i = 0; i < 16; ++i) {
-                    x[i] = load_elem(v, in_dtype,
-                                     tok * in_token_stride + (uint64_t)h * D + q * 16 + i);
-                    ss += x[i] * x[i];
+                    /* BF16 and FP32 inputs are exact in FP32 */
+                    x[i] = (float)load_elem(v, in_dtype,
+                                            tok * in_token_stride + (uint64_t)h * D + q * 16 + i);
+                    ss = fmaf(x[i], x[i], ss);
                 }
                 uint32_t codes[16];
                 uint8_t scale = 0;
-                if (ss > 0.0) {
-                    double r = sqrt(ss / 16.0), cn = 0.0;
+                if (ss > 0.0f) {
+                    float r = sqrtf(ss * 0.0625f);
+                    float inv = 1.0f / r;
+                    double cn = 0.0;      /* exact: at most 16 squares of E4M3 values */
                     for (int i = 0; i < 16; ++i) {
-                        double u = x[i] / r, au = fabs(u);
+                        float u = x[i] * inv;
+                        float au = fabsf(u);
                         uint32_t m = 0;
-                        while ((int)m + 1 < M && au > thr[m])
+                        while ((int)m + 1 < M && (double)au > thr[m])
                             ++m;
-                        codes[i] = (signbit(u) && u != 0.0 ? 1u : 0u) << (bits - 1) | m;
+                        codes[i] = (u < 0.0f ? 1u : 0u) << (bits - 1) | m;
                         cn += mags[m] * mags[m];
                     }
-                    scale = pkvo_e4m3_from_f64((double)(float)(sqrt(ss) / sqrt(cn)));
+                    float ratio = sqrtf(ss) / sqrtf((float)cn);
+                    scale = pkvo_e4m3_from_f64((double)ratio);
                 } else {
                     for (int i = 0; i < 16; ++i)
                         codes[i] = 0;

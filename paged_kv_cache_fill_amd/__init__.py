@@ -19,13 +19,14 @@ import os
 import torch
 
 __all__ = ["fill_slots", "cache_write_k_fused", "cache_write_v", "decode_workspace_bytes",
-           "paged_decode_attn", "paged_prefill_attn", "mla_cache_assemble", "library_path", "load",
-           "PkvError"]
+           "paged_decode_attn", "paged_prefill_attn", "mla_cache_assemble", "v_block_bytes",
+           "tq_codebook", "library_path", "load", "PkvError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 BF16, FP8_E4M3, FP32 = 0, 1, 2
+TQ2, TQ3, TQ4 = 3, 4, 5                  # TurboQuant-style V cache formats (see pkv.h)
 _DT = {torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3, torch.uint8: FP8_E4M3,
        torch.float32: FP32}
 
@@ -48,6 +49,8 @@ _SIGNATURES = {
                                 _U32, _P, _P, _P], _I32),
     "pkv_mla_cache_assemble": ([_P, _P, _I32, _U64, _U64, _P, _U32, _U32, _U32, _U32, _U32, _U32,
                                 _P, _P, _P], _I32),
+    "pkv_v_block_bytes": ([_I32, _U32, _U32, _U32], _SZ),
+    "pkv_tq_codebook": ([_I32, _P], _I32),
 }
 
 
@@ -179,12 +182,46 @@ def cache_write_k_fused(k_in, slot_mapping, k_cache, *, norm_weight=None, eps: f
     return k_cache
 
 
-def cache_write_v(v, slot_mapping, v_cache, v_scale: float = 1.0):
+def v_block_bytes(v_dtype: int, block_size: int, num_kv_heads: int, head_dim_v: int) -> int:
+    """Bytes of one V cache block in the given format (pkv_v_block_bytes)."""
+    return int(load().pkv_v_block_bytes(v_dtype, block_size, num_kv_heads, head_dim_v))
+
+
+def tq_codebook(tq_bits: int):
+    """E4M3 codes of a TQ format's positive codebook magnitudes (pkv_tq_codebook)."""
+    out = (ctypes.c_uint8 * 8)()
+    _check(load().pkv_tq_codebook(tq_bits + 1, out))
+    return bytes(out[:1 << (tq_bits - 1)])
+
+
+def _tq_pool(v_cache, tq_bits, block_size, H, D):
+    if v_cache.dtype != torch.uint8 or v_cache.dim() != 2 or not v_cache.is_contiguous():
+        raise ValueError("a TQ V pool is a contiguous uint8 [num_blocks, block_bytes] tensor")
+    if v_cache.shape[1] != v_block_bytes(tq_bits + 1, block_size, H, D):
+        raise ValueError("TQ V pool rows must be v_block_bytes(...) long")
+    return v_cache.shape[0]
+
+
+def cache_write_v(v, slot_mapping, v_cache, v_scale: float = 1.0, tq_bits: int = 0,
+                  block_size: int = 16):
     """V rows into the V pool at their slots (pkv_cache_write_v): a byte copy
-    when the pool has v's dtype, E4M3 of v / v_scale for an FP8 pool."""
+    when the pool has v's dtype, E4M3 of v / v_scale for an FP8 pool, or the
+    TurboQuant-style b-bit format when ``tq_bits`` is 2, 3 or 4 (v_cache a
+    uint8 [num_blocks, block_bytes] tensor)."""
     _dev(v, slot_mapping, v_cache)
-    nb, B, H, D = _pool(v_cache, "v_cache")
     T = v.shape[0]
+    if tq_bits:
+        if v.dim() != 3:
+            raise ValueError("v must be [T, Hkv, Dv]")
+        H, D = v.shape[1], v.shape[2]
+        nb, B = _tq_pool(v_cache, tq_bits, block_size, H, D), block_size
+        if slot_mapping.numel() != T or slot_mapping.dtype != torch.int64:
+            raise ValueError("slot_mapping must be int64 [T]")
+        stride = _token_stride(v, "v")
+        _check(load().pkv_cache_write_v(_ptr(v), _dtype(v), stride, _ptr(slot_mapping), T, H, D,
+                                        B, nb, _ptr(v_cache), tq_bits + 1, v_scale, _stream()))
+        return v_cache
+    nb, B, H, D = _pool(v_cache, "v_cache")
     if v.shape[1:] != (H, D):
         raise ValueError("v [T, Hkv, Dv] must match the pool's shape")
     if slot_mapping.numel() != T or slot_mapping.dtype != torch.int64:
@@ -206,7 +243,8 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: flo
                       k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0,
                       sinks=None, gate=None, out=None, q_rope: bool = False,
                       q_rope_theta: float = 10000.0, q_rope_offset: int = 0,
-                      q_rope_dim: int = 0, split_tokens: int = 0, workspace=None):
+                      q_rope_dim: int = 0, split_tokens: int = 0, workspace=None,
+                      v_tq_bits: int = 0):
     """One-query-token paged decode attention (pkv_paged_decode_attn).
 
     q [S, Hq, Dqk]; k_cache [nb, B, Hkv, Dqk]; v_cache [nb, B, Hkv, Dv];
@@ -216,9 +254,16 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: flo
     """
     _dev(q, k_cache, v_cache, block_tables, seq_lens, sinks, gate, out, workspace)
     nb, B, Hkv, Dqk = _pool(k_cache, "k_cache")
-    nb2, B2, Hkv2, Dv = _pool(v_cache, "v_cache")
-    if (nb2, B2, Hkv2) != (nb, B, Hkv):
-        raise ValueError("K and V pools must have the same blocks and heads")
+    if v_tq_bits:
+        Dv = Dqk
+        if _tq_pool(v_cache, v_tq_bits, B, Hkv, Dv) != nb:
+            raise ValueError("K and V pools must have the same blocks")
+        v_dt = v_tq_bits + 1
+    else:
+        nb2, B2, Hkv2, Dv = _pool(v_cache, "v_cache")
+        if (nb2, B2, Hkv2) != (nb, B, Hkv):
+            raise ValueError("K and V pools must have the same blocks and heads")
+        v_dt = _dtype(v_cache)
     if q.dim() != 3 or q.shape[2] != Dqk or q.stride(2) != 1 or q.stride(1) != Dqk:
         raise ValueError("q must be [S, Hq, Dqk] with packed heads")
     S, Hq = q.shape[0], q.shape[1]
@@ -245,7 +290,7 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: flo
     q_stride = q.stride(0) if S > 1 else Hq * Dqk
     _check(load().pkv_paged_decode_attn(
         _ptr(q), _dtype(q), q_stride, _ptr(k_cache), _dtype(k_cache), k_scale, _ptr(v_cache),
-        _dtype(v_cache), v_scale, _ptr(block_tables), M, _ptr(seq_lens), S, nb, Hq, Hkv, Dqk, Dv,
+        v_dt, v_scale, _ptr(block_tables), M, _ptr(seq_lens), S, nb, Hq, Hkv, Dqk, Dv,
         B, scale, sliding_window, _ptr(sinks), int(bool(q_rope)), q_rope_theta, q_rope_offset,
         q_rope_dim, _ptr(gate), _ptr(out),
         split_tokens, _ptr(workspace), ws_bytes, _stream()))

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["abi.cpp", "slots.hip", "cache_write_v.hip", "cache_write_k.hip", "decode_attn.hip",
+SOURCES = ["abi.cpp", "tq.cpp", "slots.hip", "cache_write_v.hip", "cache_write_k.hip", "decode_attn.hip",
            "prefill_attn.hip", "mla_cache.hip"]
 
 # Per-source flags: the prefill kernel keeps its MFMA accumulators in VGPRs

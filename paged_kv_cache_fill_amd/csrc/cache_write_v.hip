@@ -2,7 +2,8 @@
 // (page 1, kv_cache.rs, reshape_and_cache_flash_v_only: V rows copied into
 // the paged V pool at slot_mapping, leaving the K side to the fused K write),
 // and its E4M3 form (page 1, reshape_and_cache_fp8: V stored as FP8 with a
-// per-tensor v_scale).
+// per-tensor v_scale), and the TurboQuant-style V forms (page 1,
+// reshape_and_cache_bf16k_turbo{2,3,4}v; the format is stated with pkv_dtype).
 //
 // A token's V row (num_kv_heads * head_dim_v elements) is contiguous in the
 // input and, under the [num_blocks, block_size, Hkv, Dv] layout, contiguous
@@ -113,6 +114,102 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_e4m3_kernel(
     }
 }
 
+// TurboQuant-style V: one thread per (token, kv head, 16-element group).
+// Codebook constants come from the host (tq.cpp).
+struct TqArgs {
+    float mags[8];
+    float thr[7];
+};
+
+template <int IN, int BITS>   // IN: 0 = BF16 input, 2 = FP32 input
+__global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
+    const uint8_t* __restrict__ v, uint64_t in_stride_bytes, const int64_t* __restrict__ slots,
+    uint32_t num_tokens, uint32_t H, uint32_t D, uint32_t B, uint64_t num_slots,
+    uint64_t blk_bytes, uint64_t data_bytes, TqArgs cb, uint8_t* __restrict__ cache)
+{
+    constexpr int M = 1 << (BITS - 1);                  // magnitudes
+    const uint32_t groups = D / 16;
+    const uint64_t gid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (uint64_t)num_tokens * H * groups)
+        return;
+    const uint32_t q = (uint32_t)(gid % groups);
+    const uint64_t th = gid / groups;
+    const uint32_t h = (uint32_t)(th % H);
+    const uint64_t tok = th / H;
+    const int64_t slot = slots[tok];
+    if (slot < 0 || (uint64_t)slot >= num_slots)
+        return;
+
+    float x[16];
+    const uint8_t* src = v + tok * in_stride_bytes + ((uint64_t)h * D + 16u * q) * (IN == 0 ? 2 : 4);
+    if constexpr (IN == 0) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const u32x4 w = load_nt((const u32x4*)src + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[8 * j + 2 * e] = bf16_lo(w[e]);
+                x[8 * j + 2 * e + 1] = bf16_hi(w[e]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const u32x4 w = load_nt((const u32x4*)src + j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                x[4 * j + e] = __uint_as_float(w[e]);
+        }
+    }
+    // The decisions below follow the FP32 sequence stated with pkv_dtype
+    // (in-order fused sum of squares, one reciprocal of the rms, one product
+    // per element), so that codes and scales are reproducible bit for bit.
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        ss = fmaf(x[i], x[i], ss);
+
+    uint64_t codes = 0;
+    uint32_t scale = 0;
+    if (ss > 0.f) {
+        const float inv_r = 1.0f / sqrtf(ss * 0.0625f);
+        float cn = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float u = x[i] * inv_r;
+            const float au = fabsf(u);
+            uint32_t m = 0;
+            float mag = cb.mags[0];
+#pragma unroll
+            for (int j = 0; j + 1 < M; ++j) {
+                const bool up = au > cb.thr[j];        // ties stay on the smaller magnitude
+                m += up;
+                mag = up ? cb.mags[j + 1] : mag;
+            }
+            cn = fmaf(mag, mag, cn);
+            const uint32_t code = (u < 0.f ? (1u << (BITS - 1)) : 0u) | m;
+            codes |= (uint64_t)code << (BITS * i);
+        }
+        // the norm correction: scale so that |scale x levels| = |x|
+        scale = e4m3_sat_x4(sqrtf(ss) / sqrtf(cn), 0.f, 0.f, 0.f) & 0xFFu;
+    }
+    const uint64_t blk = (uint64_t)slot / B;
+    const uint32_t t = (uint32_t)((uint64_t)slot % B);
+    uint8_t* base = cache + blk * blk_bytes;
+    uint8_t* dst = base + ((uint64_t)t * H + h) * D * BITS / 8 + (uint64_t)q * 2 * BITS;
+    if constexpr (BITS == 2) {
+        *(uint32_t*)dst = (uint32_t)codes;
+    } else if constexpr (BITS == 3) {
+        uint16_t* d16 = (uint16_t*)dst;                 // 6 bytes, 2-byte aligned
+        d16[0] = (uint16_t)codes;
+        d16[1] = (uint16_t)(codes >> 16);
+        d16[2] = (uint16_t)(codes >> 32);
+    } else {
+        *(uint64_t*)dst = codes;
+    }
+    base[data_bytes + ((uint64_t)t * H + h) * groups + q] = (uint8_t)scale;
+}
+
 }  // namespace pkv
 
 extern "C" int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_token_stride,
@@ -127,11 +224,53 @@ extern "C" int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_
         return PKV_OK;
     if (!v || !slot_mapping || !v_cache)
         return fail(PKV_ERR_INVALID, "cache_write_v: v, slot_mapping and v_cache must be non-NULL");
-    if (!valid_dtype(in_dtype) || !valid_dtype(cache_dtype))
+    if (!valid_dtype(in_dtype) || !(valid_dtype(cache_dtype) || is_tq(cache_dtype)))
         return fail(PKV_ERR_INVALID, "cache_write_v: bad dtype (%d, %d)", (int)in_dtype,
                     (int)cache_dtype);
     if (in_dtype != PKV_BF16 && in_dtype != PKV_FP32)
         return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: input dtype must be BF16 or FP32");
+    if (is_tq(cache_dtype)) {
+        if (num_kv_heads == 0 || head_dim_v == 0 || block_size == 0 || num_blocks == 0)
+            return fail(PKV_ERR_INVALID, "cache_write_v: zero dimension");
+        if (head_dim_v % 16)
+            return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: TQ needs head_dim_v %% 16 == 0");
+        // keeps every block, and so every group's code store, naturally aligned
+        if (((uint64_t)block_size * num_kv_heads * (head_dim_v / 16)) % 8)
+            return fail(PKV_ERR_UNSUPPORTED,
+                        "cache_write_v: TQ needs block_size * num_kv_heads * head_dim_v / 16 %% 8 == 0");
+        const uint64_t es = dtype_size(in_dtype);
+        if (in_token_stride < (uint64_t)num_kv_heads * head_dim_v)
+            return fail(PKV_ERR_INVALID, "cache_write_v: in_token_stride smaller than a row");
+        if ((in_token_stride * es) % 16 || !aligned16(v) || !aligned16(v_cache))
+            return fail(PKV_ERR_UNSUPPORTED,
+                        "cache_write_v: strides and pointers must be 16-byte aligned");
+        const int bits = tq_bits(cache_dtype);
+        const TqCodebook& book = tq_codebook(bits);
+        TqArgs cb{};
+        for (int j = 0; j < 8; ++j)
+            cb.mags[j] = book.mags[j];
+        for (int j = 0; j < 7; ++j)
+            cb.thr[j] = book.thr[j];
+        const uint64_t groups = (uint64_t)num_tokens * num_kv_heads * (head_dim_v / 16);
+        const uint64_t nblk = (groups + 255) / 256;
+        if (nblk >= (1ull << 31))
+            return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: too many tokens");
+        const uint64_t blk_bytes = tq_block_bytes(bits, block_size, num_kv_heads, head_dim_v);
+        const uint64_t data_bytes = (uint64_t)block_size * num_kv_heads * head_dim_v * bits / 8;
+        hipStream_t st = (hipStream_t)stream;
+#define PKV_TQW(IN, BITS)                                                                      \
+    hipLaunchKernelGGL((cache_write_v_tq_kernel<IN, BITS>), dim3((uint32_t)nblk), dim3(256), 0, st, \
+                       (const uint8_t*)v, in_token_stride * es, slot_mapping, num_tokens,      \
+                       num_kv_heads, head_dim_v, block_size, (uint64_t)num_blocks * block_size, \
+                       blk_bytes, data_bytes, cb, (uint8_t*)v_cache)
+        if (in_dtype == PKV_BF16) {
+            if (bits == 2) PKV_TQW(0, 2); else if (bits == 3) PKV_TQW(0, 3); else PKV_TQW(0, 4);
+        } else {
+            if (bits == 2) PKV_TQW(2, 2); else if (bits == 3) PKV_TQW(2, 3); else PKV_TQW(2, 4);
+        }
+#undef PKV_TQW
+        return check_launch("cache_write_v");
+    }
     if (cache_dtype != in_dtype && cache_dtype != PKV_FP8_E4M3)
         return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: cache dtype must be the input's or E4M3");
     const bool e4m3 = cache_dtype == PKV_FP8_E4M3;

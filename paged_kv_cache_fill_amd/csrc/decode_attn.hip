@@ -63,6 +63,10 @@ struct DecodeArgs {
     float qk_scale;         // scale * log2(e) (* k_scale for E4M3 K)
     float out_scale;        // v_scale for E4M3 V, else 1
     uint32_t window;        // sliding window in tokens, 0 = none
+    // TurboQuant-style V: codebook magnitudes as an E4M3 byte table, block
+    // and code-section bytes
+    uint32_t tq_lut_lo, tq_lut_hi;
+    uint32_t v_blk_bytes, v_data_bytes;
     // query rotation (FP32 path)
     uint32_t q_rope;
     float q_rope_theta;
@@ -143,8 +147,9 @@ __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint3
 
 // ------------------------------------------------------------------ MFMA path
 
-// KT, VT: 0 = BF16, 1 = E4M3 (K and V caches).  D: head dim of q, K and V
-// (64 or 128).  The K operand layout is KFrag (attn_common.h).
+// KT: 0 = BF16, 1 = E4M3 K cache.  VT: 0 = BF16, 1 = E4M3, 2/3/4 = the
+// TurboQuant-style V with that many bits per code (D = 128).  D: head dim
+// of q, K and V (64 or 128).  The K operand layout is KFrag (attn_common.h).
 //
 template <int KT, int VT, int D, int PF>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t kv_groups)
@@ -154,8 +159,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     __shared__ u32x4 s_k[8][16 * KF::CPR];          // one K tile per wave
     constexpr int NT = D / 16;                 // PV N-tiles
     constexpr int DPL = D / 16;                // V dims per lane
-    constexpr uint32_t VES = VT == 0 ? 2 : 1;  // V element bytes
-    constexpr int VW = DPL * VES / 4;          // V words per lane per token (4, 2 or 1)
+    constexpr bool TQ = VT >= 2;               // TurboQuant-style V, VT bits per code
+    static_assert(!TQ || D == 128, "TQ V decode is for head dim 128");
+    constexpr uint32_t VES = VT == 0 ? 2 : 1;  // V element bytes (BF16 / E4M3)
+    // V words per lane per token: 4, 2 or 1; TQ: the code window (2) + scale
+    constexpr int VW = TQ ? 3 : DPL * VES / 4;
     constexpr uint32_t KES = KT == 0 ? 2 : 1;  // K element bytes
 
     const int lane = threadIdx.x & 63;
@@ -238,7 +246,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     // to that block); each lane's byte offsets inside a block are
     // loop-invariant 32-bit values.
     const uint32_t kblk_bytes = (uint32_t)(kBS * krow_stride);
-    const uint32_t vblk_bytes = (uint32_t)(kBS * vrow_stride * VES);
+    const uint32_t vblk_bytes = TQ ? a.v_blk_bytes : (uint32_t)(kBS * vrow_stride * VES);
     const uint32_t koff = (uint32_t)((lane / KF::CPR) * krow_stride + (uint64_t)kvh * D * KES +
                                      16 * (lane % KF::CPR));
     const uint32_t kstep = (uint32_t)(KF::RPL * krow_stride);     // next load: RPL rows down
@@ -252,6 +260,16 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     uint8_t* ktile = (uint8_t*)&s_k[wave][0];
     const uint32_t voff = (uint32_t)((4 * kg) * vrow_stride * VES + ((uint64_t)kvh * D + DPL * ln) * VES);
     const uint32_t vrow_bytes = (uint32_t)(vrow_stride * VES);
+    // TQ: codes of columns 8 ln .. 8 ln + 7 are VT bytes at VT * ln in the
+    // 16 VT-byte row of (token, kv head); an 8-byte window from the dword at
+    // or below holds them.  Their group's scale: byte ln / 2 of the row's 8.
+    [[maybe_unused]] const uint32_t tq_coff =
+        (uint32_t)((4 * kg) * a.Hkv + kvh) * 16u * VT + ((VT * ln) & ~3u);
+    [[maybe_unused]] const uint32_t tq_crow = a.Hkv * 16u * VT;        // next token row
+    [[maybe_unused]] const uint32_t tq_soff =
+        a.v_data_bytes + (uint32_t)((4 * kg) * a.Hkv + kvh) * 8u + ln / 2;
+    [[maybe_unused]] const uint32_t tq_srow = a.Hkv * 8u;
+    [[maybe_unused]] const uint32_t tq_shift = 8u * ((VT * ln) & 3u);
 
     // An unmapped block is read from block 0 instead (always inside the pool):
     // compute_block masks all of its tokens, so what it holds never counts.
@@ -270,7 +288,13 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {                                     // V: t = 4kg + r
-            if constexpr (VW == 4) {
+            if constexpr (TQ) {
+                const u32x2 c2 = __builtin_bit_cast(
+                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr, tq_coff, r * tq_crow, kNT));
+                st.v[r][0] = c2[0];
+                st.v[r][1] = c2[1];
+                st.v[r][2] = __builtin_amdgcn_raw_buffer_load_b8(vr, tq_soff, r * tq_srow, kNT);
+            } else if constexpr (VW == 4) {
                 const u32x4 t4 = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, r * vrow_bytes, kNT));
                 st.v[r][0] = t4[0]; st.v[r][1] = t4[1]; st.v[r][2] = t4[2]; st.v[r][3] = t4[3];
@@ -381,11 +405,38 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
                     vf[r][4 * w + 2] = hi.x;
                     vf[r][4 * w + 3] = hi.y;
                 }
+        } else if constexpr (TQ) {
+            // 8 codes -> one per byte -> magnitude byte lookup (v_perm over the
+            // 8-byte table) with the sign moved to bit 7 = the E4M3 level codes;
+            // decoded value = level x scale, exact in FP32 and in BF16
+            constexpr uint32_t MSK = (1u << VT) - 1;
+            constexpr uint32_t MAGM = ((1u << (VT - 1)) - 1) * 0x01010101u;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const uint64_t c64 = ((uint64_t)st.v[r][1] << 32) | st.v[r][0];
+                const uint32_t c = (uint32_t)(c64 >> tq_shift);
+                uint32_t sel[2] = {0u, 0u};
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    sel[i / 4] |= ((c >> (VT * i)) & MSK) << (8 * (i % 4));
+                const float sc = unpack_e4m3x2(st.v[r][2], false).x;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t e = __builtin_amdgcn_perm(a.tq_lut_hi, a.tq_lut_lo, sel[h] & MAGM) |
+                                       ((sel[h] << (8 - VT)) & 0x80808080u);
+                    const f32x2 lo = unpack_e4m3x2(e, false);
+                    const f32x2 hi = unpack_e4m3x2(e, true);
+                    vf[r][4 * h] = lo.x * sc;
+                    vf[r][4 * h + 1] = lo.y * sc;
+                    vf[r][4 * h + 2] = hi.x * sc;
+                    vf[r][4 * h + 3] = hi.y * sc;
+                }
+            }
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             uint32_t b01, b23;
-            if constexpr (VT == 1) {
+            if constexpr (VT != 0) {
                 b01 = hi16_pair(__float_as_uint(vf[0][nt]), __float_as_uint(vf[1][nt]));
                 b23 = hi16_pair(__float_as_uint(vf[2][nt]), __float_as_uint(vf[3][nt]));
             } else {
@@ -699,7 +750,7 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
         return PKV_OK;
     if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
         return fail(PKV_ERR_INVALID, "paged_decode_attn: q, caches, block_tables, seq_lens and out must be non-NULL");
-    if (!valid_dtype(q_dtype) || !valid_dtype(k_dtype) || !valid_dtype(v_dtype))
+    if (!valid_dtype(q_dtype) || !valid_dtype(k_dtype) || !(valid_dtype(v_dtype) || is_tq(v_dtype)))
         return fail(PKV_ERR_INVALID, "paged_decode_attn: bad dtype");
     if (!num_q_heads || !num_kv_heads || !head_dim_qk || !head_dim_v || !max_blocks_per_seq ||
         !num_blocks || !block_size)
@@ -713,7 +764,9 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     const uint32_t G = num_q_heads / num_kv_heads;
     const bool mfma_path = q_dtype == PKV_BF16 &&
                            (k_dtype == PKV_BF16 || k_dtype == PKV_FP8_E4M3) &&
-                           (v_dtype == PKV_BF16 || v_dtype == PKV_FP8_E4M3);
+                           (v_dtype == PKV_BF16 || v_dtype == PKV_FP8_E4M3 || is_tq(v_dtype));
+    if (is_tq(v_dtype) && (head_dim_qk != 128 || head_dim_v != 128))
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: TQ V needs head_dim 128");
     const bool f32_path = q_dtype == PKV_FP32 && k_dtype == PKV_FP32 && v_dtype == PKV_FP32;
     if (!mfma_path && !f32_path)
         return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: dtypes (q,K,V) must be (BF16, BF16|E4M3, BF16|E4M3) or (FP32,FP32,FP32)");
@@ -774,6 +827,13 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     a.qk_scale = scale * kLog2e * (k_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f);
     a.out_scale = v_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
     a.window = sliding_window;
+    if (is_tq(v_dtype)) {
+        const TqCodebook& book = tq_codebook(tq_bits(v_dtype));
+        a.tq_lut_lo = book.lut_lo;
+        a.tq_lut_hi = book.lut_hi;
+        a.v_blk_bytes = (uint32_t)tq_block_bytes(book.bits, kBS, num_kv_heads, head_dim_v);
+        a.v_data_bytes = (uint32_t)((uint64_t)kBS * num_kv_heads * head_dim_v * book.bits / 8);
+    }
     a.q_rope = (q_rope && q_rope_dim > 0) ? 1u : 0u;
     a.q_rope_theta = q_rope_theta;
     a.q_rope_offset = q_rope_offset;
@@ -787,12 +847,15 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
         const uint32_t kvg = num_kv_heads / kvpb;
         const dim3 grid(num_seqs * kvg, plan.max_splits);
         const dim3 block(64 * kvpb);
-        const int kt = k_dtype == PKV_FP8_E4M3, vt = v_dtype == PKV_FP8_E4M3;
+        const int kt = k_dtype == PKV_FP8_E4M3;
+        const int vt = is_tq(v_dtype) ? tq_bits(v_dtype) : v_dtype == PKV_FP8_E4M3;
 #define PKV_MFMA(KT, VT, D)                                                                     \
     if (kt == KT && vt == VT && head_dim_qk == D)                                              \
         hipLaunchKernelGGL((decode_mfma_kernel<KT, VT, D, kPrefetch>), grid, block, 0, st, a, kvg);
         PKV_MFMA(0, 0, 128) PKV_MFMA(0, 0, 64) PKV_MFMA(1, 0, 128) PKV_MFMA(1, 0, 64)
         PKV_MFMA(0, 1, 128) PKV_MFMA(0, 1, 64) PKV_MFMA(1, 1, 128) PKV_MFMA(1, 1, 64)
+        PKV_MFMA(0, 2, 128) PKV_MFMA(0, 3, 128) PKV_MFMA(0, 4, 128)
+        PKV_MFMA(1, 2, 128) PKV_MFMA(1, 3, 128) PKV_MFMA(1, 4, 128)
 #undef PKV_MFMA
     } else {
         const dim3 grid(num_kv_heads, num_seqs, plan.max_splits);

@@ -31,6 +31,23 @@ inline size_t dtype_size(pkv_dtype t)
 
 inline bool valid_dtype(int t) { return t == PKV_BF16 || t == PKV_FP8_E4M3 || t == PKV_FP32; }
 
+// TurboQuant-style V formats (V caches only)
+inline bool is_tq(int t) { return t == PKV_TQ2 || t == PKV_TQ3 || t == PKV_TQ4; }
+inline int tq_bits(int t) { return t - PKV_TQ2 + 2; }
+
+// A TQ codebook: E4M3 codes and values of the 2^(b-1) positive magnitudes
+// (ascending), the encoder's magnitude thresholds (midpoints; +inf past the
+// last), and the codes packed 4 per word as a byte lookup table.
+struct TqCodebook {
+    int bits, mags_count;
+    uint8_t codes[8];
+    float mags[8];
+    float thr[7];
+    uint32_t lut_lo, lut_hi;
+};
+const TqCodebook& tq_codebook(int bits);
+uint64_t tq_block_bytes(int bits, uint32_t B, uint32_t H, uint32_t D);
+
 inline uint32_t ceil_div(uint64_t a, uint64_t b) { return (uint32_t)((a + b - 1) / b); }
 
 // ---------------------------------------------------------------- device side

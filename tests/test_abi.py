@@ -176,3 +176,43 @@ def test_prefill_and_mla_validation(lib):
     assert mla(ls=500) == -1                      # latent stride below the row
     assert mla(lora=500, ls=500, dim=576) == -2   # 1000 bytes: not a 16-byte multiple
     assert mla(dt=1) == -2                        # E4M3 not an MLA cache dtype here
+
+
+def test_tq_queries_match_the_oracle(lib):
+    import oracle
+    for bits in (2, 3, 4):
+        got = pkv.tq_codebook(bits)
+        assert got == bytes(oracle.tq_codebook(bits))
+        for B, H, D in ((16, 8, 128), (16, 1, 16), (32, 3, 64)):
+            assert pkv.v_block_bytes(bits + 1, B, H, D) == oracle.tq_block_bytes(bits, B, H, D)
+    assert pkv.v_block_bytes(pkv.TQ3, 16, 8, 128) == 16 * 8 * 128 * 3 // 8 + 16 * 8 * 8
+    assert pkv.v_block_bytes(pkv.TQ2, 16, 8, 120) == 0          # head_dim % 16
+    assert pkv.v_block_bytes(pkv.BF16, 16, 8, 128) == 16 * 8 * 128 * 2
+    assert pkv.v_block_bytes(9, 16, 8, 128) == 0
+    buf = (ctypes.c_uint8 * 8)()
+    assert lib.pkv_tq_codebook(pkv.FP8_E4M3, buf) == -1
+    assert lib.pkv_tq_codebook(pkv.TQ2, None) == -1
+
+
+def test_tq_validation(lib):
+    def vw(ind=0, cd=pkv.TQ3, H=8, D=128, B=16, stride=1024):
+        return lib.pkv_cache_write_v(FAKE, ind, stride, FAKE, 10, H, D, B, 4, FAKE, cd, 1.0,
+                                     None)
+    assert vw(D=120, stride=960) == -2            # head_dim % 16
+    assert vw(H=1, D=16, B=3, stride=16) == -2    # blocks would break the stores' alignment
+    assert vw(ind=1) == -2                        # E4M3 input
+    assert vw(stride=512) == -1                   # token stride smaller than a row
+
+    def dec(**kw):
+        a = dict(q=FAKE, qd=0, qs=32 * 128, k=FAKE, kd=0, ks=1.0, v=FAKE, vd=pkv.TQ3, vs=1.0,
+                 bt=FAKE, M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1,
+                 win=0, sinks=None, qr=0, qt=1e4, qo=0, qdim=0, gate=None, out=FAKE, split=0,
+                 ws=FAKE, wsb=1 << 30)
+        a.update(kw)
+        return lib.pkv_paged_decode_attn(*a.values(), None)
+    assert dec(Dqk=64, Dv=64, qs=32 * 64) == -2   # TQ V decode: head dim 128 only
+    assert dec(qd=2, kd=2) == -2                  # FP32 q/K with TQ V
+    pre = lib.pkv_paged_prefill_attn(FAKE, 0, 32 * 128, FAKE, 8, 64, FAKE, 0, 1.0, FAKE, pkv.TQ3,
+                                     1.0, FAKE, 4, FAKE, 2, 8, 32, 8, 128, 128, 16, 0.1, 0, None,
+                                     FAKE, None)
+    assert pre in (-1, -2) and _err(lib) != ""    # prefill reads BF16 / E4M3 V only

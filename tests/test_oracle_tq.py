@@ -105,10 +105,12 @@ def test_group_codes_are_nearest_levels_and_norm_is_corrected(bits):
                 # by the scale and find each element's level
                 scale = np.linalg.norm(d) / np.linalg.norm(levels[np.argmin(dist, axis=1)])
                 chosen = np.argmin(np.abs(d[:, None] / scale - levels[None, :]), axis=1)
-                # each element's level is a nearest level of x / rms (ties allowed)
-                assert np.allclose(dist[np.arange(16), chosen], dist.min(axis=1), atol=1e-9)
+                # each element's level is a nearest level of x / rms (ties, and
+                # the FP32 rounding of x / rms in the decision, allowed)
+                assert np.allclose(dist[np.arange(16), chosen], dist.min(axis=1),
+                                   atol=1e-6 * np.abs(u).max())
                 assert np.sign(d[g != 0]).tolist() == np.sign(g[g != 0]).tolist()
-                assert abs(np.linalg.norm(d) / np.linalg.norm(g) - 1) <= 2.0 ** -4 + 1e-12
+                assert abs(np.linalg.norm(d) / np.linalg.norm(g) - 1) <= 2.0 ** -4 + 1e-6
 
 
 def test_power_of_two_scaling_only_scales():
@@ -174,3 +176,15 @@ def test_attention_over_tq_cache_equals_attention_over_decoded_rows():
                             head_dim_qk=D, head_dim_v=D, block_size=16, scale=D ** -0.5,
                             k_scale=0.5)
     assert np.abs(a - b).max() <= 1e-6 * np.abs(b).max()
+
+
+def test_hand_worked_ties_example():
+    rows = {}
+    for line in open(os.path.join(GOLDEN, "tq3_ties_example.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            rows[k] = v
+    x = np.array([float(a) for a in rows["x"]], np.float32).reshape(1, 1, 16)
+    enc = _encode(x, 3)
+    assert bytes(enc[:6]) == bytes(int(b, 16) for b in rows["bytes"])
+    assert enc[16 * 6] == int(rows["scale"][0], 16)
