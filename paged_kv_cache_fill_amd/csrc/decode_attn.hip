@@ -63,9 +63,10 @@ struct DecodeArgs {
     float qk_scale;         // scale * log2(e) (* k_scale for E4M3 K)
     float out_scale;        // v_scale for E4M3 V, else 1
     uint32_t window;        // sliding window in tokens, 0 = none
-    // TurboQuant-style V: codebook magnitudes as an E4M3 byte table, block
-    // and code-section bytes
-    uint32_t tq_lut_lo, tq_lut_hi;
+    // TurboQuant-style V: the FP16 level table as byte-lookup words (low
+    // bytes of entries 0-3, 4-7, high bytes of 0-3, 4-7), block and
+    // code-section bytes
+    uint32_t tq_f16[4];
     uint32_t v_blk_bytes, v_data_bytes;
     // query rotation (FP32 path)
     uint32_t q_rope;
@@ -145,6 +146,86 @@ __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint3
     }
 }
 
+// ------------------------------------------------------------------ TQ V
+
+// The PV product of one 16-token block over a TurboQuant-style V cache (head
+// dim 128).  Lane (ln, kg) holds the weights p[r] of tokens t = 4kg + r (A
+// operand, row g = ln) and the raw V words of those tokens for its columns
+// 8 ln .. 8 ln + 7 (one half of a 16-element group): the codes and the
+// group's E4M3 scale byte.
+//
+// Decoding works on two tokens at a time, so that every lookup already
+// yields the (t, t + 1) pairs that the FP16 B operand packs per column:
+//  - the two tokens' codes of four columns are placed one per nibble,
+//    [t: c0 c1 | t: c2 c3 | t+1: c0 c1 | t+1: c2 c3] (3-bit codes are spread
+//    from their packed form by two shift-and-insert steps; 2- and 4-bit codes
+//    need only byte moves);
+//  - even and odd nibbles become byte selectors into the 8-entry FP16 level
+//    table (low and high bytes looked up separately with v_perm; a 4-bit
+//    code's sign bit goes straight to the FP16 sign);
+//  - a v_perm pairs the low and high bytes into the two tokens' FP16 values
+//    of one column, and one packed FP16 multiply applies the two tokens'
+//    scales.  level x scale has at most 8 significant bits and lies in
+//    [2^-12, 1232], so the FP16 product is exact.
+// The weights are FP16 (scaled by 2^15 by the caller); the products
+// accumulate in FP32.
+template <int VT, int VW>
+__device__ __forceinline__ void tq_pv(const DecodeArgs& a, const float (&p)[4],
+                                      const uint32_t (&v)[4][VW], uint32_t shift, f32x4 (&o)[8])
+{
+    constexpr uint32_t MSK = VT == 2 ? 0x03030303u : 0x07070707u;
+    const f16x2 pa = __builtin_bit_cast(f16x2, pack_f16(p[0], p[1]));
+    const f16x2 pb = __builtin_bit_cast(f16x2, pack_f16(p[2], p[3]));
+    const f16x4 ap = f16x4{pa[0], pa[1], pb[0], pb[1]};
+    uint32_t vb[2][8];                         // [token pair][column]: FP16 (t, t + 1)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+        const int r0 = 2 * pr, r1 = 2 * pr + 1;
+        const f32x2 sc = unpack_e4m3x2(v[r0][VW - 1] | (v[r1][VW - 1] << 8), false);
+        const f16x2 scale = __builtin_bit_cast(f16x2, pack_f16(sc.x, sc.y));
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {       // columns 4 hh .. 4 hh + 3
+            uint32_t nw;
+            if constexpr (VT == 4) {
+                nw = __builtin_amdgcn_perm(v[r1][0], v[r0][0], hh ? 0x07060302u : 0x05040100u);
+            } else if constexpr (VT == 2) {
+                const uint32_t x = __builtin_amdgcn_perm(v[r1][0], v[r0][0],
+                                                         hh ? 0x0C050C01u : 0x0C040C00u);
+                const uint32_t y = bit_insert(0xFF00FF00u, x << 4, x);
+                nw = bit_insert(0xF0F0F0F0u, y << 2, y);
+            } else {
+                // the lane's 24 code bits start `shift` (0, 8, 16 or 24) bits
+                // into the 8-byte window
+                const uint32_t c0 = __builtin_amdgcn_alignbit(v[r0][1], v[r0][0], shift);
+                const uint32_t c1 = __builtin_amdgcn_alignbit(v[r1][1], v[r1][0], shift);
+                const uint32_t x = __builtin_amdgcn_perm(hh ? c1 >> 12 : c1, hh ? c0 >> 12 : c0,
+                                                         0x05040100u);
+                const uint32_t y = bit_insert(0xFF00FF00u, x << 2, x);
+                nw = bit_insert(0xF0F0F0F0u, y << 1, y);
+            }
+#pragma unroll
+            for (int odd = 0; odd < 2; ++odd) {
+                const uint32_t sel = (odd ? nw >> 4 : nw) & MSK;
+                const uint32_t lo = __builtin_amdgcn_perm(a.tq_f16[1], a.tq_f16[0], sel);
+                uint32_t hi = __builtin_amdgcn_perm(a.tq_f16[3], a.tq_f16[2], sel);
+                if constexpr (VT == 4)
+                    hi |= (odd ? nw : nw << 4) & 0x80808080u;
+                // selector bytes: [t: c_a, t: c_b, t+1: c_a, t+1: c_b]
+                const int ca = 4 * hh + odd, cb = 4 * hh + 2 + odd;
+                vb[pr][ca] = __builtin_bit_cast(
+                    uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x06020400u)) * scale);
+                vb[pr][cb] = __builtin_bit_cast(
+                    uint32_t, __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(hi, lo, 0x07030501u)) * scale);
+            }
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+        const f16x4 bv = __builtin_bit_cast(f16x4, u32x2{vb[0][nt], vb[1][nt]});
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap, bv, o[nt], 0, 0, 0);
+    }
+}
+
 // ------------------------------------------------------------------ MFMA path
 
 // KT: 0 = BF16, 1 = E4M3 K cache.  VT: 0 = BF16, 1 = E4M3, 2/3/4 = the
@@ -162,8 +243,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     constexpr bool TQ = VT >= 2;               // TurboQuant-style V, VT bits per code
     static_assert(!TQ || D == 128, "TQ V decode is for head dim 128");
     constexpr uint32_t VES = VT == 0 ? 2 : 1;  // V element bytes (BF16 / E4M3)
-    // V words per lane per token: 4, 2 or 1; TQ: the code window (2) + scale
-    constexpr int VW = TQ ? 3 : DPL * VES / 4;
+    // V words per lane per token: 4, 2 or 1; TQ: the codes (an 8-byte window
+    // for 3-bit codes, else one word) + the scale byte
+    constexpr int VW = TQ ? (VT == 3 ? 3 : 2) : DPL * VES / 4;
     constexpr uint32_t KES = KT == 0 ? 2 : 1;  // K element bytes
 
     const int lane = threadIdx.x & 63;
@@ -261,15 +343,16 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     const uint32_t voff = (uint32_t)((4 * kg) * vrow_stride * VES + ((uint64_t)kvh * D + DPL * ln) * VES);
     const uint32_t vrow_bytes = (uint32_t)(vrow_stride * VES);
     // TQ: codes of columns 8 ln .. 8 ln + 7 are VT bytes at VT * ln in the
-    // 16 VT-byte row of (token, kv head); an 8-byte window from the dword at
-    // or below holds them.  Their group's scale: byte ln / 2 of the row's 8.
+    // 16 VT-byte row of (token, kv head): a 16-bit or 32-bit load for 2- and
+    // 4-bit codes, an 8-byte window from the dword at or below for 3-bit
+    // codes.  Their group's scale: byte ln / 2 of the row's 8.
     [[maybe_unused]] const uint32_t tq_coff =
-        (uint32_t)((4 * kg) * a.Hkv + kvh) * 16u * VT + ((VT * ln) & ~3u);
+        (uint32_t)((4 * kg) * a.Hkv + kvh) * 16u * VT + (VT == 3 ? ((3u * ln) & ~3u) : VT * ln);
     [[maybe_unused]] const uint32_t tq_crow = a.Hkv * 16u * VT;        // next token row
     [[maybe_unused]] const uint32_t tq_soff =
         a.v_data_bytes + (uint32_t)((4 * kg) * a.Hkv + kvh) * 8u + ln / 2;
     [[maybe_unused]] const uint32_t tq_srow = a.Hkv * 8u;
-    [[maybe_unused]] const uint32_t tq_shift = 8u * ((VT * ln) & 3u);
+    [[maybe_unused]] const uint32_t tq_shift = 8u * ((3u * ln) & 3u);
 
     // An unmapped block is read from block 0 instead (always inside the pool):
     // compute_block masks all of its tokens, so what it holds never counts.
@@ -289,11 +372,17 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
 #pragma unroll
         for (int r = 0; r < 4; ++r) {                                     // V: t = 4kg + r
             if constexpr (TQ) {
-                const u32x2 c2 = __builtin_bit_cast(
-                    u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr, tq_coff, r * tq_crow, kNT));
-                st.v[r][0] = c2[0];
-                st.v[r][1] = c2[1];
-                st.v[r][2] = __builtin_amdgcn_raw_buffer_load_b8(vr, tq_soff, r * tq_srow, kNT);
+                if constexpr (VT == 3) {
+                    const u32x2 c2 = __builtin_bit_cast(
+                        u32x2, __builtin_amdgcn_raw_buffer_load_b64(vr, tq_coff, r * tq_crow, kNT));
+                    st.v[r][0] = c2[0];
+                    st.v[r][1] = c2[1];
+                } else if constexpr (VT == 4) {
+                    st.v[r][0] = __builtin_amdgcn_raw_buffer_load_b32(vr, tq_coff, r * tq_crow, kNT);
+                } else {
+                    st.v[r][0] = __builtin_amdgcn_raw_buffer_load_b16(vr, tq_coff, r * tq_crow, kNT);
+                }
+                st.v[r][VW - 1] = __builtin_amdgcn_raw_buffer_load_b8(vr, tq_soff, r * tq_srow, kNT);
             } else if constexpr (VW == 4) {
                 const u32x4 t4 = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, r * vrow_bytes, kNT));
@@ -351,11 +440,15 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         // masked scores give p = 0, and alpha = 0 leaves the zero state zero
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+        // TQ: the weights go to the PV product as FP16 scaled by 2^15 (kept
+        // clear of FP16 subnormals; p <= 1); the normalisation divides it out
+        constexpr float kPOff = TQ ? 15.f : 0.f;
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            p[r] = __builtin_amdgcn_exp2f(sv[r] - m_ref);
-        l = l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+            p[r] = __builtin_amdgcn_exp2f(sv[r] - (m_ref - kPOff));
+        const float psum = (p[0] + p[1]) + (p[2] + p[3]);
+        l = TQ ? __builtin_fmaf(psum, 1.f / 32768.f, l * alpha) : l * alpha + psum;
         m = m_new;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
             // O rows are g = 4kg + r; their factor lives in lane g
@@ -368,6 +461,20 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
             }
         }
 
+        // masked tokens must not bring NaN/Inf into 0 * V
+        if (ntok < kBS || tlo > 0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (4 * kg + r >= ntok || 4 * kg + r < tlo)
+#pragma unroll
+                    for (int w = 0; w < VW; ++w)
+                        st.v[r][w] = 0u;
+        }
+        if constexpr (TQ) {
+            tq_pv<VT>(a, p, st.v, tq_shift, o);
+            return;
+        }
+
         // P as hi + lo BF16 (A operand: lane holds P[g = ln][t = 4kg + r])
         uint32_t ph[2], pl[2];
 #pragma unroll
@@ -378,16 +485,6 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         }
         const i16x4 a_hi = __builtin_bit_cast(i16x4, u32x2{ph[0], ph[1]});
         const i16x4 a_lo = __builtin_bit_cast(i16x4, u32x2{pl[0], pl[1]});
-
-        // masked tokens must not bring NaN/Inf into 0 * V
-        if (ntok < kBS || tlo > 0) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (4 * kg + r >= ntok || 4 * kg + r < tlo)
-#pragma unroll
-                    for (int w = 0; w < VW; ++w)
-                        st.v[r][w] = 0u;
-        }
 
         // B operand of N-tile nt: element nt of the lane's DPL columns, rows
         // t = 4kg + 0..3; E4M3 codes are widened to FP32 (exact) and their
@@ -405,38 +502,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
                     vf[r][4 * w + 2] = hi.x;
                     vf[r][4 * w + 3] = hi.y;
                 }
-        } else if constexpr (TQ) {
-            // 8 codes -> one per byte -> magnitude byte lookup (v_perm over the
-            // 8-byte table) with the sign moved to bit 7 = the E4M3 level codes;
-            // decoded value = level x scale, exact in FP32 and in BF16
-            constexpr uint32_t MSK = (1u << VT) - 1;
-            constexpr uint32_t MAGM = ((1u << (VT - 1)) - 1) * 0x01010101u;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const uint64_t c64 = ((uint64_t)st.v[r][1] << 32) | st.v[r][0];
-                const uint32_t c = (uint32_t)(c64 >> tq_shift);
-                uint32_t sel[2] = {0u, 0u};
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    sel[i / 4] |= ((c >> (VT * i)) & MSK) << (8 * (i % 4));
-                const float sc = unpack_e4m3x2(st.v[r][2], false).x;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t e = __builtin_amdgcn_perm(a.tq_lut_hi, a.tq_lut_lo, sel[h] & MAGM) |
-                                       ((sel[h] << (8 - VT)) & 0x80808080u);
-                    const f32x2 lo = unpack_e4m3x2(e, false);
-                    const f32x2 hi = unpack_e4m3x2(e, true);
-                    vf[r][4 * h] = lo.x * sc;
-                    vf[r][4 * h + 1] = lo.y * sc;
-                    vf[r][4 * h + 2] = hi.x * sc;
-                    vf[r][4 * h + 3] = hi.y * sc;
-                }
-            }
         }
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             uint32_t b01, b23;
-            if constexpr (VT != 0) {
+            if constexpr (VT == 1) {
                 b01 = hi16_pair(__float_as_uint(vf[0][nt]), __float_as_uint(vf[1][nt]));
                 b23 = hi16_pair(__float_as_uint(vf[2][nt]), __float_as_uint(vf[3][nt]));
             } else {
@@ -829,8 +899,9 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     a.window = sliding_window;
     if (is_tq(v_dtype)) {
         const TqCodebook& book = tq_codebook(tq_bits(v_dtype));
-        a.tq_lut_lo = book.lut_lo;
-        a.tq_lut_hi = book.lut_hi;
+        for (int i = 0; i < 4; ++i)
+            a.tq_f16[i] = book.f16_lut[i];
+        a.out_scale = 1.f / 32768.f;          // the 2^15 on the FP16 weights
         a.v_blk_bytes = (uint32_t)tq_block_bytes(book.bits, kBS, num_kv_heads, head_dim_v);
         a.v_data_bytes = (uint32_t)((uint64_t)kBS * num_kv_heads * head_dim_v * book.bits / 8);
     }

@@ -37,13 +37,16 @@ inline int tq_bits(int t) { return t - PKV_TQ2 + 2; }
 
 // A TQ codebook: E4M3 codes and values of the 2^(b-1) positive magnitudes
 // (ascending), the encoder's magnitude thresholds (midpoints; +inf past the
-// last), and the codes packed 4 per word as a byte lookup table.
+// last), and the decoder's 8-entry FP16 level table as byte-lookup words:
+// f16_lut[0], [1] hold the low bytes of entries 0-3 and 4-7, f16_lut[2], [3]
+// the high bytes.  Entry e is the level of code e (sign << (b-1) | index)
+// for b = 2, 3 and the magnitude of index e for b = 4.
 struct TqCodebook {
     int bits, mags_count;
     uint8_t codes[8];
     float mags[8];
     float thr[7];
-    uint32_t lut_lo, lut_hi;
+    uint32_t f16_lut[4];
 };
 const TqCodebook& tq_codebook(int bits);
 uint64_t tq_block_bytes(int bits, uint32_t B, uint32_t H, uint32_t D);
@@ -59,6 +62,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 // Two BF16 halves of a 32-bit word -> FP32 (exact: BF16 is the top half of
 // a binary32 pattern).
@@ -71,6 +76,21 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b)
     bf16x2 v;
     v.x = (__bf16)a;
     v.y = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Bitfield insert: bits of a where m is set, bits of b elsewhere (v_bfi_b32).
+__device__ __forceinline__ uint32_t bit_insert(uint32_t m, uint32_t a, uint32_t b)
+{
+    return (a & m) | (b & ~m);
+}
+
+// Two FP32 -> packed FP16, round to nearest even (v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b)
+{
+    f16x2 v;
+    v.x = (_Float16)a;
+    v.y = (_Float16)b;
     return __builtin_bit_cast(uint32_t, v);
 }
 

@@ -1,7 +1,8 @@
 // tq.cpp -- host side of the TurboQuant-style V formats (PKV_TQ2/3/4; page 1,
 // kv_cache.rs, reshape_and_cache_bf16k_turbo{2,3,4}v: b-bit Lloyd-Max codes
 // plus an FP8 per-group scale; page 2: one FP8 scale per 16 elements): the
-// codebook, computed once per bit width, and the block-size query.
+// codebook, computed once per bit width (with the decoder's FP16 level
+// table), and the block-size query.
 //
 // Codebook: Lloyd's iteration on the standard normal density -- cells at
 // the midpoints between levels, each level moved to its cell's conditional
@@ -48,6 +49,20 @@ static double e4m3_value(uint8_t c)
     return (c & 0x80) ? -v : v;
 }
 
+// IEEE binary16 bits of a value that binary16 holds exactly (a normal number
+// with at most 11 significant bits, as every E4M3 magnitude of the codebook).
+static uint16_t f16_bits(double v)
+{
+    if (v == 0.0)
+        return 0;
+    const uint16_t sign = v < 0 ? 0x8000 : 0;
+    int e2;
+    const double f = std::frexp(std::fabs(v), &e2);   // |v| = f * 2^e2, f in [0.5, 1)
+    const int field = e2 - 1 + 15;
+    const int man = (int)std::ldexp(2.0 * f - 1.0, 10);
+    return (uint16_t)(sign | field << 10 | man);
+}
+
 static void lloyd_max(int bits, double* lv)
 {
     const int L = 1 << bits;
@@ -92,9 +107,15 @@ const TqCodebook& tq_codebook(int bits)
             b.thr[j] = 0.5f * (b.mags[j] + b.mags[j + 1]);   // exact: E4M3 sums
         for (int j = b.mags_count - 1; j < 7; ++j)
             b.thr[j] = INFINITY;
-        for (int j = 0; j < 4; ++j) {
-            b.lut_lo |= (uint32_t)b.codes[j] << (8 * j);
-            b.lut_hi |= (uint32_t)b.codes[4 + j] << (8 * j);
+        for (int e = 0; e < 8; ++e) {
+            double v = 0.0;
+            if (bits == 4)
+                v = b.mags[e];
+            else if (e < 2 * b.mags_count)
+                v = e < b.mags_count ? b.mags[e] : -b.mags[e - b.mags_count];
+            const uint16_t h = f16_bits(v);
+            b.f16_lut[e / 4] |= (uint32_t)(h & 0xFF) << (8 * (e % 4));
+            b.f16_lut[2 + e / 4] |= (uint32_t)(h >> 8) << (8 * (e % 4));
         }
     });
     return books[i];
