@@ -512,17 +512,17 @@ def cpu_baseline(idx, lay, k_scale, v_kind="bf16", v_scale=1.0, window=0, sinks=
     v_fp8 = v_kind == "fp8"
     vb = v_elem_bytes(v_kind)
     if v_kind.startswith("tq"):
-        # random code bytes and random finite E4M3 scales
+        # random code bytes and random finite E4M3 scales; a block is one
+        # region per kv head: 16 code rows, then 16 scale rows
         bits = int(v_kind[2])
-        data = 16 * Hkv * Dv * bits // 8
-        blk = data + 16 * Hkv * Dv // 16
+        codes_b, scales_b = 16 * Dv * bits // 8, 16 * Dv // 16
         g = torch.Generator(device="cuda")
         g.manual_seed(W.seed_of(idx) * 1000 + W.S_POOLV)
-        codes = torch.randint(0, 256, (lay.num_blocks, data), dtype=torch.uint8, device="cuda",
-                              generator=g)
-        scales = torch.randint(0, 0x50, (lay.num_blocks, blk - data), dtype=torch.uint8,
+        codes = torch.randint(0, 256, (lay.num_blocks, Hkv, codes_b), dtype=torch.uint8,
+                              device="cuda", generator=g)
+        scales = torch.randint(0, 0x50, (lay.num_blocks, Hkv, scales_b), dtype=torch.uint8,
                                device="cuda", generator=g)
-        vp = torch.cat([codes, scales], dim=1).cpu().numpy()
+        vp = torch.cat([codes, scales], dim=2).reshape(lay.num_blocks, -1).cpu().numpy()
         del codes, scales
     elif v_fp8:
         g = torch.Generator(device="cuda")

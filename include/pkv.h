@@ -75,11 +75,13 @@ extern "C" {
  *     i = 0..15; u_i = x_i * (1 / sqrt(ss * 1/16)); magnitude index = the
  *     number of midpoints between adjacent magnitudes that |u_i| exceeds;
  *     sign = u_i < 0; scale = E4M3(sqrt(ss) / sqrt(sum of chosen m^2));
- *   - a cache block of B tokens is B * H * D * b / 8 bytes of codes -- token
- *     t, head h at byte (t * H + h) * D * b / 8, group q at 2 b bytes each,
- *     element i at bits [b i, b i + b) of the group's little-endian bytes --
- *     followed by B * H * D / 16 scale bytes, (t, h, q) at offset
- *     (t * H + h) * D / 16 + q (pkv_v_block_bytes gives the block size). */
+ *   - a cache block of B tokens holds one region of B * (D * b / 8 + D / 16)
+ *     bytes per kv head h, in head order: the code rows of tokens 0..B-1
+ *     (token t at t * D * b / 8, group q at 2 b bytes each, element i at
+ *     bits [b i, b i + b) of the group's little-endian bytes), then the
+ *     scale rows (scale of (t, q) at B * D * b / 8 + t * D / 16 + q), so a
+ *     head's codes and scales of one block are contiguous
+ *     (pkv_v_block_bytes gives the block size). */
 typedef enum pkv_dtype {
     PKV_BF16 = 0,
     PKV_FP8_E4M3 = 1,
@@ -210,7 +212,7 @@ int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype, uint64_t in_to
  *   (BF16, FP8_E4M3), (FP32, FP8_E4M3), (BF16 or FP32, TQ2/3/4); the cache
  *   row num_kv_heads * head_dim_v elements a multiple of 16 bytes in both
  *   dtypes; for TQ, head_dim_v a multiple of 16 and block_size *
- *   num_kv_heads * head_dim_v / 16 a multiple of 8 (v_cache: num_blocks *
+ *   head_dim_v / 16 a multiple of 8 (v_cache: num_blocks *
  *   pkv_v_block_bytes bytes, 16-byte aligned).
  */
 int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_token_stride,

@@ -359,10 +359,13 @@ void pkvo_cache_write_k(const void* k_in, int in_dtype, uint64_t in_token_stride
  *    positive), and its scale is E4M3 of |x| / |levels of the codes| (the
  *    norm correction: the decoded group has the input's L2 norm up to the
  *    scale's rounding); an all-zero group stores scale 0 and code 0;
- *  - layout of a cache block of B tokens: the codes of token t, head h at
- *    byte (t * H + h) * D * b / 8, group q at 2 b bytes each, element i at
- *    bits [b i, b i + b) of the group's little-endian bytes; then the scale
- *    section, scale of (t, h, q) at data_bytes + (t * H + h) * D / 16 + q.
+ *  - layout of a cache block of B tokens: one region per kv head h, at
+ *    h * B * (D * b / 8 + D / 16); in it the code rows of tokens 0..B-1
+ *    (token t at t * D * b / 8, group q at 2 b bytes each, element i at bits
+ *    [b i, b i + b) of the group's little-endian bytes), then the scale rows
+ *    (scale of (t, q) at B * D * b / 8 + t * D / 16 + q).  A head's codes and
+ *    scales of one block are thus contiguous (the pages fix no layout);
+ *  - the encoder's decisions are taken in FP32 (stated with its code).
  *  - no rotation and no sparse skip (the decode is exact). */
 
 static double std_normal_pdf(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846); }
@@ -411,25 +414,32 @@ void pkvo_tq_codebook(int bits, uint8_t* mag_codes)
 static int tq_bits(int dtype) { return dtype - O_TQ2 + 2; }
 static int is_tq(int dtype) { return dtype >= O_TQ2 && dtype <= O_TQ4; }
 
-/* bytes of one cache block of B tokens x H heads x D elements */
+/* bytes of one cache block of B tokens x H heads x D elements: one region
+ * per head, B code rows of D * bits / 8 bytes followed by B scale rows of
+ * D / 16 bytes */
+static uint64_t tq_region_bytes(int bits, uint32_t B, uint32_t D)
+{
+    return (uint64_t)B * D * bits / 8 + (uint64_t)B * D / 16;
+}
+
 uint64_t pkvo_tq_block_bytes(int bits, uint32_t B, uint32_t H, uint32_t D)
 {
-    return (uint64_t)B * H * D * bits / 8 + (uint64_t)B * H * D / 16;
+    return H * tq_region_bytes(bits, B, D);
 }
 
 /* Decoded element (blk, t, h, d) of a TQ cache. */
 static double tq_elem(const void* cache, int bits, uint32_t B, uint32_t H, uint32_t D,
                       const double* mags, uint64_t blk, uint32_t t, uint32_t h, uint32_t d)
 {
-    const uint8_t* base = (const uint8_t*)cache + blk * pkvo_tq_block_bytes(bits, B, H, D);
-    uint64_t data_bytes = (uint64_t)B * H * D * bits / 8;
-    const uint8_t* row = base + ((uint64_t)t * H + h) * D * bits / 8;
+    const uint8_t* base = (const uint8_t*)cache + blk * pkvo_tq_block_bytes(bits, B, H, D) +
+                          h * tq_region_bytes(bits, B, D);
+    const uint8_t* row = base + (uint64_t)t * D * bits / 8;
     uint32_t q = d / 16, i = d % 16;
     const uint8_t* grp = row + (uint64_t)q * 2 * bits;
     uint32_t bit = (uint32_t)bits * i, code = 0;
     for (int k = 0; k < bits; ++k, ++bit)
         code |= (uint32_t)((grp[bit / 8] >> (bit % 8)) & 1u) << k;
-    uint8_t sc = base[data_bytes + ((uint64_t)t * H + h) * (D / 16) + q];
+    uint8_t sc = base[(uint64_t)B * D * bits / 8 + (uint64_t)t * (D / 16) + q];
     double mag = mags[code & ((1u << (bits - 1)) - 1)];
     double v = (code >> (bits - 1)) ? -mag : mag;
     return pkvo_f64_from_e4m3(sc) * v;
@@ -459,7 +469,6 @@ void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride
     for (int j = 0; j + 1 < M; ++j)
         thr[j] = 0.5 * (mags[j] + mags[j + 1]);
     uint64_t blk_bytes = pkvo_tq_block_bytes(bits, B, H, D);
-    uint64_t data_bytes = (uint64_t)B * H * D * bits / 8;
     uint64_t num_slots = (uint64_t)num_blocks * B;
     for (uint64_t tok = 0; tok < num_tokens; ++tok) {
         int64_t slot = slots[tok];
@@ -467,9 +476,9 @@ void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride
             continue;
         uint64_t blk = (uint64_t)slot / B;
         uint32_t t = (uint32_t)((uint64_t)slot % B);
-        uint8_t* base = (uint8_t*)v_cache + blk * blk_bytes;
         for (uint32_t h = 0; h < H; ++h) {
-            uint8_t* row = base + ((uint64_t)t * H + h) * D * bits / 8;
+            uint8_t* base = (uint8_t*)v_cache + blk * blk_bytes + h * tq_region_bytes(bits, B, D);
+            uint8_t* row = base + (uint64_t)t * D * bits / 8;
             for (uint32_t q = 0; q < D / 16; ++q) {
                 float x[16], ss = 0.0f;
                 for (int i = 0; i < 16; ++i) {
@@ -506,7 +515,7 @@ void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride
                         uint32_t bit = (uint32_t)bits * i + k;
                         grp[bit / 8] |= (uint8_t)(((codes[i] >> k) & 1u) << (bit % 8));
                     }
-                base[data_bytes + ((uint64_t)t * H + h) * (D / 16) + q] = scale;
+                base[(uint64_t)B * D * bits / 8 + (uint64_t)t * (D / 16) + q] = scale;
             }
         }
     }

@@ -125,7 +125,7 @@ template <int IN, int BITS>   // IN: 0 = BF16 input, 2 = FP32 input
 __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
     const uint8_t* __restrict__ v, uint64_t in_stride_bytes, const int64_t* __restrict__ slots,
     uint32_t num_tokens, uint32_t H, uint32_t D, uint32_t B, uint64_t num_slots,
-    uint64_t blk_bytes, uint64_t data_bytes, TqArgs cb, uint8_t* __restrict__ cache)
+    uint64_t blk_bytes, uint64_t region_bytes, TqArgs cb, uint8_t* __restrict__ cache)
 {
     constexpr int M = 1 << (BITS - 1);                  // magnitudes
     const uint32_t groups = D / 16;
@@ -193,10 +193,12 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
         // the norm correction: scale so that |scale x levels| = |x|
         scale = e4m3_sat_x4(sqrtf(ss) / sqrtf(cn), 0.f, 0.f, 0.f) & 0xFFu;
     }
+    // head h's region of the block: B code rows of D * BITS / 8 bytes, then
+    // B scale rows of D / 16 bytes
     const uint64_t blk = (uint64_t)slot / B;
     const uint32_t t = (uint32_t)((uint64_t)slot % B);
-    uint8_t* base = cache + blk * blk_bytes;
-    uint8_t* dst = base + ((uint64_t)t * H + h) * D * BITS / 8 + (uint64_t)q * 2 * BITS;
+    uint8_t* base = cache + blk * blk_bytes + h * region_bytes;
+    uint8_t* dst = base + (uint64_t)t * D * BITS / 8 + (uint64_t)q * 2 * BITS;
     if constexpr (BITS == 2) {
         *(uint32_t*)dst = (uint32_t)codes;
     } else if constexpr (BITS == 3) {
@@ -207,7 +209,7 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
     } else {
         *(uint64_t*)dst = codes;
     }
-    base[data_bytes + ((uint64_t)t * H + h) * groups + q] = (uint8_t)scale;
+    base[(uint64_t)B * D * BITS / 8 + (uint64_t)t * groups + q] = (uint8_t)scale;
 }
 
 }  // namespace pkv
@@ -234,10 +236,10 @@ extern "C" int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_
             return fail(PKV_ERR_INVALID, "cache_write_v: zero dimension");
         if (head_dim_v % 16)
             return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: TQ needs head_dim_v %% 16 == 0");
-        // keeps every block, and so every group's code store, naturally aligned
-        if (((uint64_t)block_size * num_kv_heads * (head_dim_v / 16)) % 8)
+        // keeps every head region, and so every group's code store, naturally aligned
+        if (((uint64_t)block_size * (head_dim_v / 16)) % 8)
             return fail(PKV_ERR_UNSUPPORTED,
-                        "cache_write_v: TQ needs block_size * num_kv_heads * head_dim_v / 16 %% 8 == 0");
+                        "cache_write_v: TQ needs block_size * head_dim_v / 16 %% 8 == 0");
         const uint64_t es = dtype_size(in_dtype);
         if (in_token_stride < (uint64_t)num_kv_heads * head_dim_v)
             return fail(PKV_ERR_INVALID, "cache_write_v: in_token_stride smaller than a row");
@@ -256,13 +258,13 @@ extern "C" int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_
         if (nblk >= (1ull << 31))
             return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: too many tokens");
         const uint64_t blk_bytes = tq_block_bytes(bits, block_size, num_kv_heads, head_dim_v);
-        const uint64_t data_bytes = (uint64_t)block_size * num_kv_heads * head_dim_v * bits / 8;
+        const uint64_t region_bytes = blk_bytes / num_kv_heads;
         hipStream_t st = (hipStream_t)stream;
 #define PKV_TQW(IN, BITS)                                                                      \
     hipLaunchKernelGGL((cache_write_v_tq_kernel<IN, BITS>), dim3((uint32_t)nblk), dim3(256), 0, st, \
                        (const uint8_t*)v, in_token_stride * es, slot_mapping, num_tokens,      \
                        num_kv_heads, head_dim_v, block_size, (uint64_t)num_blocks * block_size, \
-                       blk_bytes, data_bytes, cb, (uint8_t*)v_cache)
+                       blk_bytes, region_bytes, cb, (uint8_t*)v_cache)
         if (in_dtype == PKV_BF16) {
             if (bits == 2) PKV_TQW(0, 2); else if (bits == 3) PKV_TQW(0, 3); else PKV_TQW(0, 4);
         } else {

@@ -39,6 +39,7 @@ namespace pkv {
 // Launch shape of the MFMA path.
 constexpr uint32_t kKvPerGroup = 2;     // kv heads (waves) per work-group, at most
 constexpr int kPrefetch = 1;            // cache blocks loaded ahead of the one in use
+constexpr bool kKDirect = false;        // K loaded straight into the operand layout
 constexpr uint64_t kTargetGroups = 2048;// (sequence, split, kv group) work-groups wanted
 constexpr uint32_t kMinChunk = 4;       // blocks per split, automatic choice: at least
 constexpr uint32_t kMaxChunk = 128;     // ... and at most (two table entries per lane)
@@ -64,10 +65,9 @@ struct DecodeArgs {
     float out_scale;        // v_scale for E4M3 V, else 1
     uint32_t window;        // sliding window in tokens, 0 = none
     // TurboQuant-style V: the FP16 level table as byte-lookup words (low
-    // bytes of entries 0-3, 4-7, high bytes of 0-3, 4-7), block and
-    // code-section bytes
+    // bytes of entries 0-3, 4-7, high bytes of 0-3, 4-7), and block bytes
     uint32_t tq_f16[4];
-    uint32_t v_blk_bytes, v_data_bytes;
+    uint32_t v_blk_bytes;
     // query rotation (FP32 path)
     uint32_t q_rope;
     float q_rope_theta;
@@ -237,7 +237,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
 {
     using KF = KFrag<KT, D>;
     constexpr int NI = KF::NI, NL = KF::NL;
-    __shared__ u32x4 s_k[8][16 * KF::CPR];          // one K tile per wave
+    __shared__ u32x4 s_k[kKvPerGroup][16 * KF::CPR]; // one K tile per wave
     constexpr int NT = D / 16;                 // PV N-tiles
     constexpr int DPL = D / 16;                // V dims per lane
     constexpr bool TQ = VT >= 2;               // TurboQuant-style V, VT bits per code
@@ -252,6 +252,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     const int wave = threadIdx.x >> 6;
     const int kg = lane >> 4;                  // 0..3
     const int ln = lane & 15;
+    // Token of MFMA row m (K operand row, k index of the PV product): m for
+    // BF16 / E4M3 V; for TQ V the 4 x 4 transpose, so that lane group kg,
+    // register r holds token 4 r + kg and one V load instruction (fixed r)
+    // reads four consecutive token rows of the head's contiguous region.
+    auto row_token = [](int m) { return TQ ? 4 * (m & 3) + (m >> 2) : m; };
     // Dispatch order is split-major: x = sequence * kv_groups + kv group,
     // y = split.  Work-groups are dealt to the XCDs round-robin by linear id,
     // so each split "layer" spreads the sequences that reach it evenly over
@@ -329,29 +334,33 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     // loop-invariant 32-bit values.
     const uint32_t kblk_bytes = (uint32_t)(kBS * krow_stride);
     const uint32_t vblk_bytes = TQ ? a.v_blk_bytes : (uint32_t)(kBS * vrow_stride * VES);
-    const uint32_t koff = (uint32_t)((lane / KF::CPR) * krow_stride + (uint64_t)kvh * D * KES +
-                                     16 * (lane % KF::CPR));
-    const uint32_t kstep = (uint32_t)(KF::RPL * krow_stride);     // next load: RPL rows down
+    const uint32_t koff = kKDirect
+        ? (uint32_t)(ln * krow_stride + (uint64_t)kvh * D * KES + 16 * kg)
+        : (uint32_t)((lane / KF::CPR) * krow_stride + (uint64_t)kvh * D * KES + 16 * (lane % KF::CPR));
+    // next load: RPL rows down (row-wise loads) or 4 chunks right (operand loads)
+    const uint32_t kstep = kKDirect ? 64u : (uint32_t)(KF::RPL * krow_stride);
     // LDS positions: written chunk of load j, operand chunk of MFMA group j
     uint32_t lds_w[NL], lds_r[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
         lds_w[j] = KF::lds_off(j * KF::RPL + lane / KF::CPR, lane % KF::CPR);
-        lds_r[j] = KF::lds_off(ln, KF::op_chunk(j, kg));
+        lds_r[j] = KF::lds_off(row_token(ln), KF::op_chunk(j, kg));
     }
     uint8_t* ktile = (uint8_t*)&s_k[wave][0];
     const uint32_t voff = (uint32_t)((4 * kg) * vrow_stride * VES + ((uint64_t)kvh * D + DPL * ln) * VES);
     const uint32_t vrow_bytes = (uint32_t)(vrow_stride * VES);
-    // TQ: codes of columns 8 ln .. 8 ln + 7 are VT bytes at VT * ln in the
-    // 16 VT-byte row of (token, kv head): a 16-bit or 32-bit load for 2- and
-    // 4-bit codes, an 8-byte window from the dword at or below for 3-bit
-    // codes.  Their group's scale: byte ln / 2 of the row's 8.
+    // TQ: a block holds one contiguous region per kv head: 16 code rows of
+    // 16 VT bytes, then 16 scale rows of 8 bytes.  Codes of columns
+    // 8 ln .. 8 ln + 7 are VT bytes at VT * ln in the token's code row (a
+    // 16-bit or 32-bit load for 2- and 4-bit codes, an 8-byte window from the
+    // dword at or below for 3-bit codes); their group's scale is byte ln / 2
+    // of the token's scale row.  Register r of lane group kg: token 4 r + kg.
+    constexpr uint32_t kTqRegion = kBS * (16u * VT + 8u);
     [[maybe_unused]] const uint32_t tq_coff =
-        (uint32_t)((4 * kg) * a.Hkv + kvh) * 16u * VT + (VT == 3 ? ((3u * ln) & ~3u) : VT * ln);
-    [[maybe_unused]] const uint32_t tq_crow = a.Hkv * 16u * VT;        // next token row
-    [[maybe_unused]] const uint32_t tq_soff =
-        a.v_data_bytes + (uint32_t)((4 * kg) * a.Hkv + kvh) * 8u + ln / 2;
-    [[maybe_unused]] const uint32_t tq_srow = a.Hkv * 8u;
+        kvh * kTqRegion + kg * 16u * VT + (VT == 3 ? ((3u * ln) & ~3u) : VT * ln);
+    [[maybe_unused]] const uint32_t tq_crow = 4u * 16u * VT;           // r -> r + 1: 4 rows
+    [[maybe_unused]] const uint32_t tq_soff = kvh * kTqRegion + kBS * 16u * VT + kg * 8u + ln / 2;
+    [[maybe_unused]] const uint32_t tq_srow = 4u * 8u;
     [[maybe_unused]] const uint32_t tq_shift = 8u * ((3u * ln) & 3u);
 
     // An unmapped block is read from block 0 instead (always inside the pool):
@@ -407,18 +416,24 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         // K rows -> MFMA operand layout through the wave's LDS tile (lanes
         // exchange data: order the writes after the previous block's reads
         // and before this block's reads, at wavefront scope)
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int j = 0; j < NL; ++j)
-            *(u32x4*)(ktile + lds_w[j]) = st.k[j];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         u32x4 kop[NL];
+        if constexpr (kKDirect) {
 #pragma unroll
-        for (int j = 0; j < NL; ++j)
-            kop[j] = *(const u32x4*)(ktile + lds_r[j]);
+            for (int j = 0; j < NL; ++j)
+                kop[j] = st.k[j];
+        } else {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int j = 0; j < NL; ++j)
+                *(u32x4*)(ktile + lds_w[j]) = st.k[j];
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int j = 0; j < NL; ++j)
+                kop[j] = *(const u32x4*)(ktile + lds_r[j]);
+        }
 
         // S^T = K q^T : lane holds S[t = 4kg + r][g = ln]
         f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -430,7 +445,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         float mx = -INFINITY;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int t = 4 * kg + r;
+            const int t = row_token(4 * kg + r);
             sv[r] = (t < ntok && t >= tlo) ? sacc[r] * a.qk_scale : -INFINITY;
             mx = fmaxf(mx, sv[r]);
         }
@@ -465,7 +480,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         if (ntok < kBS || tlo > 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                if (4 * kg + r >= ntok || 4 * kg + r < tlo)
+                if (row_token(4 * kg + r) >= ntok || row_token(4 * kg + r) < tlo)
 #pragma unroll
                     for (int w = 0; w < VW; ++w)
                         st.v[r][w] = 0u;
@@ -903,7 +918,6 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
             a.tq_f16[i] = book.f16_lut[i];
         a.out_scale = 1.f / 32768.f;          // the 2^15 on the FP16 weights
         a.v_blk_bytes = (uint32_t)tq_block_bytes(book.bits, kBS, num_kv_heads, head_dim_v);
-        a.v_data_bytes = (uint32_t)((uint64_t)kBS * num_kv_heads * head_dim_v * book.bits / 8);
     }
     a.q_rope = (q_rope && q_rope_dim > 0) ? 1u : 0u;
     a.q_rope_theta = q_rope_theta;

@@ -14,7 +14,7 @@ import torch
 import oracle
 import paged_kv_cache_fill_amd as pkv
 import pkv_workloads as W
-from _util import ATTN_TOL, attn_err, dev, host, say
+from _util import ATTN_TOL, attn_err, dev, host, say, tq_scale_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -127,11 +127,12 @@ def _tq_pool(lay, H, D, bits, seed, random_codes=False):
     block's scales are NaN (0x7F), so a read of it would show."""
     nb = lay.num_blocks
     blk = _blk(bits, H, D)
-    data = 16 * H * D * bits // 8
+    sm = tq_scale_mask(bits, H, D)
     pool = np.zeros((nb, blk), np.uint8)
     if random_codes:
-        pool[:, :data] = np.random.default_rng(seed).integers(0, 256, (nb, data), dtype=np.uint8)
-        pool[:, data:] = W.e4m3_codes(2, seed, (nb, blk - data))
+        pool[:, ~sm] = np.random.default_rng(seed).integers(0, 256, (nb, int((~sm).sum())),
+                                                             dtype=np.uint8)
+        pool[:, sm] = W.e4m3_codes(2, seed, (nb, int(sm.sum())))
     else:
         rng = np.random.default_rng(seed)
         x = (rng.standard_normal((nb * 16, H, D)) *
@@ -139,7 +140,7 @@ def _tq_pool(lay, H, D, bits, seed, random_codes=False):
         oracle.cache_write_v(x, "f32", np.arange(nb * 16, dtype=np.int64), pool, num_kv_heads=H,
                              head_dim_v=D, block_size=16, cache_dtype=f"tq{bits}")
     if lay.pad_block >= 0:
-        pool[lay.pad_block, data:] = 0x7F
+        pool[lay.pad_block, sm] = 0x7F
     return pool
 
 

@@ -22,6 +22,7 @@ from scipy.stats import norm
 
 import oracle
 import pkv_workloads as W
+from _util import tq_scale_mask
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -118,12 +119,13 @@ def test_power_of_two_scaling_only_scales():
     x = rng.standard_normal((3, 2, 32)).astype(np.float32)
     a = _encode(x, 3)
     b = _encode(x * np.float32(4.0), 3)
-    blk = oracle.tq_block_bytes(3, 16, 2, 32)
-    data = 16 * 2 * 32 * 3 // 8
-    assert (a[:data] == b[:data]).all()                           # same codes
-    sa = oracle.f64_from_e4m3(a[data:blk]).reshape(16, 2, 2)[:3]
-    sb = oracle.f64_from_e4m3(b[data:blk]).reshape(16, 2, 2)[:3]
-    assert np.allclose(sb, 4 * sa)
+    sm = tq_scale_mask(3, 2, 32)
+    assert sm.size == oracle.tq_block_bytes(3, 16, 2, 32)
+    assert (a[~sm] == b[~sm]).all()                               # same codes
+    # scale rows: [head][token][group]; tokens 0..2 hold the rows
+    sa = oracle.f64_from_e4m3(a[sm]).reshape(2, 16, 2)[:, :3]
+    sb = oracle.f64_from_e4m3(b[sm]).reshape(2, 16, 2)[:, :3]
+    assert (sa > 0).all() and np.allclose(sb, 4 * sa)
 
 
 def test_hand_worked_packing_example():
