@@ -513,7 +513,7 @@ def cpu_baseline(idx, lay, k_scale, v_kind="bf16", v_scale=1.0, window=0, sinks=
     vb = v_elem_bytes(v_kind)
     if v_kind.startswith("tq"):
         # random code bytes and random finite E4M3 scales; a block is one
-        # region per kv head: 16 code rows, then 16 scale rows
+        # region per kv head: 16 code rows, then Dv / 16 scale rows of 16 bytes
         bits = int(v_kind[2])
         codes_b, scales_b = 16 * Dv * bits // 8, 16 * Dv // 16
         g = torch.Generator(device="cuda")

@@ -78,9 +78,9 @@ extern "C" {
  *   - a cache block of B tokens holds one region of B * (D * b / 8 + D / 16)
  *     bytes per kv head h, in head order: the code rows of tokens 0..B-1
  *     (token t at t * D * b / 8, group q at 2 b bytes each, element i at
- *     bits [b i, b i + b) of the group's little-endian bytes), then the
- *     scale rows (scale of (t, q) at B * D * b / 8 + t * D / 16 + q), so a
- *     head's codes and scales of one block are contiguous
+ *     bits [b i, b i + b) of the group's little-endian bytes), then one
+ *     scale row of B bytes per group (scale of (t, q) at B * D * b / 8 +
+ *     q * B + t), so a head's codes and scales of one block are contiguous
  *     (pkv_v_block_bytes gives the block size). */
 typedef enum pkv_dtype {
     PKV_BF16 = 0,

@@ -362,9 +362,10 @@ void pkvo_cache_write_k(const void* k_in, int in_dtype, uint64_t in_token_stride
  *  - layout of a cache block of B tokens: one region per kv head h, at
  *    h * B * (D * b / 8 + D / 16); in it the code rows of tokens 0..B-1
  *    (token t at t * D * b / 8, group q at 2 b bytes each, element i at bits
- *    [b i, b i + b) of the group's little-endian bytes), then the scale rows
- *    (scale of (t, q) at B * D * b / 8 + t * D / 16 + q).  A head's codes and
- *    scales of one block are thus contiguous (the pages fix no layout);
+ *    [b i, b i + b) of the group's little-endian bytes), then one scale row
+ *    per group (scale of (t, q) at B * D * b / 8 + q * B + t).  A head's
+ *    codes and scales of one block are thus contiguous (the pages fix no
+ *    layout);
  *  - the encoder's decisions are taken in FP32 (stated with its code).
  *  - no rotation and no sparse skip (the decode is exact). */
 
@@ -415,8 +416,8 @@ static int tq_bits(int dtype) { return dtype - O_TQ2 + 2; }
 static int is_tq(int dtype) { return dtype >= O_TQ2 && dtype <= O_TQ4; }
 
 /* bytes of one cache block of B tokens x H heads x D elements: one region
- * per head, B code rows of D * bits / 8 bytes followed by B scale rows of
- * D / 16 bytes */
+ * per head, B code rows of D * bits / 8 bytes followed by D / 16 scale rows
+ * (one per group) of B bytes */
 static uint64_t tq_region_bytes(int bits, uint32_t B, uint32_t D)
 {
     return (uint64_t)B * D * bits / 8 + (uint64_t)B * D / 16;
@@ -439,7 +440,7 @@ static double tq_elem(const void* cache, int bits, uint32_t B, uint32_t H, uint3
     uint32_t bit = (uint32_t)bits * i, code = 0;
     for (int k = 0; k < bits; ++k, ++bit)
         code |= (uint32_t)((grp[bit / 8] >> (bit % 8)) & 1u) << k;
-    uint8_t sc = base[(uint64_t)B * D * bits / 8 + (uint64_t)t * (D / 16) + q];
+    uint8_t sc = base[(uint64_t)B * D * bits / 8 + (uint64_t)q * B + t];
     double mag = mags[code & ((1u << (bits - 1)) - 1)];
     double v = (code >> (bits - 1)) ? -mag : mag;
     return pkvo_f64_from_e4m3(sc) * v;
@@ -515,7 +516,7 @@ void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride
                         uint32_t bit = (uint32_t)bits * i + k;
                         grp[bit / 8] |= (uint8_t)(((codes[i] >> k) & 1u) << (bit % 8));
                     }
-                base[(uint64_t)B * D * bits / 8 + (uint64_t)t * (D / 16) + q] = scale;
+                base[(uint64_t)B * D * bits / 8 + (uint64_t)q * B + t] = scale;
             }
         }
     }

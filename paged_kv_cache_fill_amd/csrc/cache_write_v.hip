@@ -194,7 +194,7 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
         scale = e4m3_sat_x4(sqrtf(ss) / sqrtf(cn), 0.f, 0.f, 0.f) & 0xFFu;
     }
     // head h's region of the block: B code rows of D * BITS / 8 bytes, then
-    // B scale rows of D / 16 bytes
+    // D / 16 scale rows (one per group) of B bytes
     const uint64_t blk = (uint64_t)slot / B;
     const uint32_t t = (uint32_t)((uint64_t)slot % B);
     uint8_t* base = cache + blk * blk_bytes + h * region_bytes;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
     } else {
         *(uint64_t*)dst = codes;
     }
-    base[(uint64_t)B * D * BITS / 8 + (uint64_t)t * groups + q] = (uint8_t)scale;
+    base[(uint64_t)B * D * BITS / 8 + (uint64_t)q * B + t] = (uint8_t)scale;
 }
 
 }  // namespace pkv

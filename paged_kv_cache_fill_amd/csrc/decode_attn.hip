@@ -151,8 +151,8 @@ __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint3
 // The PV product of one 16-token block over a TurboQuant-style V cache (head
 // dim 128).  Lane (ln, kg) holds the weights p[r] of tokens t = 4kg + r (A
 // operand, row g = ln) and the raw V words of those tokens for its columns
-// 8 ln .. 8 ln + 7 (one half of a 16-element group): the codes and the
-// group's E4M3 scale byte.
+// 8 ln .. 8 ln + 7 (one half of a 16-element group): the codes, and a word
+// of the group's scale row whose byte `ssel` selects belongs to the token.
 //
 // Decoding works on two tokens at a time, so that every lookup already
 // yields the (t, t + 1) pairs that the FP16 B operand packs per column:
@@ -171,7 +171,8 @@ __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint3
 // accumulate in FP32.
 template <int VT, int VW>
 __device__ __forceinline__ void tq_pv(const DecodeArgs& a, const float (&p)[4],
-                                      const uint32_t (&v)[4][VW], uint32_t shift, f32x4 (&o)[8])
+                                      const uint32_t (&v)[4][VW], uint32_t shift, uint32_t ssel,
+                                      f32x4 (&o)[8])
 {
     constexpr uint32_t MSK = VT == 2 ? 0x03030303u : 0x07070707u;
     const f16x2 pa = __builtin_bit_cast(f16x2, pack_f16(p[0], p[1]));
@@ -181,7 +182,7 @@ __device__ __forceinline__ void tq_pv(const DecodeArgs& a, const float (&p)[4],
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
         const int r0 = 2 * pr, r1 = 2 * pr + 1;
-        const f32x2 sc = unpack_e4m3x2(v[r0][VW - 1] | (v[r1][VW - 1] << 8), false);
+        const f32x2 sc = unpack_e4m3x2(__builtin_amdgcn_perm(v[r1][VW - 1], v[r0][VW - 1], ssel), false);
         const f16x2 scale = __builtin_bit_cast(f16x2, pack_f16(sc.x, sc.y));
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {       // columns 4 hh .. 4 hh + 3
@@ -350,18 +351,21 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     const uint32_t voff = (uint32_t)((4 * kg) * vrow_stride * VES + ((uint64_t)kvh * D + DPL * ln) * VES);
     const uint32_t vrow_bytes = (uint32_t)(vrow_stride * VES);
     // TQ: a block holds one contiguous region per kv head: 16 code rows of
-    // 16 VT bytes, then 16 scale rows of 8 bytes.  Codes of columns
-    // 8 ln .. 8 ln + 7 are VT bytes at VT * ln in the token's code row (a
-    // 16-bit or 32-bit load for 2- and 4-bit codes, an 8-byte window from the
-    // dword at or below for 3-bit codes); their group's scale is byte ln / 2
-    // of the token's scale row.  Register r of lane group kg: token 4 r + kg.
+    // 16 VT bytes, then 8 scale rows (one per 16-column group) of 16 bytes,
+    // one per token.  Codes of columns 8 ln .. 8 ln + 7 are VT bytes at VT * ln
+    // in the token's code row (a 16-bit or 32-bit load for 2- and 4-bit codes,
+    // an 8-byte window from the dword at or below for 3-bit codes); the scales
+    // of their group are row ln / 2, one 16-byte load, of which dword r, byte
+    // kg belongs to token 4 r + kg = register r of lane group kg.
     constexpr uint32_t kTqRegion = kBS * (16u * VT + 8u);
     [[maybe_unused]] const uint32_t tq_coff =
         kvh * kTqRegion + kg * 16u * VT + (VT == 3 ? ((3u * ln) & ~3u) : VT * ln);
     [[maybe_unused]] const uint32_t tq_crow = 4u * 16u * VT;           // r -> r + 1: 4 rows
-    [[maybe_unused]] const uint32_t tq_soff = kvh * kTqRegion + kBS * 16u * VT + kg * 8u + ln / 2;
-    [[maybe_unused]] const uint32_t tq_srow = 4u * 8u;
+    [[maybe_unused]] const uint32_t tq_soff = kvh * kTqRegion + kBS * 16u * VT + (ln / 2) * 16u;
     [[maybe_unused]] const uint32_t tq_shift = 8u * ((3u * ln) & 3u);
+    // v_perm selector taking byte kg of two scale dwords (tokens 4 r + kg of
+    // a register pair) into bytes 0 and 1
+    [[maybe_unused]] const uint32_t tq_ssel = (uint32_t)kg | (4u + kg) << 8 | 0x0C0C0000u;
 
     // An unmapped block is read from block 0 instead (always inside the pool):
     // compute_block masks all of its tokens, so what it holds never counts.
@@ -378,6 +382,13 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff, j * kstep, kNT));
             st.k[j] = w;
         }
+        if constexpr (TQ) {                                               // scales of 16 tokens
+            const u32x4 s4 = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, tq_soff, 0, kNT));
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                st.v[r][VW - 1] = s4[r];
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {                                     // V: t = 4kg + r
             if constexpr (TQ) {
@@ -391,7 +402,6 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
                 } else {
                     st.v[r][0] = __builtin_amdgcn_raw_buffer_load_b16(vr, tq_coff, r * tq_crow, kNT);
                 }
-                st.v[r][VW - 1] = __builtin_amdgcn_raw_buffer_load_b8(vr, tq_soff, r * tq_srow, kNT);
             } else if constexpr (VW == 4) {
                 const u32x4 t4 = __builtin_bit_cast(
                     u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff, r * vrow_bytes, kNT));
@@ -486,7 +496,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
                         st.v[r][w] = 0u;
         }
         if constexpr (TQ) {
-            tq_pv<VT>(a, p, st.v, tq_shift, o);
+            tq_pv<VT>(a, p, st.v, tq_shift, tq_ssel, o);
             return;
         }
 

@@ -96,7 +96,7 @@ def say(*a):
 def tq_scale_mask(bits, H, D, B=16):
     """Boolean mask over one TQ cache block's bytes: True at scale bytes.
     The block is one region per kv head of B code rows (D * bits / 8 bytes
-    each) followed by B scale rows (D / 16 bytes each)."""
+    each) followed by D / 16 scale rows (B bytes each)."""
     codes, scales = B * D * bits // 8, B * D // 16
     region = np.concatenate([np.zeros(codes, bool), np.ones(scales, bool)])
     return np.tile(region, H)

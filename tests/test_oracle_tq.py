@@ -122,9 +122,9 @@ def test_power_of_two_scaling_only_scales():
     sm = tq_scale_mask(3, 2, 32)
     assert sm.size == oracle.tq_block_bytes(3, 16, 2, 32)
     assert (a[~sm] == b[~sm]).all()                               # same codes
-    # scale rows: [head][token][group]; tokens 0..2 hold the rows
-    sa = oracle.f64_from_e4m3(a[sm]).reshape(2, 16, 2)[:, :3]
-    sb = oracle.f64_from_e4m3(b[sm]).reshape(2, 16, 2)[:, :3]
+    # scale rows: [head][group][token]; tokens 0..2 hold the rows
+    sa = oracle.f64_from_e4m3(a[sm]).reshape(2, 2, 16)[:, :, :3]
+    sb = oracle.f64_from_e4m3(b[sm]).reshape(2, 2, 16)[:, :, :3]
     assert (sa > 0).all() and np.allclose(sb, 4 * sa)
 
 
