@@ -115,33 +115,38 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_e4m3_kernel(
 }
 
 // TurboQuant-style V: one thread per (token, kv head, 16-element group).
-// Codebook constants come from the host (tq.cpp).
+// The grid is (token blocks, kv heads); a work-group's threads are (token,
+// group) with the group index in the low `gshift` bits, so a wavefront covers
+// consecutive tokens of one head, whose code rows and scale bytes are
+// neighbours in the head's region of a cache block.  Codebook constants come
+// from the host (tq.cpp): the encoder's thresholds (midpoints of adjacent
+// magnitudes, +inf past the last), the magnitudes' E4M3 codes as an 8-byte
+// lookup table, and their squares.
 struct TqArgs {
-    float mags[8];
     float thr[7];
+    float sq[8];
+    uint32_t mag_lo, mag_hi;
 };
 
 template <int IN, int BITS>   // IN: 0 = BF16 input, 2 = FP32 input
 __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
     const uint8_t* __restrict__ v, uint64_t in_stride_bytes, const int64_t* __restrict__ slots,
-    uint32_t num_tokens, uint32_t H, uint32_t D, uint32_t B, uint64_t num_slots,
-    uint64_t blk_bytes, uint64_t region_bytes, TqArgs cb, uint8_t* __restrict__ cache)
+    uint32_t num_tokens, uint32_t groups, uint32_t gshift, uint32_t D, uint32_t B,
+    uint64_t num_slots, uint64_t blk_bytes, uint64_t region_bytes, TqArgs cb,
+    uint8_t* __restrict__ cache)
 {
     constexpr int M = 1 << (BITS - 1);                  // magnitudes
-    const uint32_t groups = D / 16;
-    const uint64_t gid = (uint64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (uint64_t)num_tokens * H * groups)
+    const uint32_t q = threadIdx.x & ((1u << gshift) - 1);
+    const uint32_t tok = (blockIdx.x << (8 - gshift)) + (threadIdx.x >> gshift);
+    const uint32_t h = blockIdx.y;
+    if (q >= groups || tok >= num_tokens)
         return;
-    const uint32_t q = (uint32_t)(gid % groups);
-    const uint64_t th = gid / groups;
-    const uint32_t h = (uint32_t)(th % H);
-    const uint64_t tok = th / H;
     const int64_t slot = slots[tok];
     if (slot < 0 || (uint64_t)slot >= num_slots)
         return;
 
     float x[16];
-    const uint8_t* src = v + tok * in_stride_bytes + ((uint64_t)h * D + 16u * q) * (IN == 0 ? 2 : 4);
+    const uint8_t* src = v + (uint64_t)tok * in_stride_bytes + ((uint64_t)h * D + 16u * q) * (IN == 0 ? 2 : 4);
     if constexpr (IN == 0) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -169,45 +174,68 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
     for (int i = 0; i < 16; ++i)
         ss = fmaf(x[i], x[i], ss);
 
-    uint64_t codes = 0;
+    uint32_t w[2] = {0u, 0u};                           // codes of elements 0-7, 8-15
     uint32_t scale = 0;
     if (ss > 0.f) {
         const float inv_r = 1.0f / sqrtf(ss * 0.0625f);
-        float cn = 0.f;
+        [[maybe_unused]] float cn4 = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float u = x[i] * inv_r;
             const float au = fabsf(u);
             uint32_t m = 0;
-            float mag = cb.mags[0];
 #pragma unroll
-            for (int j = 0; j + 1 < M; ++j) {
-                const bool up = au > cb.thr[j];        // ties stay on the smaller magnitude
-                m += up;
-                mag = up ? cb.mags[j + 1] : mag;
+            for (int j = 0; j + 1 < M; ++j)
+                m += au > cb.thr[j] ? 1u : 0u;          // ties stay on the smaller magnitude
+            if constexpr (BITS == 4) {
+                const float mag = unpack_e4m3x2(__builtin_amdgcn_perm(cb.mag_hi, cb.mag_lo, m), false).x;
+                cn4 = fmaf(mag, mag, cn4);
             }
-            cn = fmaf(mag, mag, cn);
             const uint32_t code = (u < 0.f ? (1u << (BITS - 1)) : 0u) | m;
-            codes |= (uint64_t)code << (BITS * i);
+            w[i / 8] |= code << (BITS * (i % 8));
+        }
+        // sum of the chosen magnitudes' squares: for 2- and 3-bit codes from
+        // the counts of each magnitude index in the packed codes (exact: a
+        // count times a square, summed, has few significant bits)
+        float cn;
+        if constexpr (BITS == 2) {
+            const uint32_t n1 = __builtin_popcount((w[0] | (w[1] << 16)) & 0x55555555u);
+            cn = fmaf((float)n1, cb.sq[1], (float)(16u - n1) * cb.sq[0]);
+        } else if constexpr (BITS == 3) {
+            uint32_t n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const uint32_t p0 = w[k] & 0x249249u, p1 = (w[k] >> 1) & 0x249249u;
+                const uint32_t both = __builtin_popcount(p0 & p1);
+                n3 += both;
+                n1 += __builtin_popcount(p0) - both;
+                n2 += __builtin_popcount(p1) - both;
+            }
+            cn = (float)(16u - n1 - n2 - n3) * cb.sq[0];
+            cn = fmaf((float)n1, cb.sq[1], cn);
+            cn = fmaf((float)n2, cb.sq[2], cn);
+            cn = fmaf((float)n3, cb.sq[3], cn);
+        } else {
+            cn = cn4;
         }
         // the norm correction: scale so that |scale x levels| = |x|
         scale = e4m3_sat_x4(sqrtf(ss) / sqrtf(cn), 0.f, 0.f, 0.f) & 0xFFu;
     }
     // head h's region of the block: B code rows of D * BITS / 8 bytes, then
     // D / 16 scale rows (one per group) of B bytes
-    const uint64_t blk = (uint64_t)slot / B;
-    const uint32_t t = (uint32_t)((uint64_t)slot % B);
-    uint8_t* base = cache + blk * blk_bytes + h * region_bytes;
+    const uint32_t blk = (uint32_t)slot / B;            // slots < 2^32 (checked by the host)
+    const uint32_t t = (uint32_t)slot - blk * B;
+    uint8_t* base = cache + (uint64_t)blk * blk_bytes + h * region_bytes;
     uint8_t* dst = base + (uint64_t)t * D * BITS / 8 + (uint64_t)q * 2 * BITS;
     if constexpr (BITS == 2) {
-        *(uint32_t*)dst = (uint32_t)codes;
+        *(uint32_t*)dst = w[0] | (w[1] << 16);
     } else if constexpr (BITS == 3) {
         uint16_t* d16 = (uint16_t*)dst;                 // 6 bytes, 2-byte aligned
-        d16[0] = (uint16_t)codes;
-        d16[1] = (uint16_t)(codes >> 16);
-        d16[2] = (uint16_t)(codes >> 32);
+        d16[0] = (uint16_t)w[0];
+        d16[1] = (uint16_t)((w[0] >> 16) | (w[1] << 8));
+        d16[2] = (uint16_t)(w[1] >> 8);
     } else {
-        *(uint64_t*)dst = codes;
+        *(u32x2*)dst = u32x2{w[0], w[1]};
     }
     base[(uint64_t)B * D * BITS / 8 + (uint64_t)q * B + t] = (uint8_t)scale;
 }
@@ -249,22 +277,31 @@ extern "C" int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_
         const int bits = tq_bits(cache_dtype);
         const TqCodebook& book = tq_codebook(bits);
         TqArgs cb{};
-        for (int j = 0; j < 8; ++j)
-            cb.mags[j] = book.mags[j];
         for (int j = 0; j < 7; ++j)
             cb.thr[j] = book.thr[j];
-        const uint64_t groups = (uint64_t)num_tokens * num_kv_heads * (head_dim_v / 16);
-        const uint64_t nblk = (groups + 255) / 256;
-        if (nblk >= (1ull << 31))
-            return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: too many tokens");
+        for (int j = 0; j < 8; ++j)
+            cb.sq[j] = book.mags[j] * book.mags[j];   // exact: E4M3 values
+        for (int j = 0; j < 4; ++j) {
+            cb.mag_lo |= (uint32_t)book.codes[j] << (8 * j);
+            cb.mag_hi |= (uint32_t)book.codes[4 + j] << (8 * j);
+        }
+        const uint32_t groups = head_dim_v / 16;
+        uint32_t gshift = 0;
+        while ((1u << gshift) < groups)
+            ++gshift;
+        if (gshift > 8 || num_kv_heads > 65535 || (uint64_t)num_blocks * block_size >= (1ull << 32))
+            return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: TQ shape too large");
+        const uint32_t tok_per_wg = 256u >> gshift;
+        const uint64_t nblk = ((uint64_t)num_tokens + tok_per_wg - 1) / tok_per_wg;
         const uint64_t blk_bytes = tq_block_bytes(bits, block_size, num_kv_heads, head_dim_v);
         const uint64_t region_bytes = blk_bytes / num_kv_heads;
         hipStream_t st = (hipStream_t)stream;
 #define PKV_TQW(IN, BITS)                                                                      \
-    hipLaunchKernelGGL((cache_write_v_tq_kernel<IN, BITS>), dim3((uint32_t)nblk), dim3(256), 0, st, \
-                       (const uint8_t*)v, in_token_stride * es, slot_mapping, num_tokens,      \
-                       num_kv_heads, head_dim_v, block_size, (uint64_t)num_blocks * block_size, \
-                       blk_bytes, region_bytes, cb, (uint8_t*)v_cache)
+    hipLaunchKernelGGL((cache_write_v_tq_kernel<IN, BITS>), dim3((uint32_t)nblk, num_kv_heads),     \
+                       dim3(256), 0, st, (const uint8_t*)v, in_token_stride * es, slot_mapping, \
+                       num_tokens, groups, gshift, head_dim_v, block_size,                      \
+                       (uint64_t)num_blocks * block_size, blk_bytes, region_bytes, cb,          \
+                       (uint8_t*)v_cache)
         if (in_dtype == PKV_BF16) {
             if (bits == 2) PKV_TQW(0, 2); else if (bits == 3) PKV_TQW(0, 3); else PKV_TQW(0, 4);
         } else {
