@@ -62,7 +62,7 @@ struct DecodeArgs {
     uint32_t chunk_blocks;
     uint32_t max_splits;
     float qk_scale;         // scale * log2(e) (* k_scale for E4M3 K)
-    float out_scale;        // v_scale for E4M3 V, else 1
+    float out_scale;        // output factor: v_scale (E4M3 V), 2^-15 for FP16 weights
     uint32_t window;        // sliding window in tokens, 0 = none
     // TurboQuant-style V: the FP16 level table as byte-lookup words (low
     // bytes of entries 0-3, 4-7, high bytes of 0-3, 4-7), and block bytes
@@ -146,6 +146,26 @@ __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint3
     }
 }
 
+// ------------------------------------------------------------------ FP16 PV
+
+// FP16 A operands of the PV product from the weights p[0..3] of the lane's
+// tokens (scaled by 2^15 by the caller): a hi part, and the rounding error
+// of it as a lo part, so that hi + lo keeps the weights to ~22 bits.
+struct F16Weights {
+    f16x4 hi, lo;
+};
+__device__ __forceinline__ F16Weights f16_weights(const float (&p)[4])
+{
+    F16Weights w;
+    const uint32_t h01 = pack_f16(p[0], p[1]), h23 = pack_f16(p[2], p[3]);
+    const f16x2 a = __builtin_bit_cast(f16x2, h01), b = __builtin_bit_cast(f16x2, h23);
+    const f16x2 c = __builtin_bit_cast(f16x2, pack_f16(p[0] - (float)a[0], p[1] - (float)a[1]));
+    const f16x2 d = __builtin_bit_cast(f16x2, pack_f16(p[2] - (float)b[0], p[3] - (float)b[1]));
+    w.hi = f16x4{a[0], a[1], b[0], b[1]};
+    w.lo = f16x4{c[0], c[1], d[0], d[1]};
+    return w;
+}
+
 // ------------------------------------------------------------------ TQ V
 
 // The PV product of one 16-token block over a TurboQuant-style V cache (head
@@ -175,9 +195,7 @@ __device__ __forceinline__ void tq_pv(const DecodeArgs& a, const float (&p)[4],
                                       f32x4 (&o)[8])
 {
     constexpr uint32_t MSK = VT == 2 ? 0x03030303u : 0x07070707u;
-    const f16x2 pa = __builtin_bit_cast(f16x2, pack_f16(p[0], p[1]));
-    const f16x2 pb = __builtin_bit_cast(f16x2, pack_f16(p[2], p[3]));
-    const f16x4 ap = f16x4{pa[0], pa[1], pb[0], pb[1]};
+    const F16Weights ap = f16_weights(p);
     uint32_t vb[2][8];                         // [token pair][column]: FP16 (t, t + 1)
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
@@ -223,7 +241,42 @@ __device__ __forceinline__ void tq_pv(const DecodeArgs& a, const float (&p)[4],
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
         const f16x4 bv = __builtin_bit_cast(f16x4, u32x2{vb[0][nt], vb[1][nt]});
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap, bv, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap.hi, bv, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap.lo, bv, o[nt], 0, 0, 0);
+    }
+}
+
+// The PV product of one 16-token block over an E4M3 V cache, in FP16: for
+// each pair of tokens a v_perm puts their codes of two columns side by side
+// and v_cvt_scalef32_pk_f16_fp8 (scale 1) widens each pair of codes to the
+// FP16 pair (t, t + 1) of one column -- exact, every E4M3 value is an FP16
+// number.  Weights as for TQ V (FP16, scaled by 2^15 by the caller).
+template <int NT, int VW>
+__device__ __forceinline__ void e4m3_pv(const float (&p)[4], const uint32_t (&v)[4][VW],
+                                        f32x4 (&o)[NT])
+{
+    const F16Weights ap = f16_weights(p);
+    uint32_t vb[2][NT];                        // [token pair][column]: FP16 (t, t + 1)
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+        for (int w = 0; w < VW; ++w) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {   // columns 4w + 2hh, 4w + 2hh + 1
+                const uint32_t x = __builtin_amdgcn_perm(v[2 * pr + 1][w], v[2 * pr][w],
+                                                         hh ? 0x07030602u : 0x05010400u);
+                vb[pr][4 * w + 2 * hh] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, false));
+                vb[pr][4 * w + 2 * hh + 1] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, 1.0f, true));
+            }
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const f16x4 bv = __builtin_bit_cast(f16x4, u32x2{vb[0][nt], vb[1][nt]});
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap.hi, bv, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ap.lo, bv, o[nt], 0, 0, 0);
     }
 }
 
@@ -465,15 +518,17 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         // masked scores give p = 0, and alpha = 0 leaves the zero state zero
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
-        // TQ: the weights go to the PV product as FP16 scaled by 2^15 (kept
-        // clear of FP16 subnormals; p <= 1); the normalisation divides it out
-        constexpr float kPOff = TQ ? 15.f : 0.f;
+        // TQ and E4M3 V: the weights go to the PV product as FP16 scaled by
+        // 2^15 (kept clear of FP16 subnormals; p <= 1); the normalisation
+        // divides it out
+        constexpr bool F16PV = TQ || VT == 1;
+        constexpr float kPOff = F16PV ? 15.f : 0.f;
         float p[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             p[r] = __builtin_amdgcn_exp2f(sv[r] - (m_ref - kPOff));
         const float psum = (p[0] + p[1]) + (p[2] + p[3]);
-        l = TQ ? __builtin_fmaf(psum, 1.f / 32768.f, l * alpha) : l * alpha + psum;
+        l = F16PV ? __builtin_fmaf(psum, 1.f / 32768.f, l * alpha) : l * alpha + psum;
         m = m_new;
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
             // O rows are g = 4kg + r; their factor lives in lane g
@@ -498,6 +553,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         if constexpr (TQ) {
             tq_pv<VT>(a, p, st.v, tq_shift, tq_ssel, o);
             return;
+        } else if constexpr (VT == 1) {
+            e4m3_pv<NT>(p, st.v, o);
+            return;
         }
 
         // P as hi + lo BF16 (A operand: lane holds P[g = ln][t = 4kg + r])
@@ -512,37 +570,17 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         const i16x4 a_lo = __builtin_bit_cast(i16x4, u32x2{pl[0], pl[1]});
 
         // B operand of N-tile nt: element nt of the lane's DPL columns, rows
-        // t = 4kg + 0..3; E4M3 codes are widened to FP32 (exact) and their
-        // upper halves are the BF16 values
-        [[maybe_unused]] float vf[4][DPL];
-        if constexpr (VT == 1) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int w = 0; w < VW; ++w) {
-                    const f32x2 lo = unpack_e4m3x2(st.v[r][w], false);
-                    const f32x2 hi = unpack_e4m3x2(st.v[r][w], true);
-                    vf[r][4 * w] = lo.x;
-                    vf[r][4 * w + 1] = lo.y;
-                    vf[r][4 * w + 2] = hi.x;
-                    vf[r][4 * w + 3] = hi.y;
-                }
-        }
+        // t = 4kg + 0..3
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             uint32_t b01, b23;
-            if constexpr (VT == 1) {
-                b01 = hi16_pair(__float_as_uint(vf[0][nt]), __float_as_uint(vf[1][nt]));
-                b23 = hi16_pair(__float_as_uint(vf[2][nt]), __float_as_uint(vf[3][nt]));
+            const int w = nt >> 1;
+            if (nt & 1) {
+                b01 = hi16_pair(st.v[0][w], st.v[1][w]);
+                b23 = hi16_pair(st.v[2][w], st.v[3][w]);
             } else {
-                const int w = nt >> 1;
-                if (nt & 1) {
-                    b01 = hi16_pair(st.v[0][w], st.v[1][w]);
-                    b23 = hi16_pair(st.v[2][w], st.v[3][w]);
-                } else {
-                    b01 = lo16_pair(st.v[0][w], st.v[1][w]);
-                    b23 = lo16_pair(st.v[2][w], st.v[3][w]);
-                }
+                b01 = lo16_pair(st.v[0][w], st.v[1][w]);
+                b23 = lo16_pair(st.v[2][w], st.v[3][w]);
             }
             const i16x4 bv = __builtin_bit_cast(i16x4, u32x2{b01, b23});
             o[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a_hi, bv, o[nt], 0, 0, 0);
@@ -920,7 +958,8 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     a.chunk_blocks = plan.chunk_blocks;
     a.max_splits = plan.max_splits;
     a.qk_scale = scale * kLog2e * (k_dtype == PKV_FP8_E4M3 ? k_scale : 1.0f);
-    a.out_scale = v_dtype == PKV_FP8_E4M3 ? v_scale : 1.0f;
+    // E4M3 and TQ V: the FP16 weights carry 2^15 (divided out here)
+    a.out_scale = v_dtype == PKV_FP8_E4M3 ? v_scale / 32768.f : 1.0f;
     a.window = sliding_window;
     if (is_tq(v_dtype)) {
         const TqCodebook& book = tq_codebook(tq_bits(v_dtype));
