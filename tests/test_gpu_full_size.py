@@ -1,0 +1,262 @@
+"""GPU parity at the full workload sizes, in the launch configuration that
+bench.py times, checked on sampled outputs the oracle computes one by one.
+
+Each decode workload is built as the bench builds it: every sequence's
+history (n - 1 tokens) goes through the library's slot fill, fused K write
+and V write into the shuffled pools; then one decode step writes the new
+token of every sequence and runs the decode attention over the whole batch
+with the automatic split plan.  Checked against the oracle:
+  * slots of the decode step: all of them, bit-exact;
+  * K rows of sampled history tokens and of the new tokens of sampled
+    sequences: the K-store bar (BF16 <= 1 ulp or the row floor, E4M3 <= 1
+    step); V rows of the same tokens bit-exact (copy, E4M3 or TQ bytes);
+  * the attention output of sampled sequences (the shortest, the longest and
+    random ones), recomputed by the oracle over the blocks those sequences
+    own (gathered from the device pools): <= 2e-3 row-relative.
+The prefill workload is checked the same way on sampled sequences.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import oracle
+import paged_kv_cache_fill_amd as pkv
+import pkv_workloads as W
+from _util import ATTN_TOL, attn_err, bf16_ok, e4m3_ok, host, say
+
+pytestmark = pytest.mark.gpu
+
+B = 16
+K_SCALE = 0.0625            # an input scalar; parity does not depend on its value
+V_SCALE = 0.02
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.int32)).cuda()
+
+
+def _bits(t):
+    """device tensor -> numpy with BF16 as uint16 and E4M3 as uint8."""
+    return host(t)
+
+
+def _check_k_rows(k_in, pos, got, cfg, w, cache_dtype, k_scale):
+    n, H, D = k_in.shape
+    ref = np.zeros(((n + B - 1) // B, B, H, D), oracle.NP_TYPES[cache_dtype])
+    oracle.cache_write_k(k_in, "bf16", np.arange(n, dtype=np.int64), ref, cache_dtype,
+                         num_kv_heads=H, head_dim=D, block_size=B, norm_weight=w,
+                         eps=cfg["eps"], pos_t=pos, theta=cfg["theta"], k_scale=k_scale,
+                         nthreads=8)
+    ref = ref.reshape(-1, H, D)[:n]
+    ok = bf16_ok(got, ref) if cache_dtype == "bf16" else e4m3_ok(got, ref)
+    assert ok.all(), f"{int((~ok).sum())} K elements outside the bar"
+
+
+def _tq_token_bytes(block_rows, t, bits, H, D):
+    """Bytes of token t (codes, then its scale of each group) of every head
+    region, from cache blocks [n, block_bytes]."""
+    region = B * (D * bits // 8 + D // 16)
+    cb = D * bits // 8
+    out = []
+    for h in range(H):
+        r = block_rows[:, h * region:(h + 1) * region]
+        codes = r[:, t * cb:(t + 1) * cb]
+        scales = r[:, B * cb + np.arange(D // 16) * B + t]
+        out.append(np.concatenate([codes, scales], axis=1))
+    return np.concatenate(out, axis=1)
+
+
+def _check_v_rows(v_in, got_rows, v_kind, H, D):
+    """v_in [n, H, D] BF16 bits; got_rows: [n, H, D] (copy / E4M3) or, for
+    TQ, [n, bytes] of each token's bytes in slot order."""
+    n = v_in.shape[0]
+    if v_kind == "bf16":
+        assert (got_rows == v_in).all()
+        return
+    if v_kind == "fp8":
+        ref = np.zeros(((n + B - 1) // B, B, H, D), np.uint8)
+        oracle.cache_write_v(v_in, "bf16", np.arange(n, dtype=np.int64), ref, num_kv_heads=H,
+                             head_dim_v=D, block_size=B, cache_dtype="fp8", v_scale=V_SCALE)
+        assert (got_rows == ref.reshape(-1, H, D)[:n]).all()
+        return
+    bits = int(v_kind[2])
+    nb = (n + B - 1) // B
+    ref = np.zeros((nb, oracle.tq_block_bytes(bits, B, H, D)), np.uint8)
+    oracle.cache_write_v(v_in, "bf16", np.arange(n, dtype=np.int64), ref, num_kv_heads=H,
+                         head_dim_v=D, block_size=B, cache_dtype=v_kind)
+    want = np.stack([_tq_token_bytes(ref[i // B:i // B + 1], i % B, bits, H, D)[0]
+                     for i in range(n)])
+    assert (got_rows == want).all()
+
+
+def _gather_rows(pool, slots, v_kind, H, D):
+    """Rows at the given slots from a device pool (numpy, cache dtype)."""
+    s = torch.from_numpy(np.asarray(slots, np.int64)).cuda()
+    if v_kind is not None and v_kind.startswith("tq"):
+        bits = int(v_kind[2])
+        blocks = _bits(pool.index_select(0, s // B))
+        return np.stack([_tq_token_bytes(blocks[i:i + 1], int(slots[i]) % B, bits, H, D)[0]
+                         for i in range(len(slots))])
+    flat = pool.view(-1, H, D)
+    return _bits(flat.index_select(0, s))
+
+
+def _sub_pool(lay, seqs, k_pool, v_pool):
+    """The blocks of the sampled sequences, gathered from the device pools,
+    and their block tables renumbered into that sub-pool."""
+    nblk = (lay.seq_lens.astype(np.int64) + B - 1) // B
+    ids = np.unique(np.concatenate([lay.block_tables[s, :nblk[s]] for s in seqs]))
+    new = np.full(lay.num_blocks, -1, np.int64)
+    new[ids] = np.arange(ids.size)
+    bt = np.zeros((len(seqs), lay.block_tables.shape[1]), np.int32)
+    for i, s in enumerate(seqs):
+        bt[i, :nblk[s]] = new[lay.block_tables[s, :nblk[s]]]
+    idx = torch.from_numpy(ids).cuda()
+    return _bits(k_pool.index_select(0, idx)), _bits(v_pool.index_select(0, idx)), bt
+
+
+def _sample_seqs(lens, k, seed):
+    rng = np.random.default_rng(seed)
+    pick = {int(np.argmin(lens)), int(np.argmax(lens))}
+    pick |= set(int(x) for x in rng.choice(len(lens), size=k, replace=False))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", sorted(bench.WORKLOADS))
+def test_full_size_decode_step_sampled(name):
+    idx, v_kind, window, use_sinks = bench.WORKLOADS[name]
+    tq = int(v_kind[2]) if v_kind.startswith("tq") else 0
+    lay = W.layout(idx)
+    cfg = lay.cfg
+    S, Hq, Hkv, D = lay.num_seqs, cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"]
+    fp8 = cfg["k_cache_dtype"] == "fp8"
+    k_dt = "fp8" if fp8 else "bf16"
+    k_scale = K_SCALE if fp8 else 1.0
+    v_scale = V_SCALE if v_kind == "fp8" else 1.0
+    say(f"full-size decode step {name}: {S} seqs, {lay.total_tokens} tokens, "
+        f"pool {lay.num_blocks} blocks")
+    dev = torch.device("cuda")
+    k_pool = torch.empty((lay.num_blocks, B, Hkv, D),
+                         dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16, device=dev)
+    if tq:
+        v_pool = torch.empty((lay.num_blocks, pkv.v_block_bytes(tq + 1, B, Hkv, D)),
+                             dtype=torch.uint8, device=dev)
+    else:
+        v_pool = torch.empty((lay.num_blocks, B, Hkv, D),
+                             dtype=torch.float8_e4m3fn if v_kind == "fp8" else torch.bfloat16,
+                             device=dev)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    seq_lens = torch.from_numpy(lay.seq_lens).to(dev)
+    w_np = W.norm_weight(idx)
+    w = torch.from_numpy(w_np.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    # population write (history = positions 0 .. n-2)
+    lens = lay.seq_lens.astype(np.int64)
+    Th = int((lens - 1).sum())
+    start_h, cu_h, pos_h = W.positions_history(lay)
+    k_hist = W.device_normal(idx, W.S_K, (Th, Hkv, D), torch.bfloat16, dev, outliers=fp8)
+    v_hist = W.device_normal(idx, W.S_V, (Th, Hkv, D), torch.bfloat16, dev)
+    slots_h = torch.empty(Th, dtype=torch.int64, device=dev)
+    pkv.fill_slots(slots_h, bt, _i32(start_h), _i32(cu_h), B)
+    pkv.cache_write_k_fused(k_hist, slots_h, k_pool, norm_weight=w, eps=cfg["eps"],
+                            pos_t=_i32(pos_h), theta=cfg["theta"], k_scale=k_scale)
+    pkv.cache_write_v(v_hist, slots_h, v_pool, v_scale=v_scale, tq_bits=tq)
+
+    # the decode step: new token at position n - 1 of every sequence
+    k_new = W.device_normal(idx, W.S_KNEW, (S, Hkv, D), torch.bfloat16, dev, outliers=fp8)
+    v_new = W.device_normal(idx, W.S_VNEW, (S, Hkv, D), torch.bfloat16, dev)
+    q = W.device_normal(idx, W.S_Q, (S, Hq, D), torch.bfloat16, dev, outliers=fp8)
+    start_d, cu_d, pos_d = W.positions_decode(lay)
+    slots_d = torch.empty(S, dtype=torch.int64, device=dev)
+    pkv.fill_slots(slots_d, bt, _i32(start_d), _i32(cu_d), B)
+    pkv.cache_write_k_fused(k_new, slots_d, k_pool, norm_weight=w, eps=cfg["eps"],
+                            pos_t=_i32(pos_d), theta=cfg["theta"], k_scale=k_scale)
+    pkv.cache_write_v(v_new, slots_d, v_pool, v_scale=v_scale, tq_bits=tq)
+    sinks = W.normal(idx, W.S_SINKS, (Hq,)) if use_sinks else None
+    ws = torch.empty(max(16, pkv.decode_workspace_bytes(S, Hq, Hkv, D, lay.max_blocks_per_seq,
+                                                        B, 0, window)),
+                     dtype=torch.uint8, device=dev)
+    out = pkv.paged_decode_attn(q, k_pool, v_pool, bt, seq_lens, scale=D ** -0.5,
+                                k_scale=k_scale, v_scale=v_scale, sliding_window=window,
+                                sinks=None if sinks is None else torch.from_numpy(sinks).to(dev),
+                                workspace=ws, v_tq_bits=tq)
+    torch.cuda.synchronize()
+
+    # slots of the step: all of them
+    ref_slots = oracle.fill_slots(lay.block_tables, start_d, cu_d, S, B)
+    assert (host(slots_d) == ref_slots).all()
+
+    # K and V rows: sampled history tokens and the new tokens of sampled sequences
+    rng = np.random.default_rng(idx)
+    hist_tok = np.sort(rng.choice(Th, size=96, replace=False))
+    seqs = _sample_seqs(lens, 4, 100 + idx)
+    tok_idx = torch.from_numpy(hist_tok).to(dev)
+    h_slots = host(slots_h)[hist_tok]
+    for rows_k, rows_v, slots, pos in (
+            (_bits(k_hist.index_select(0, tok_idx)), _bits(v_hist.index_select(0, tok_idx)),
+             h_slots, pos_h[hist_tok]),
+            (_bits(k_new)[seqs], _bits(v_new)[seqs], ref_slots[seqs], pos_d[seqs])):
+        _check_k_rows(rows_k, pos, _gather_rows(k_pool, slots, None, Hkv, D), cfg, w_np,
+                      k_dt, k_scale)
+        _check_v_rows(rows_v, _gather_rows(v_pool, slots, v_kind, Hkv, D), v_kind, Hkv, D)
+
+    # attention output of sampled sequences
+    kp, vp, bt_sub = _sub_pool(lay, seqs, k_pool, v_pool)
+    qs = _bits(q)[seqs]
+    ref = oracle.paged_decode(qs, "bf16", kp, k_dt, vp, v_kind, bt_sub, lay.seq_lens[seqs],
+                              num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=D,
+                              block_size=B, scale=D ** -0.5, k_scale=k_scale, v_scale=v_scale,
+                              sliding_window=window, sinks=sinks, nthreads=8)
+    got = host(out)[seqs]
+    err = attn_err(got, ref)
+    say(f"  sequences {seqs} (lengths {lens[seqs].tolist()}): err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATTN_TOL
+
+
+def test_full_size_prefill_sampled():
+    name = "prefill_bf16_256seq_chunk256"
+    idx, chunk = bench.PREFILL_WORKLOADS[name]
+    lay = W.layout(idx)
+    cfg = lay.cfg
+    S, Hq, Hkv, D = lay.num_seqs, cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"]
+    say(f"full-size prefill {name}: {S} seqs, chunk {chunk}")
+    dev = torch.device("cuda")
+    lens = lay.seq_lens.astype(np.int64)
+    qlens = np.minimum(lens, chunk)
+    Tc = int(qlens.sum())
+    # the whole cache (history and chunk rows) written through the library
+    start, cu, pos = W.positions_all(lay)
+    T = int(cu[-1])
+    k_pool = torch.empty((lay.num_blocks, B, Hkv, D), dtype=torch.bfloat16, device=dev)
+    v_pool = torch.empty_like(k_pool)
+    bt = torch.from_numpy(lay.block_tables).to(dev)
+    w = torch.from_numpy(W.norm_weight(idx).view(np.int16)).to(dev).view(torch.bfloat16)
+    k_all = W.device_normal(idx, W.S_K, (T, Hkv, D), torch.bfloat16, dev)
+    v_all = W.device_normal(idx, W.S_V, (T, Hkv, D), torch.bfloat16, dev)
+    slots = torch.empty(T, dtype=torch.int64, device=dev)
+    pkv.fill_slots(slots, bt, _i32(start), _i32(cu), B)
+    pkv.cache_write_k_fused(k_all, slots, k_pool, norm_weight=w, eps=cfg["eps"], pos_t=_i32(pos),
+                            theta=cfg["theta"])
+    pkv.cache_write_v(v_all, slots, v_pool)
+    del k_all, v_all
+    cu_q = np.concatenate([[0], np.cumsum(qlens)]).astype(np.int32)
+    q = W.device_normal(idx, W.S_Q, (Tc, Hq, D), torch.bfloat16, dev)
+    out = pkv.paged_prefill_attn(q, _i32(cu_q), k_pool, v_pool, bt,
+                                 torch.from_numpy(lay.seq_lens).to(dev), max_q_len=chunk,
+                                 scale=D ** -0.5)
+    torch.cuda.synchronize()
+    seqs = _sample_seqs(lens, 1, 7)
+    kp, vp, bt_sub = _sub_pool(lay, seqs, k_pool, v_pool)
+    qh = _bits(q)
+    qs = np.concatenate([qh[cu_q[s]:cu_q[s + 1]] for s in seqs])
+    cu_sub = np.concatenate([[0], np.cumsum(qlens[seqs])]).astype(np.int32)
+    ref = oracle.paged_prefill(qs, "bf16", cu_sub, kp, "bf16", vp, "bf16", bt_sub,
+                               lay.seq_lens[seqs], num_q_heads=Hq, num_kv_heads=Hkv,
+                               head_dim_qk=D, head_dim_v=D, block_size=B, scale=D ** -0.5,
+                               nthreads=8)
+    oh = host(out)
+    got = np.concatenate([oh[cu_q[s]:cu_q[s + 1]] for s in seqs])
+    err = attn_err(got, ref)
+    say(f"  sequences {seqs} (lengths {lens[seqs].tolist()}): err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATTN_TOL
