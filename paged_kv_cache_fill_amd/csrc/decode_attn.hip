@@ -42,7 +42,8 @@ constexpr int kPrefetch = 1;            // cache blocks loaded ahead of the one 
 constexpr bool kKDirect = false;        // K loaded straight into the operand layout
 constexpr uint64_t kTargetGroups = 2048;// (sequence, split, kv group) work-groups wanted
 constexpr uint32_t kMinChunk = 4;       // blocks per split, automatic choice: at least
-constexpr uint32_t kMaxChunk = 128;     // ... and at most (two table entries per lane)
+constexpr int kBtRegs = 2;              // table entries held per lane
+constexpr uint32_t kMaxChunk = 64 * kBtRegs;  // ... and at most (the table entries held)
 
 struct DecodeArgs {
     const void* q;
@@ -352,18 +353,21 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         }
     }
 
-    // block-table entries of this split, two per lane (chunk_blocks <= 128):
-    // entry i is lane i % 64 of bt_lane[i / 64]; lanes past the split re-read
-    // its last entry, so the loads are unconditional
-    int32_t bt_lane[2];
+    // block-table entries of this split, kBtRegs per lane (chunk_blocks <=
+    // 64 kBtRegs): entry i is lane i % 64 of bt_lane[i / 64]; lanes past the
+    // split re-read its last entry, so the loads are unconditional
+    int32_t bt_lane[kBtRegs];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kBtRegs; ++h) {
         const uint32_t idx = b0 + 64 * h + lane;
         bt_lane[h] = a.bt[(uint64_t)s * a.M + (idx < b1 ? idx : b1 - 1)];
     }
     auto table_entry = [&](uint32_t i) -> int32_t {
-        return i < 64 ? __builtin_amdgcn_readlane(bt_lane[0], (int)i)
-                      : __builtin_amdgcn_readlane(bt_lane[1], (int)(i - 64));
+        int32_t r = bt_lane[0];
+#pragma unroll
+        for (int h = 1; h < kBtRegs; ++h)
+            r = i >= 64u * h ? bt_lane[h] : r;          // wave-uniform choice
+        return __builtin_amdgcn_readlane(r, (int)(i & 63));
     };
 
     const uint8_t* kbase = (const uint8_t*)a.k_cache;

@@ -260,3 +260,67 @@ def test_full_size_prefill_sampled():
     err = attn_err(got, ref)
     say(f"  sequences {seqs} (lengths {lens[seqs].tolist()}): err {err:.3e}")
     assert np.isfinite(got).all() and err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("v_kind", ["bf16", "tq3"])
+def test_pool_beyond_4gib(v_kind):
+    """Sequences whose blocks lie past 4 GiB of a 5.8 GiB pool (BF16 K; BF16
+    or TQ3 V): slot fill, K and V writes, and decode reach them through
+    64-bit offsets."""
+    Hq, Hkv, D = 32, 8, 128
+    nb = 180_000                                  # x 32 KiB per BF16 block = 5.5 GiB
+    lens = np.array([1, 700, 2500, 5000], np.int32)
+    nblk = (lens + B - 1) // B
+    M = int(nblk.max())
+    # each sequence's blocks: the last ones of the pool, shuffled
+    rng = np.random.default_rng(11)
+    top = rng.permutation(np.arange(nb - int(nblk.sum()), nb)).astype(np.int32)
+    bt = np.zeros((lens.size, M), np.int32)
+    off = 0
+    for s, k in enumerate(nblk):
+        bt[s, :k] = top[off:off + k]
+        off += k
+    lay = W.Layout(2, lens, bt, nb, -1, B)
+    assert int(bt.max()) * B * Hkv * D * 2 >= 1 << 32
+    tq = 3 if v_kind == "tq3" else 0
+    say(f"pool of {nb} blocks, V {v_kind}: blocks {int(bt[bt > 0].min())}..{int(bt.max())}")
+    dev = torch.device("cuda")
+    k_pool = torch.zeros((nb, B, Hkv, D), dtype=torch.bfloat16, device=dev)
+    if tq:
+        v_pool = torch.zeros((nb, pkv.v_block_bytes(tq + 1, B, Hkv, D)), dtype=torch.uint8,
+                             device=dev)
+    else:
+        v_pool = torch.zeros_like(k_pool)
+    cfg = W.WORKLOADS[2]
+    start, cu, pos = W.positions_all(lay)
+    T = int(cu[-1])
+    k_in = W.device_normal(2, 501, (T, Hkv, D), torch.bfloat16, dev)
+    v_in = W.device_normal(2, 502, (T, Hkv, D), torch.bfloat16, dev)
+    w_np = W.norm_weight(2)
+    w = torch.from_numpy(w_np.view(np.int16)).to(dev).view(torch.bfloat16)
+    slots = torch.empty(T, dtype=torch.int64, device=dev)
+    bt_d = torch.from_numpy(bt).to(dev)
+    pkv.fill_slots(slots, bt_d, _i32(start), _i32(cu), B)
+    pkv.cache_write_k_fused(k_in, slots, k_pool, norm_weight=w, eps=cfg["eps"], pos_t=_i32(pos),
+                            theta=cfg["theta"])
+    pkv.cache_write_v(v_in, slots, v_pool, tq_bits=tq)
+    q = W.device_normal(2, 503, (lens.size, Hq, D), torch.bfloat16, dev)
+    out = pkv.paged_decode_attn(q, k_pool, v_pool, bt_d, torch.from_numpy(lens).to(dev),
+                                scale=D ** -0.5, v_tq_bits=tq)
+    torch.cuda.synchronize()
+    ref_slots = oracle.fill_slots(bt, start, cu, T, B)
+    assert (host(slots) == ref_slots).all() and ref_slots.max() * Hkv * D * 2 >= 1 << 32
+    pick = np.sort(rng.choice(T, size=64, replace=False))
+    idx = torch.from_numpy(pick).to(dev)
+    _check_k_rows(_bits(k_in.index_select(0, idx)), pos[pick],
+                  _gather_rows(k_pool, ref_slots[pick], None, Hkv, D), cfg, w_np, "bf16", 1.0)
+    _check_v_rows(_bits(v_in.index_select(0, idx)),
+                  _gather_rows(v_pool, ref_slots[pick], v_kind, Hkv, D), v_kind, Hkv, D)
+    seqs = list(range(lens.size))
+    kp, vp, bt_sub = _sub_pool(lay, seqs, k_pool, v_pool)
+    ref = oracle.paged_decode(_bits(q), "bf16", kp, "bf16", vp, v_kind, bt_sub, lens,
+                              num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=D,
+                              block_size=B, scale=D ** -0.5, nthreads=8)
+    err = attn_err(host(out), ref)
+    say(f"  err {err:.3e}")
+    assert np.isfinite(host(out)).all() and err <= ATTN_TOL
