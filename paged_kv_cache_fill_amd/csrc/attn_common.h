@@ -119,12 +119,13 @@ struct KFrag {
             u32x4 r;
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
+                // E4M3 values are exact in BF16: widen each pair of codes in
+                // one step (v_cvt_scalef32_pk_bf16_fp8, scale 1)
                 const uint32_t word = src[base + q];
-                f32x2 a = unpack_e4m3x2(word, false);
-                f32x2 b = unpack_e4m3x2(word, true);
-                // E4M3 values are exact in BF16: keep the upper halves
-                r[2 * q] = hi16_pair(__float_as_uint(a.x), __float_as_uint(a.y));
-                r[2 * q + 1] = hi16_pair(__float_as_uint(b.x), __float_as_uint(b.y));
+                r[2 * q] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, false));
+                r[2 * q + 1] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, true));
             }
             return __builtin_bit_cast(bf16x8, r);
         }
