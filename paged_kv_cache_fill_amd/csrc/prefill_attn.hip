@@ -362,26 +362,22 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
                     vr[r][0] = keep ? x : 0u;
                 }
             }
-            [[maybe_unused]] float vf[4][DPL];
-            if constexpr (VT == 1) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-#pragma unroll
-                    for (int w = 0; w < VW; ++w) {
-                        const f32x2 lo = unpack_e4m3x2(vr[r][w], false);
-                        const f32x2 hi = unpack_e4m3x2(vr[r][w], true);
-                        vf[r][4 * w] = lo.x;
-                        vf[r][4 * w + 1] = lo.y;
-                        vf[r][4 * w + 2] = hi.x;
-                        vf[r][4 * w + 3] = hi.y;
-                    }
-            }
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 uint32_t b01, b23;
                 if constexpr (VT == 1) {
-                    b01 = hi16_pair(__float_as_uint(vf[0][nt]), __float_as_uint(vf[1][nt]));
-                    b23 = hi16_pair(__float_as_uint(vf[2][nt]), __float_as_uint(vf[3][nt]));
+                    // the two rows' codes of column nt side by side, then widened
+                    // exactly to a BF16 pair (v_cvt_scalef32_pk_bf16_fp8, scale 1)
+                    const int w = nt / 4, e = nt % 4;
+                    const uint32_t sel = e < 2 ? 0x05010400u : 0x07030602u;
+                    const uint32_t x01 = __builtin_amdgcn_perm(vr[1][w], vr[0][w], sel);
+                    const uint32_t x23 = __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel);
+                    const bf16x2 p01 = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x01, 1.0f, true)
+                                               : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x01, 1.0f, false);
+                    const bf16x2 p23 = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x23, 1.0f, true)
+                                               : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x23, 1.0f, false);
+                    b01 = __builtin_bit_cast(uint32_t, p01);
+                    b23 = __builtin_bit_cast(uint32_t, p23);
                 } else {
                     const int w = nt >> 1;
                     if (nt & 1) {
