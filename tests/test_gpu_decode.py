@@ -196,3 +196,40 @@ def test_f32_gqa_groups(G):
     got, ref = run_both(4, lay, Hq=Hkv * G, Hkv=Hkv, D=128, Dv=64, q=q, kp=kp, vp=vp,
                         split_tokens=128)
     assert attn_err(got, ref) <= ATTN_TOL
+
+
+@pytest.mark.parametrize("Hkv", [1, 3, 5])
+@pytest.mark.parametrize("G", [1, 16])
+@pytest.mark.parametrize("kv", ["bf16/bf16", "fp8/bf16", "bf16/fp8", "bf16/tq3"])
+def test_kv_head_counts(Hkv, G, kv):
+    """One kv head (MQA) and odd counts, which pack one wavefront per
+    work-group, for every MFMA-path cache format."""
+    k_dt, v_dt = kv.split("/")
+    D = 128
+    lay = W.layout_for(2, [1, 40, 300, 1000])
+    rng = np.random.default_rng(Hkv * 100 + G)
+    shape = (lay.num_blocks, 16, Hkv, D)
+    kp = W.e4m3_codes(2, 40 + Hkv, shape) if k_dt == "fp8" else \
+        W.bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    if v_dt == "tq3":
+        vp = np.zeros((lay.num_blocks, oracle.tq_block_bytes(3, 16, Hkv, D)), np.uint8)
+        x = rng.standard_normal((lay.num_blocks * 16, Hkv, D)).astype(np.float32)
+        oracle.cache_write_v(x, "f32", np.arange(lay.num_blocks * 16, dtype=np.int64), vp,
+                             num_kv_heads=Hkv, head_dim_v=D, block_size=16, cache_dtype="tq3")
+    elif v_dt == "fp8":
+        vp = W.e4m3_codes(2, 50 + Hkv, shape)
+    else:
+        vp = W.bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    q = W.bf16_bits(rng.standard_normal((4, Hkv * G, D)).astype(np.float32))
+    ref = oracle.paged_decode(q, "bf16", kp, k_dt, vp, v_dt, lay.block_tables, lay.seq_lens,
+                              num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=D,
+                              block_size=16, scale=D ** -0.5, k_scale=0.5, v_scale=0.25,
+                              nthreads=8)
+    say(f"decode Hkv={Hkv} G={G} K={k_dt} V={v_dt}")
+    vdev = dev(vp, torch.uint8) if v_dt == "tq3" else dev(vp)
+    out = pkv.paged_decode_attn(dev(q), dev(kp), vdev, dev(lay.block_tables), dev(lay.seq_lens),
+                                scale=D ** -0.5, k_scale=0.5, v_scale=0.25, split_tokens=256,
+                                v_tq_bits=3 if v_dt == "tq3" else 0)
+    err = attn_err(host(out), ref)
+    say(f"  err {err:.3e}")
+    assert np.isfinite(host(out)).all() and err <= ATTN_TOL

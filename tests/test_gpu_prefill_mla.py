@@ -163,3 +163,13 @@ def test_mla_cache_assemble_bit_exact(dtype):
     pkv.mla_cache_assemble(latd[:, :lora], dev(kr), dev(slots), kc, vc, kv_lora=lora, rope=rope)
     assert host(kc).tobytes() == kref.tobytes()
     assert host(vc).tobytes() == vref.tobytes()
+
+
+@pytest.mark.parametrize("Hkv", [1, 3, 5])
+@pytest.mark.parametrize("G", [1, 8])
+def test_prefill_kv_head_counts(Hkv, G):
+    got, ref = _both([1, 40, 130], [1, 300, 700], Hq=Hkv * G, Hkv=Hkv, D=128, seed=Hkv + G,
+                     k_dt="fp8" if Hkv == 3 else "bf16", k_scale=0.5)
+    err = attn_err(got, ref)
+    say(f"  err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATTN_TOL
