@@ -2,14 +2,18 @@
  * pkv.h -- C ABI of libpkv: paged KV-cache write and paged decode attention
  * for AMD Instinct MI355X (gfx950).
  *
- * Four operations, each an asynchronous launch on a caller-given HIP stream:
+ * Six operations, each an asynchronous launch on a caller-given HIP stream:
  *
  *   pkv_fill_slots          slot mapping from per-sequence block tables
  *   pkv_cache_write_k_fused RMSNorm -> RoPE -> one rounding, into the K pool
- *   pkv_cache_write_v       V reshape-and-cache copy (or E4M3 store) into the V pool
+ *   pkv_cache_write_v       V reshape-and-cache copy (or E4M3 / TurboQuant-style
+ *                           b-bit store) into the V pool
  *   pkv_paged_decode_attn   one-query-token GQA attention through the tables
  *   pkv_paged_prefill_attn  causal attention of N new tokens per sequence
  *   pkv_mla_cache_assemble  MLA cache rows [latent | k_rope] -> K, [latent | 0] -> V
+ *
+ * and host-side queries: pkv_decode_workspace_bytes, pkv_v_block_bytes,
+ * pkv_tq_codebook, pkv_last_error, pkv_version.
  *
  * Sources (the pages this library implements):
  *   [p1] docs.atlasinference.io, spark_model/layers/ops/kv_cache.rs
@@ -264,7 +268,9 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *   q             in  [num_seqs, num_q_heads, head_dim_qk] of q_dtype; sequence
  *                     s starts at element s * q_seq_stride
  *   k_cache       in  [num_blocks, block_size, num_kv_heads, head_dim_qk] of k_dtype
- *   v_cache       in  [num_blocks, block_size, num_kv_heads, head_dim_v] of v_dtype
+ *   v_cache       in  [num_blocks, block_size, num_kv_heads, head_dim_v] of v_dtype;
+ *                     TQ: num_blocks blocks of pkv_v_block_bytes bytes, laid out
+ *                     as stated with pkv_dtype
  *   k_scale, v_scale  E4M3 caches only: per-tensor scales, finite and > 0
  *   block_tables  in  int32 [num_seqs, max_blocks_per_seq]
  *   seq_lens      in  int32 [num_seqs]; tokens past max_blocks_per_seq *
