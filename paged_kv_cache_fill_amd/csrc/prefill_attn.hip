@@ -337,6 +337,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
             }
             l[t] += psum;
         }
+        // the PV MFMAs at raised wave priority: they issue back to back while
+        // the SIMD's other wave (in its softmax) fills the VALU slots
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int j = 0; j < kPStep; ++j) {
             if (!blk_ok[j])
@@ -395,6 +398,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
                                                                        0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     if (nblk > blo) {
