@@ -4,6 +4,9 @@ A step is one decode step of the whole path over a full-size batch:
   fill_slots (one new token per sequence, position seq_len-1)
   -> fused K write (RMSNorm, RoPE, one rounding) -> V write
   -> paged decode attention over every sequence's whole history.
+The timed steps replay the step captured once in a HIP graph (the same five
+launches without the gaps between them; --no-graph times eager launches,
+and the eager step time is reported beside it).
 Before timing, the history of every sequence is written into the shuffled
 pools through the same write calls (the population write); that write is
 timed on its own and reported as the cache-write throughput.
@@ -73,6 +76,8 @@ def parse():
                    choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--split-tokens", type=int, default=0)
+    p.add_argument("--no-graph", action="store_true",
+                   help="time the decode step as eager launches instead of a HIP graph replay")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 2 GiB device copy (counter calibration)")
     return p.parse_args()
@@ -288,20 +293,39 @@ def main():
         step_writes()
         step_attn()
 
+    def timed(fn, k):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(k):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / k
+
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
+    ms_eager = timed(step, args.steps)
+    if args.no_graph:
+        ms_per_step = ms_eager
+    else:
+        # the step's five launches captured once and replayed (same work,
+        # without the launch gaps between the small write kernels)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        ms_per_step = timed(graph.replay, args.steps)
 
     # per-call HIP-event timings on the launch stream
     attn_ms = float(np.mean(time_call(step_attn, args.steps)))
     write_ms = float(np.mean(time_call(step_writes, args.steps)))
-    log(f"step {ms_per_step:.3f} ms (decode call {attn_ms:.3f} ms, step writes {write_ms * 1e3:.1f} us)")
+    log(f"step {ms_per_step:.3f} ms ({'eager' if args.no_graph else 'graph replay'}; eager "
+        f"{ms_eager:.3f} ms; decode call {attn_ms:.3f} ms, step writes {write_ms * 1e3:.1f} us)")
 
     dec_b = decode_bytes(lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, vb, 2,
                          window=window, sinks=use_sinks)
@@ -319,6 +343,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
+        "step_launch": "eager" if args.no_graph else "hip_graph",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
