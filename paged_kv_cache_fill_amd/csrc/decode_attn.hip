@@ -40,7 +40,7 @@ namespace pkv {
 constexpr uint32_t kKvPerGroup = 2;     // kv heads (waves) per work-group, at most
 constexpr int kPrefetch = 1;            // cache blocks loaded ahead of the one in use
 constexpr bool kKDirect = false;        // K loaded straight into the operand layout
-constexpr uint64_t kTargetGroups = 2048;// (sequence, split, kv group) work-groups wanted
+constexpr uint64_t kTargetGroups = 768; // (sequence, split, kv group) work-groups wanted
 constexpr uint32_t kMinChunk = 4;       // blocks per split, automatic choice: at least
 constexpr int kBtRegs = 2;              // table entries held per lane
 constexpr uint32_t kMaxChunk = 64 * kBtRegs;  // ... and at most (the table entries held)
@@ -843,6 +843,9 @@ static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_h
         const uint64_t want = units >= kTargetGroups ? 1 : (kTargetGroups + units - 1) / units;
         cb = ceil_div(max_blocks_per_seq, want);
         cb = cb < kMinChunk ? kMinChunk : cb;
+        // equal splits: as few as the chunk cap allows, then evenly sized
+        if (cb > kMaxChunk)
+            cb = ceil_div(max_blocks_per_seq, ceil_div(max_blocks_per_seq, kMaxChunk));
     }
     cb = cb < 1 ? 1 : cb > kMaxChunk ? kMaxChunk : cb;
     p.chunk_blocks = cb;
