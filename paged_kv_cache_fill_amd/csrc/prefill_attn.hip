@@ -7,17 +7,19 @@
 //
 // Work decomposition.  Rows of the score matrix are (query token, query
 // head) pairs of one kv head's GQA group, token-major (row = i * G + g).  A
-// work-group takes 64 consecutive rows of one (sequence, kv head), one
-// wavefront per 16 rows, and walks the keys [lo_min, end_max) of its rows in
-// steps of two cache blocks.  Each step's K and V blocks are loaded once per
-// work-group (one 16-byte chunk of each per thread and block), written to
-// LDS -- K in the swizzled MFMA operand layout of KFrag, V row-major with a
-// 16-byte pad per row -- and read by all four waves; the next step's loads
-// are in flight while the current one is computed (two LDS buffers, one
-// barrier per step).  Per wave and cache block:
-//   S^T[t, row] = K[t, :] . q[row, :]   v_mfma_f32_16x16x32_bf16 (M=t, N=row)
-//   O[row, d]  += P[row, t] V[t, d]     v_mfma_f32_16x16x32_bf16 with the
-//                                       hi and lo BF16 halves of P along k
+// work-group takes 128 consecutive rows of one (sequence, kv head), four
+// wavefronts of two 16-row tiles each, and walks the keys [lo_min, end_max)
+// of its rows in steps of two cache blocks.  Each step's K and V blocks are
+// loaded once per work-group (one 16-byte chunk of each per thread and
+// block), written to LDS -- K in the swizzled MFMA operand layout of KFrag, V
+// row-major with a 16-byte pad per row -- and read by all four waves; the
+// next step's loads are in flight while the current one is computed (two LDS
+// buffers, one barrier per step).  Per wave, step and row tile:
+//   S^T[t, row] = K[t, :] . q[row, :]   v_mfma_f32_16x16x32_bf16 (M=t, N=row),
+//                                       per block
+//   O[row, d]  += P[row, t] V[t, d]     v_mfma_f32_16x16x32_bf16 whose k spans
+//                                       the two blocks' keys, once with the hi
+//                                       and once with the lo BF16 halves of P
 // with the causal / window mask per row and online softmax in the log2
 // domain, as in decode.  All query tiles of one (sequence, kv head) are
 // dealt to the same XCD (work-group id % 8), so their repeated K/V reads
@@ -167,13 +169,14 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
     }
 
     f32x4 o[RT][NT];
-    float m[RT], l[RT];
+    float m[RT], l[RT], neg_m[RT];
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
             o[t][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         m[t] = -INFINITY;
+        neg_m[t] = 0.f;                                // -m, 0 while m is -inf
         l[t] = 0.f;
     }
 
@@ -236,13 +239,13 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
         lds_r[jj] = KF::lds_off(ln, KF::op_chunk(jj, kg));
     const uint32_t v_rd = KTILE + (4 * kg) * VROW + DPL * ln * VES;
 
+    static_assert(kPStep == 2, "a step is one pair of blocks along the PV k");
     auto compute_step = [&](int buf, uint32_t b0) {
         if (!wave_live)
             return;
-        f32x4 sacc[RT][kPStep];
-        bool blk_ok[kPStep], inner[kPStep];
+        bool blk_ok[2], inner[2];
 #pragma unroll
-        for (int j = 0; j < kPStep; ++j) {
+        for (int j = 0; j < 2; ++j) {
             const uint32_t b = b0 + j;
             const int32_t t0 = (int32_t)(b * kBS);
             const int32_t pb = block_id(b);
@@ -250,56 +253,67 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
                         t0 + kBS > w_lo;
             // a block wholly inside every row's [lo, end) needs no mask
             inner[j] = blk_ok[j] && t0 >= in_lo && t0 + kBS <= in_end;
+        }
+        // a step with no attended key leaves m, l and o as they are
+        if (!(blk_ok[0] | blk_ok[1]))
+            return;
+
+        // S^T = K q^T for both blocks and row tiles.  Both blocks are in LDS
+        // (an unmapped one was read from block 0), so the MFMAs run
+        // unconditionally; masking below drops the scores not attended.
+        f32x4 sacc[RT][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
 #pragma unroll
             for (int t = 0; t < RT; ++t)
                 sacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (blk_ok[j]) {
-                const uint8_t* kt = &lds[buf][j][0];
-                u32x4 kop[NL];
+            const uint8_t* kt = &lds[buf][j][0];
+            u32x4 kop[NL];
 #pragma unroll
-                for (int jj = 0; jj < NL; ++jj)
-                    kop[jj] = *(const u32x4*)(kt + lds_r[jj]);
+            for (int jj = 0; jj < NL; ++jj)
+                kop[jj] = *(const u32x4*)(kt + lds_r[jj]);
 #pragma unroll
-                for (int i = 0; i < NI; ++i) {
-                    const bf16x8 kf = KF::operand(kop, i);
+            for (int i = 0; i < NI; ++i) {
+                const bf16x8 kf = KF::operand(kop, i);
 #pragma unroll
-                    for (int t = 0; t < RT; ++t)
-                        sacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][i],
-                                                                             sacc[t][j], 0, 0, 0);
-                }
+                for (int t = 0; t < RT; ++t)
+                    sacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[t][i], sacc[t][j],
+                                                                         0, 0, 0);
             }
         }
-        // online softmax per row tile; lane's row ln of tile t, keys
-        // (b0 + j) * 16 + 4kg + r
-        bf16x8 a_p[RT][kPStep];
+
+        // online softmax, part 1, per row tile: masks, row max, rescale.  The
+        // lane holds row ln of tile t and keys (b0 + j) * 16 + 4kg + r; raw
+        // scores, masked ones -inf (the scale is applied inside the exponent's
+        // FMA and to the row max: scale > 0 keeps the order)
+        float sr[RT][2][4];
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
-            // raw scores, masked ones -inf; the scale is applied inside the
-            // exponent's FMA (and to the row max: scale > 0 keeps the order)
-            float sr[kPStep][4];
             float mx = -INFINITY;
 #pragma unroll
-            for (int j = 0; j < kPStep; ++j) {
+            for (int j = 0; j < 2; ++j) {
                 if (inner[j]) {                          // wave-uniform
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        sr[j][r] = sacc[t][j][r];
+                        sr[t][j][r] = sacc[t][j][r];
                 } else {
                     const int32_t tk = (int32_t)((b0 + j) * kBS) + 4 * kg;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         // bitwise &: no short-circuit control flow per element
                         const bool ok = blk_ok[j] & (tk + r >= lo_r[t]) & (tk + r < end_r[t]);
-                        sr[j][r] = ok ? sacc[t][j][r] : -INFINITY;
+                        sr[t][j][r] = ok ? sacc[t][j][r] : -INFINITY;
                     }
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    mx = fmaxf(mx, sr[j][r]);
+                    mx = fmaxf(mx, sr[t][j][r]);
             }
-            mx = row_max_xor16_32(mx) * a.qk_scale;
-            // m is the row's exponent reference (-inf until a key counts)
-            if (__builtin_amdgcn_ballot_w64(mx > m[t] + kLazyRescale)) {
+            // m is the row's exponent reference (-inf until a key counts).  A
+            // row's max passes m + kLazyRescale iff one of its 4 lanes' maxima
+            // does, so the cross-lane reduction runs only then
+            if (__builtin_amdgcn_ballot_w64(mx * a.qk_scale > m[t] + kLazyRescale)) {
+                mx = row_max_xor16_32(mx) * a.qk_scale;
                 // rows whose reference stays keep alpha = 1 (also when it is
                 // -inf: -inf - -inf would be NaN); a first reference gives 0
                 const bool move = mx > m[t] + kLazyRescale;
@@ -307,6 +321,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
                 const float alpha = move ? __builtin_amdgcn_exp2f(m[t] - m_new) : 1.f;
                 l[t] *= alpha;
                 m[t] = m_new;
+                neg_m[t] = m_new == -INFINITY ? 0.f : -m_new;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float ar = __shfl(alpha, 4 * kg + r, 64);
@@ -315,90 +330,127 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
                         o[t][nt][r] *= ar;
                 }
             }
-            const float neg_m = m[t] == -INFINITY ? 0.f : -m[t];
-            float psum = 0.f;
-#pragma unroll
-            for (int j = 0; j < kPStep; ++j) {
-                float p[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    p[r] = __builtin_amdgcn_exp2f(fmaf(sr[j][r], a.qk_scale, neg_m));
-                psum += (p[0] + p[1]) + (p[2] + p[3]);
-                // A operand: k = 8kg + 0..3 -> P_hi of keys 4kg + 0..3,
-                // k = 8kg + 4..7 -> P_lo
-                uint32_t ph[2], pl[2];
-#pragma unroll
-                for (int r2 = 0; r2 < 2; ++r2) {
-                    const uint32_t hw = pack_bf16(p[2 * r2], p[2 * r2 + 1]);
-                    ph[r2] = hw;
-                    pl[r2] = pack_bf16(p[2 * r2] - bf16_lo(hw), p[2 * r2 + 1] - bf16_hi(hw));
-                }
-                a_p[t][j] = __builtin_bit_cast(bf16x8, u32x4{ph[0], ph[1], pl[0], pl[1]});
-            }
-            l[t] += psum;
         }
-        // the PV MFMAs at raised wave priority: they issue back to back while
-        // the SIMD's other wave (in its softmax) fills the VALU slots
-        __builtin_amdgcn_s_setprio(1);
+
+        // V rows 4kg + r of both blocks.  In a block that is not interior,
+        // keys outside [w_lo, w_end) (past the sequence end, or in an unmapped
+        // block read from block 0) read as zero
+        uint32_t vr[2][4][VW];
 #pragma unroll
-        for (int j = 0; j < kPStep; ++j) {
-            if (!blk_ok[j])
-                continue;
-            // V rows 4kg + r of the block; keys outside [w_lo, w_end) read as
-            // zero (they may lie past the sequence end)
-            const uint8_t* vt = &lds[buf][j][0] + v_rd;
-            uint32_t vr[4][VW];
+        for (int h = 0; h < 2; ++h) {
+            const uint8_t* vt = &lds[buf][h][0] + v_rd;
+            if (inner[h]) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int32_t tk = (int32_t)((b0 + j) * kBS) + 4 * kg + r;
-                const bool keep = inner[j] | ((tk >= w_lo) & (tk < w_end));
-                if constexpr (VW == 4) {
-                    const u32x4 x = *(const u32x4*)(vt + r * VROW);
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (VW == 4) {
+                        const u32x4 x = *(const u32x4*)(vt + r * VROW);
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) vr[r][w] = keep ? x[w] : 0u;
-                } else if constexpr (VW == 2) {
-                    const u32x2 x = *(const u32x2*)(vt + r * VROW);
+                        for (int w = 0; w < 4; ++w) vr[h][r][w] = x[w];
+                    } else if constexpr (VW == 2) {
+                        const u32x2 x = *(const u32x2*)(vt + r * VROW);
 #pragma unroll
-                    for (int w = 0; w < 2; ++w) vr[r][w] = keep ? x[w] : 0u;
-                } else {
-                    const uint32_t x = *(const uint32_t*)(vt + r * VROW);
-                    vr[r][0] = keep ? x : 0u;
+                        for (int w = 0; w < 2; ++w) vr[h][r][w] = x[w];
+                    } else {
+                        vr[h][r][0] = *(const uint32_t*)(vt + r * VROW);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int32_t tk = (int32_t)((b0 + h) * kBS) + 4 * kg + r;
+                    const bool keep = blk_ok[h] & (tk >= w_lo) & (tk < w_end);
+                    if constexpr (VW == 4) {
+                        const u32x4 x = *(const u32x4*)(vt + r * VROW);
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) vr[h][r][w] = keep ? x[w] : 0u;
+                    } else if constexpr (VW == 2) {
+                        const u32x2 x = *(const u32x2*)(vt + r * VROW);
+#pragma unroll
+                        for (int w = 0; w < 2; ++w) vr[h][r][w] = keep ? x[w] : 0u;
+                    } else {
+                        const uint32_t x = *(const uint32_t*)(vt + r * VROW);
+                        vr[h][r][0] = keep ? x : 0u;
+                    }
                 }
             }
+        }
+
+        // B operand of column tile nt: k = 8kg + 0..3 -> keys 4kg + 0..3 of
+        // block 0, k = 8kg + 4..7 -> the same keys of block 1
+        auto v_operand = [&](int nt) -> bf16x8 {
+            uint32_t bw[4];
 #pragma unroll
-            for (int nt = 0; nt < NT; ++nt) {
-                uint32_t b01, b23;
+            for (int h = 0; h < 2; ++h) {
                 if constexpr (VT == 1) {
-                    // the two rows' codes of column nt side by side, then widened
-                    // exactly to a BF16 pair (v_cvt_scalef32_pk_bf16_fp8, scale 1)
+                    // the two rows' codes of column nt side by side, then
+                    // widened exactly to a BF16 pair (v_cvt_scalef32_pk_bf16_fp8,
+                    // scale 1)
                     const int w = nt / 4, e = nt % 4;
                     const uint32_t sel = e < 2 ? 0x05010400u : 0x07030602u;
-                    const uint32_t x01 = __builtin_amdgcn_perm(vr[1][w], vr[0][w], sel);
-                    const uint32_t x23 = __builtin_amdgcn_perm(vr[3][w], vr[2][w], sel);
+                    const uint32_t x01 = __builtin_amdgcn_perm(vr[h][1][w], vr[h][0][w], sel);
+                    const uint32_t x23 = __builtin_amdgcn_perm(vr[h][3][w], vr[h][2][w], sel);
                     const bf16x2 p01 = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x01, 1.0f, true)
                                                : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x01, 1.0f, false);
                     const bf16x2 p23 = (e & 1) ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x23, 1.0f, true)
                                                : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x23, 1.0f, false);
-                    b01 = __builtin_bit_cast(uint32_t, p01);
-                    b23 = __builtin_bit_cast(uint32_t, p23);
+                    bw[2 * h] = __builtin_bit_cast(uint32_t, p01);
+                    bw[2 * h + 1] = __builtin_bit_cast(uint32_t, p23);
                 } else {
                     const int w = nt >> 1;
                     if (nt & 1) {
-                        b01 = hi16_pair(vr[0][w], vr[1][w]);
-                        b23 = hi16_pair(vr[2][w], vr[3][w]);
+                        bw[2 * h] = hi16_pair(vr[h][0][w], vr[h][1][w]);
+                        bw[2 * h + 1] = hi16_pair(vr[h][2][w], vr[h][3][w]);
                     } else {
-                        b01 = lo16_pair(vr[0][w], vr[1][w]);
-                        b23 = lo16_pair(vr[2][w], vr[3][w]);
+                        bw[2 * h] = lo16_pair(vr[h][0][w], vr[h][1][w]);
+                        bw[2 * h + 1] = lo16_pair(vr[h][2][w], vr[h][3][w]);
                     }
                 }
-                const bf16x8 bv = __builtin_bit_cast(bf16x8, u32x4{b01, b23, b01, b23});
+            }
+            return __builtin_bit_cast(bf16x8, u32x4{bw[0], bw[1], bw[2], bw[3]});
+        };
+        // P of tile t: weights 2^(s * scale - m), their sum, and the A operands
+        // (k as for V) of their hi and lo BF16 halves
+        auto p_operands = [&](int t, bf16x8& a_hi, bf16x8& a_lo) {
+            uint32_t ph[2][2], pl[2][2];
+            float psum;
 #pragma unroll
-                for (int t = 0; t < RT; ++t)
-                    o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_p[t][j], bv, o[t][nt], 0,
-                                                                       0, 0);
+            for (int j = 0; j < 2; ++j) {
+                float p[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    p[r] = __builtin_amdgcn_exp2f(fmaf(sr[t][j][r], a.qk_scale, neg_m[t]));
+                const float bsum = (p[0] + p[1]) + (p[2] + p[3]);
+                psum = j == 0 ? bsum : psum + bsum;
+#pragma unroll
+                for (int r2 = 0; r2 < 2; ++r2) {
+                    uint32_t hw = pack_bf16(p[2 * r2], p[2 * r2 + 1]);
+                    // an empty asm hides hw's origin, so the low half below is
+                    // hw << 16 rather than a second conversion of p[2 * r2]
+                    asm("" : "+v"(hw));
+                    ph[j][r2] = hw;
+                    pl[j][r2] = pack_bf16(p[2 * r2] - bf16_lo(hw), p[2 * r2 + 1] - bf16_hi(hw));
+                }
+            }
+            l[t] += psum;
+            a_hi = __builtin_bit_cast(bf16x8, u32x4{ph[0][0], ph[0][1], ph[1][0], ph[1][1]});
+            a_lo = __builtin_bit_cast(bf16x8, u32x4{pl[0][0], pl[0][1], pl[1][0], pl[1][1]});
+        };
+        bf16x8 bv[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+            bv[nt] = v_operand(nt);
+        bf16x8 a_hi[RT], a_lo[RT];
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+            p_operands(t, a_hi[t], a_lo[t]);
+#pragma unroll
+        for (int t = 0; t < RT; ++t) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi[t], bv[nt], o[t][nt], 0, 0, 0);
+                o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[t], bv[nt], o[t][nt], 0, 0, 0);
             }
         }
-        __builtin_amdgcn_s_setprio(0);
     };
 
     if (nblk > blo) {
