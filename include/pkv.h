@@ -272,6 +272,8 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *                     TQ: num_blocks blocks of pkv_v_block_bytes bytes, laid out
  *                     as stated with pkv_dtype
  *   k_scale, v_scale  E4M3 caches only: per-tensor scales, finite and > 0
+ *   scale             softmax scale of the scores, finite and > 0 (else
+ *                     PKV_ERR_INVALID)
  *   block_tables  in  int32 [num_seqs, max_blocks_per_seq]
  *   seq_lens      in  int32 [num_seqs]; tokens past max_blocks_per_seq *
  *                     block_size are excluded

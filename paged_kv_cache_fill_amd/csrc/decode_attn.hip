@@ -508,15 +508,22 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         for (int i = 0; i < NI; ++i)
             sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(KF::operand(kop, i), qf[i], sacc, 0, 0, 0);
 
+        // scaled scores, masked ones -inf (a block wholly inside the range
+        // needs no mask)
         float sv[4];
-        float mx = -INFINITY;
+        if (ntok == kBS && tlo <= 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int t = row_token(4 * kg + r);
-            sv[r] = (t < ntok && t >= tlo) ? sacc[r] * a.qk_scale : -INFINITY;
-            mx = fmaxf(mx, sv[r]);
+            for (int r = 0; r < 4; ++r)
+                sv[r] = sacc[r] * a.qk_scale;
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = row_token(4 * kg + r);
+                sv[r] = (t < ntok && t >= tlo) ? sacc[r] * a.qk_scale : -INFINITY;
+            }
         }
-        mx = wave_max_xor16_32(mx);
+        float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+        mx = row_max_xor16_32(mx);
         const float m_new = fmaxf(m, mx);
         // while no token has counted yet (m_new = -inf) use 0 as the reference:
         // masked scores give p = 0, and alpha = 0 leaves the zero state zero
@@ -527,10 +534,16 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         // divides it out
         constexpr bool F16PV = TQ || VT == 1;
         constexpr float kPOff = F16PV ? 15.f : 0.f;
+        // the exponent is the difference of the rounded scaled score and the
+        // reference, never an FMA of the raw score: with kPOff = 0 the row's
+        // largest score gives exactly 1 (one attended token returns its V row)
         float p[4];
+        {
+#pragma clang fp contract(off)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            p[r] = __builtin_amdgcn_exp2f(sv[r] - (m_ref - kPOff));
+            for (int r = 0; r < 4; ++r)
+                p[r] = __builtin_amdgcn_exp2f(sv[r] - (m_ref - kPOff));
+        }
         const float psum = (p[0] + p[1]) + (p[2] + p[3]);
         l = F16PV ? __builtin_fmaf(psum, 1.f / 32768.f, l * alpha) : l * alpha + psum;
         m = m_new;
@@ -913,6 +926,8 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     if ((q_seq_stride * dtype_size(q_dtype)) % 16 || !aligned16(q) || !aligned16(k_cache) ||
         !aligned16(v_cache) || !aligned16(out) || (gate && !aligned16(gate)))
         return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: pointers and q stride must be 16-byte aligned");
+    if (!(scale > 0.0f && scale < INFINITY))
+        return fail(PKV_ERR_INVALID, "paged_decode_attn: scale must be finite and > 0");
     if (k_dtype == PKV_FP8_E4M3 && !(k_scale > 0.0f && k_scale < INFINITY))
         return fail(PKV_ERR_INVALID, "paged_decode_attn: k_scale must be finite and > 0");
     if (v_dtype == PKV_FP8_E4M3 && !(v_scale > 0.0f && v_scale < INFINITY))

@@ -543,6 +543,8 @@ extern "C" int pkv_paged_prefill_attn(const void* q, pkv_dtype q_dtype, uint64_t
     if ((q_token_stride * 2) % 16 || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
         !aligned16(out))
         return fail(PKV_ERR_UNSUPPORTED, "paged_prefill_attn: pointers and q stride must be 16-byte aligned");
+    if (!(scale > 0.0f && scale < INFINITY))
+        return fail(PKV_ERR_INVALID, "paged_prefill_attn: scale must be finite and > 0");
     if (k_dtype == PKV_FP8_E4M3 && !(k_scale > 0.0f && k_scale < INFINITY))
         return fail(PKV_ERR_INVALID, "paged_prefill_attn: k_scale must be finite and > 0");
     if (v_dtype == PKV_FP8_E4M3 && !(v_scale > 0.0f && v_scale < INFINITY))

@@ -129,6 +129,9 @@ def test_decode_validation(lib):
     assert call(M=512, wsb=16) == -3              # workspace too small
     assert "workspace" in _err(lib)
     assert call(qs=100) == -1                     # q stride smaller than a row
+    for bad in (0.0, -0.1, float("nan"), float("inf")):
+        assert call(scale=bad) == -1              # softmax scale finite and > 0
+    assert "scale" in _err(lib)
 
 
 def test_workspace_query(lib):
@@ -162,6 +165,7 @@ def test_prefill_and_mla_validation(lib):
     assert pre(kd=1, ks=0.0) == -1
     assert pre(vd=1, vs=float("nan")) == -1
     assert pre(qs=100) == -1
+    assert pre(scale=-0.5) == -1 and pre(scale=0.0) == -1
     assert pre(B=32) == -2
     assert _err(lib) != ""
 
