@@ -284,8 +284,44 @@ __global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(
         }
         __builtin_amdgcn_wave_barrier();
 
-        if (row_ok) {
-            const uint64_t dst = ((uint64_t)slot * a.Hkv + h) * a.D;
+        const uint64_t dst = ((uint64_t)slot * a.Hkv + h) * a.D;
+        if constexpr (OUT == OUT_FP8 && IN == IN_BF16 && NC % 2 == 0) {
+            // An E4M3 chunk is 8 bytes, so storing chunks in place would write
+            // each row in half-line pieces.  Instead the row's lanes exchange
+            // codes so that lane j stores 16-byte pieces P = j + L p (chunks
+            // 2P and 2P + 1) and one store instruction covers whole rows.
+            // Chunk c sits in lane c mod L, slot c / L; for L >= 2 both
+            // chunks of piece P come from lanes 2j mod L and 2j mod L + 1,
+            // slot 2p + (2j >= L).  Every lane takes part in the exchange.
+            u32x2 c[NC];
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+                c[k] = u32x2{e4m3_sat_x4(y[k][0], y[k][1], y[k][2], y[k][3]),
+                             e4m3_sat_x4(y[k][4], y[k][5], y[k][6], y[k][7])};
+            const int src0 = (int)(lane - lir + ((2 * lir) & (a.L - 1)));
+            const int src1 = a.L > 1 ? src0 + 1 : src0;
+            const bool upper = 2 * lir >= a.L;
+            uint8_t* base = (uint8_t*)a.k_cache + dst;
+#pragma unroll
+            for (int p = 0; p < NC / 2; ++p) {
+                u32x4 v;
+                if (a.L == 1) {
+                    v = u32x4{c[2 * p][0], c[2 * p][1], c[2 * p + 1][0], c[2 * p + 1][1]};
+                } else {
+                    const uint32_t a0 = __shfl(c[2 * p][0], src0, 64);
+                    const uint32_t a1 = __shfl(c[2 * p][1], src0, 64);
+                    const uint32_t a2 = __shfl(c[2 * p][0], src1, 64);
+                    const uint32_t a3 = __shfl(c[2 * p][1], src1, 64);
+                    const uint32_t b0 = __shfl(c[2 * p + 1][0], src0, 64);
+                    const uint32_t b1 = __shfl(c[2 * p + 1][1], src0, 64);
+                    const uint32_t b2 = __shfl(c[2 * p + 1][0], src1, 64);
+                    const uint32_t b3 = __shfl(c[2 * p + 1][1], src1, 64);
+                    v = upper ? u32x4{b0, b1, b2, b3} : u32x4{a0, a1, a2, a3};
+                }
+                if (row_ok)
+                    store_nt((u32x4*)(base + (uint64_t)(lir + a.L * p) * 16), v);
+            }
+        } else if (row_ok) {
 #pragma unroll
             for (int k = 0; k < NC; ++k)
                 store_chunk<OUT, VEC>(a.k_cache, dst + (uint64_t)(lir + a.L * k) * VEC, y[k]);
