@@ -793,33 +793,77 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
 
 // ------------------------------------------------------------------ merge
 
-// One work-group per (sequence, query head) with more than one split:
+// One wavefront per (sequence, query head) with more than one split, four
+// query heads per work-group:
 //   M = max_i m_i, w_i = 2^(m_i - M), out = sum_i w_i o_i / sum_i w_i l_i.
-__global__ __launch_bounds__(128) void decode_merge_kernel(DecodeArgs a, uint32_t Dv)
+// Lane i holds split i's (m, l) (64 splits per pass); each lane accumulates
+// its DPL = Dv / 64 output columns over the splits in order.  An empty split
+// (m = -inf, o = 0) gets weight 0; with every split empty the reference is 0
+// instead of M, so no weight is NaN and the row stays zero.
+constexpr uint32_t kMergeHeads = 4;
+template <int DPL>
+__global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeArgs a)
 {
-    const uint32_t s = blockIdx.x, h = blockIdx.y;
+    constexpr uint32_t DV = 64 * DPL;
+    const uint32_t s = blockIdx.x;
+    const uint32_t h = blockIdx.y * kMergeHeads + (threadIdx.x >> 6);
+    const uint32_t lane = threadIdx.x & 63;
+    if (h >= a.Hq)
+        return;
     const uint32_t nsplit = seq_range(a, s).nsplit;
     if (nsplit <= 1)
         return;
-    const uint64_t prow0 = ((uint64_t)s * a.max_splits) * a.Hq + h;
-    float M = -INFINITY;
-    for (uint32_t i = 0; i < nsplit; ++i)
-        M = fmaxf(M, a.part_ml[(prow0 + (uint64_t)i * a.Hq) * 2]);
-    for (uint32_t d = threadIdx.x; d < Dv; d += blockDim.x) {
-        float L = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
-            for (uint32_t i = 0; i < nsplit; ++i) {
-                const uint64_t prow = prow0 + (uint64_t)i * a.Hq;
-                const float w = __builtin_amdgcn_exp2f(a.part_ml[prow * 2] - M);
-                L += w * a.part_ml[prow * 2 + 1];
-                acc += w * a.part_o[prow * Dv + d];
+    const uint64_t prow0 = (uint64_t)s * a.max_splits * a.Hq + h;
+    auto ml_of = [&](uint32_t i) {
+        return *(const f32x2*)(a.part_ml + (prow0 + (uint64_t)i * a.Hq) * 2);
+    };
+    const uint64_t oi = ((uint64_t)s * a.Hq + h) * DV + lane * DPL;
+    float g[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+        g[k] = a.gate ? a.gate[oi + k] : 1.f;
+
+    const f32x2 ml0 = lane < nsplit ? ml_of(lane) : f32x2{-INFINITY, 0.f};
+    float M = ml0[0];
+    for (uint32_t i = lane + 64; i < nsplit; i += 64)
+        M = fmaxf(M, ml_of(i)[0]);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1)
+        M = fmaxf(M, __shfl_xor(M, d, 64));
+    const float Mref = M == -INFINITY ? 0.f : M;
+
+    float L = 0.f;
+    float acc[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k)
+        acc[k] = 0.f;
+    for (uint32_t i0 = 0; i0 < nsplit; i0 += 64) {
+        const f32x2 ml = i0 == 0 ? ml0
+                                 : (i0 + lane < nsplit ? ml_of(i0 + lane) : f32x2{-INFINITY, 0.f});
+        const float w = __builtin_amdgcn_exp2f(ml[0] - Mref);
+        L = __builtin_fmaf(w, ml[1], L);
+        const uint32_t n = nsplit - i0 < 64u ? nsplit - i0 : 64u;
+#pragma unroll 4
+        for (uint32_t j = 0; j < n; ++j) {
+            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (int)j));
+            const float* orow = a.part_o + (prow0 + (uint64_t)(i0 + j) * a.Hq) * DV + lane * DPL;
+            if constexpr (DPL == 2) {
+                const f32x2 o = *(const f32x2*)orow;
+                acc[0] = __builtin_fmaf(wj, o[0], acc[0]);
+                acc[1] = __builtin_fmaf(wj, o[1], acc[1]);
+            } else {
+                acc[0] = __builtin_fmaf(wj, orow[0], acc[0]);
             }
         }
-        float v = acc * norm_factor(M, L, a.sinks, h, a.out_scale);
-        const uint64_t oi = ((uint64_t)s * a.Hq + h) * Dv + d;
-        if (a.gate)
-            v *= a.gate[oi];
-        a.out[oi] = v;
+    }
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1)
+        L += __shfl_xor(L, d, 64);
+    const float inv = norm_factor(M, L, a.sinks, h, a.out_scale);
+    if constexpr (DPL == 2) {
+        *(f32x2*)(a.out + oi) = f32x2{acc[0] * inv * g[0], acc[1] * inv * g[1]};
+    } else {
+        a.out[oi] = acc[0] * inv * g[0];
     }
 }
 
@@ -1028,8 +1072,11 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     if (rc)
         return rc;
     if (plan.max_splits > 1) {
-        hipLaunchKernelGGL(decode_merge_kernel, dim3(num_seqs, num_q_heads), dim3(128), 0, st, a,
-                           head_dim_v);
+        const dim3 mgrid(num_seqs, ceil_div(num_q_heads, kMergeHeads));
+        if (head_dim_v == 128)
+            hipLaunchKernelGGL(decode_merge_kernel<2>, mgrid, dim3(64 * kMergeHeads), 0, st, a);
+        else
+            hipLaunchKernelGGL(decode_merge_kernel<1>, mgrid, dim3(64 * kMergeHeads), 0, st, a);
         rc = check_launch("paged_decode_attn merge");
     }
     return rc;
