@@ -294,7 +294,10 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *   head_dim_qk in {64, 128, 192, 256}, head_dim_v in {64, 128} (BF16/E4M3
  *   caches: head_dim_qk == head_dim_v in {64, 128}, GQA group <= 16; FP32:
  *   group 1, 2, 4 or 8); q_rope (FP32 only) with q_rope_dim even and
- *   q_rope_offset + q_rope_dim <= head_dim_qk.
+ *   q_rope_offset + q_rope_dim <= head_dim_qk.  At most 65535 split-K pieces
+ *   per sequence (a larger split_tokens lowers the count), at most 65535
+ *   sequences per call with FP32 caches, and num_seqs * num_kv_heads below
+ *   2^31 otherwise; beyond these PKV_ERR_UNSUPPORTED.
  */
 int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
                           const void* k_cache, pkv_dtype k_dtype, float k_scale,

@@ -1001,6 +1001,15 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
                     plan.workspace, workspace_bytes);
     if (plan.workspace > 0 && !aligned16(workspace))
         return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: workspace must be 16-byte aligned");
+    // the split index is a grid dimension (y, or z on the FP32 path, which
+    // also puts the sequence in y): both are limited to 65535
+    if (plan.max_splits > 65535u)
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: %u splits per sequence (limit 65535); use a larger split_tokens",
+                    plan.max_splits);
+    if (!mfma_path && num_seqs > 65535u)
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: FP32 caches support at most 65535 sequences per call");
+    if (mfma_path && (uint64_t)num_seqs * num_kv_heads > 0x7FFFFFFFull)
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: too many sequences for one call");
 
     DecodeArgs a{};
     a.q = q;

@@ -132,6 +132,13 @@ def test_decode_validation(lib):
     for bad in (0.0, -0.1, float("nan"), float("inf")):
         assert call(scale=bad) == -1              # softmax scale finite and > 0
     assert "scale" in _err(lib)
+    # the split index is a grid dimension: at most 65535 splits per sequence
+    assert call(M=70000, split=16, wsb=1 << 40) == -2
+    assert "splits" in _err(lib)
+    # FP32 caches put the sequence in a grid dimension too
+    f32 = dict(qd=2, kd=2, vd=2, Hq=8, Hkv=8, qs=8 * 128)
+    assert call(S=70000, **f32) == -2
+    assert "65535 sequences" in _err(lib)
 
 
 def test_workspace_query(lib):
