@@ -843,7 +843,6 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeAr
         const float w = __builtin_amdgcn_exp2f(ml[0] - Mref);
         L = __builtin_fmaf(w, ml[1], L);
         const uint32_t n = nsplit - i0 < 64u ? nsplit - i0 : 64u;
-#pragma unroll 4
         for (uint32_t j = 0; j < n; ++j) {
             const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (int)j));
             const float* orow = a.part_o + (prow0 + (uint64_t)(i0 + j) * a.Hq) * DV + lane * DPL;
