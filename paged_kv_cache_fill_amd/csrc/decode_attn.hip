@@ -8,9 +8,11 @@
 // [n - W, n) for a window of W tokens (W = 0: all of it); a sink adds
 // exp(sink) to the softmax denominator of its query head.
 //
-// Work decomposition.  A work-group handles one (sequence, split) pair for
-// a group of kv heads, one wavefront per kv head; a split is `chunk_blocks`
-// consecutive cache blocks of the sequence.  The work-group's waves read
+// Work decomposition.  A work-group handles a piece of work for a group of
+// kv heads, one wavefront per kv head: either one (sequence, split) pair, a
+// split being `chunk_blocks` consecutive cache blocks of the sequence, or
+// (balanced plan) an equal range of the batch's attended blocks taken in
+// sequence order, which may hold pieces of several sequences.  The work-group's waves read
 // neighbouring rows of the same pool blocks, so together they stream whole
 // blocks ([block_size, Hkv, D] is contiguous).  Every query head of a kv
 // head's GQA group is served by the same wave from the same K/V registers:
@@ -42,8 +44,10 @@ constexpr int kPrefetch = 1;            // cache blocks loaded ahead of the one 
 constexpr bool kKDirect = false;        // K loaded straight into the operand layout
 constexpr uint64_t kTargetGroups = 768; // (sequence, split, kv group) work-groups wanted
 constexpr uint32_t kMinChunk = 4;       // blocks per split, automatic choice: at least
-constexpr int kBtRegs = 2;              // table entries held per lane
-constexpr uint32_t kMaxChunk = 64 * kBtRegs;  // ... and at most (the table entries held)
+constexpr int kBtRegs = 2;              // table entries held per lane (split mode)
+constexpr uint32_t kMaxChunk = 64 * kBtRegs;  // ... so at most this many blocks per split
+constexpr int kBtRegsBal = 4;           // table entries held per lane (balanced mode)
+constexpr uint32_t kMaxRange = 64 * kBtRegsBal;  // ... so at most this many blocks per range
 
 struct DecodeArgs {
     const void* q;
@@ -54,14 +58,16 @@ struct DecodeArgs {
     const float* gate;
     const float* sinks;     // [Hq] logits, or NULL
     float* out;
-    float* part_o;          // [S][max_splits][Hq][Dv]
-    float* part_ml;         // [S][max_splits][Hq][2]  (max in log2 units, sum)
+    float* part_o;          // [rows][Hq][Dv]; rows = S * max_splits, or ranges + S
+    float* part_ml;         // [rows][Hq][2]  (max in log2 units, sum)
     uint64_t q_stride;      // elements between sequences
     uint32_t M;             // max_blocks_per_seq
     uint32_t num_blocks;
     uint32_t Hq, Hkv, G;
     uint32_t chunk_blocks;
     uint32_t max_splits;
+    uint32_t S;             // sequences
+    uint32_t ranges;        // balanced mode: block ranges per kv group (0 = split mode)
     float qk_scale;         // scale * log2(e) (* k_scale for E4M3 K)
     float out_scale;        // output factor: v_scale (E4M3 V), 2^-15 for FP16 weights
     uint32_t window;        // sliding window in tokens, 0 = none
@@ -103,11 +109,54 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeArgs& a, uint32_t s)
     return r;
 }
 
-// Writes the finished (single-split) or partial result of one wave.
+// Attended blocks of sequence s.
+__device__ __forceinline__ uint32_t att_blocks(const DecodeArgs& a, uint32_t s)
+{
+    const SeqRange r = seq_range(a, s);
+    return r.nblk > r.blo ? r.nblk - r.blo : 0u;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1)
+        v += __shfl_xor(v, d, 64);
+    return v;
+}
+
+// Balanced mode.  The attended blocks of all sequences, in sequence order,
+// form one list of T blocks; range w of every kv group is the list's blocks
+// [w C, (w + 1) C), C = ceil(T / ranges) <= 128 (the host sizes `ranges` from
+// an upper bound of T).  A sequence whose blocks lie in one range is finished
+// by that range's work-group; otherwise each range writes a partial row for
+// it at slot w + s (unique: every slot step is a range or a sequence start),
+// and the merge combines slots first + s .. last + s.  T and the prefix sums
+// are recomputed by every wave from seq_lens (at most 1024 sequences).
+__device__ __forceinline__ uint32_t range_blocks(uint32_t T, uint32_t ranges)
+{
+    const uint32_t c = T == 0 ? 1u : (T + ranges - 1) / ranges;
+    return c < kMaxRange ? c : kMaxRange;
+}
+
+// Total attended blocks T and the blocks before sequence `upto` (all lanes).
+__device__ __forceinline__ void scan_blocks(const DecodeArgs& a, uint32_t upto, int lane,
+                                            uint32_t& T, uint32_t& before)
+{
+    T = 0;
+    before = 0;
+    for (uint32_t c = 0; c < a.S; c += 64) {
+        const uint32_t s = c + (uint32_t)lane;
+        const uint32_t nb = s < a.S ? att_blocks(a, s) : 0u;
+        T += wave_sum_u32(nb);
+        before += wave_sum_u32(s < upto ? nb : 0u);
+    }
+}
+
+// Writes the finished or partial result of one wave.
 // o[nt][r]: row g = 4*(lane/16) + r of the GQA group, column d = DPL*(lane%16) + nt.
 template <int DV>
 __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint32_t kvh,
-                                          uint32_t split, uint32_t nsplit, int lane,
+                                          bool direct, uint64_t prow_base, int lane,
                                           const f32x4 (&o)[DV / 16], float m, float l)
 {
     constexpr int NT = DV / 16, DPL = DV / 16;
@@ -121,7 +170,7 @@ __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint3
             continue;
         const uint32_t h = kvh * a.G + g;
         float vals[NT];
-        if (nsplit == 1) {
+        if (direct) {
             const float inv = norm_factor(mg, lg, a.sinks, h, a.out_scale);
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt)
@@ -136,7 +185,7 @@ __device__ __forceinline__ void emit_mfma(const DecodeArgs& a, uint32_t s, uint3
             for (int nt = 0; nt < NT; nt += 4)
                 *(f32x4*)(a.out + base + nt) = f32x4{vals[nt], vals[nt + 1], vals[nt + 2], vals[nt + 3]};
         } else {
-            const uint64_t prow = ((uint64_t)s * a.max_splits + split) * a.Hq + h;
+            const uint64_t prow = prow_base + h;
             const uint64_t base = prow * DV + (uint64_t)DPL * n;
 #pragma unroll
             for (int nt = 0; nt < NT; nt += 4)
@@ -287,7 +336,7 @@ __device__ __forceinline__ void e4m3_pv(const float (&p)[4], const uint32_t (&v)
 // TurboQuant-style V with that many bits per code (D = 128).  D: head dim
 // of q, K and V (64 or 128).  The K operand layout is KFrag (attn_common.h).
 //
-template <int KT, int VT, int D, int PF>
+template <int KT, int VT, int D, int PF, bool BAL>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t kv_groups)
 {
     using KF = KFrag<KT, D>;
@@ -318,25 +367,16 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     // the XCDs (a sequence-major order would pile the always-present early
     // splits onto the same XCDs).  The kv groups of one (sequence, split) are
     // neighbours, so they stream the same cache blocks at about the same time.
-    const uint32_t split = blockIdx.y;
-    const uint32_t s = blockIdx.x / kv_groups;
     const uint32_t kvh = (blockIdx.x % kv_groups) * (blockDim.x >> 6) + wave;
     if (kvh >= a.Hkv)
         return;
 
-    const SeqRange R = seq_range(a, s);
+    // One piece of work: cache blocks [b0, b1) of sequence s (at most
+    // kMaxRange of them), finished (direct) or written as partial rows
+    // prow_base + query head.
+    auto run = [&](uint32_t s, const SeqRange& R, uint32_t b0, uint32_t b1, bool direct,
+                   uint64_t prow_base) {
     const int32_t n = R.n;
-    const uint32_t nsplit = R.nsplit;
-    const uint32_t b0 = R.blo + split * a.chunk_blocks;
-    if (split >= nsplit) {
-        if (nsplit == 0 && split == 0) {
-            // nothing attended: zero output rows of this kv head's group
-            for (uint32_t idx = lane; idx < a.G * D; idx += 64)
-                a.out[((uint64_t)s * a.Hq + kvh * a.G) * D + idx] = 0.f;
-        }
-        return;
-    }
-    const uint32_t b1 = min(b0 + a.chunk_blocks, R.nblk);
 
     // q fragments: B operand of S^T = K q^T; lane (g = ln, kg)
     bf16x8 qf[NI];
@@ -356,16 +396,17 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     // block-table entries of this split, kBtRegs per lane (chunk_blocks <=
     // 64 kBtRegs): entry i is lane i % 64 of bt_lane[i / 64]; lanes past the
     // split re-read its last entry, so the loads are unconditional
-    int32_t bt_lane[kBtRegs];
+    constexpr int NBT = BAL ? kBtRegsBal : kBtRegs;
+    int32_t bt_lane[NBT];
 #pragma unroll
-    for (int h = 0; h < kBtRegs; ++h) {
+    for (int h = 0; h < NBT; ++h) {
         const uint32_t idx = b0 + 64 * h + lane;
         bt_lane[h] = a.bt[(uint64_t)s * a.M + (idx < b1 ? idx : b1 - 1)];
     }
     auto table_entry = [&](uint32_t i) -> int32_t {
         int32_t r = bt_lane[0];
 #pragma unroll
-        for (int h = 1; h < kBtRegs; ++h)
+        for (int h = 1; h < NBT; ++h)
             r = i >= 64u * h ? bt_lane[h] : r;          // wave-uniform choice
         return __builtin_amdgcn_readlane(r, (int)(i & 63));
     };
@@ -634,7 +675,89 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     }
 
     l = wave_sum_xor16_32(l);
-    emit_mfma<D>(a, s, kvh, split, nsplit, lane, o, m, l);
+    emit_mfma<D>(a, s, kvh, direct, prow_base, lane, o, m, l);
+    };
+
+    // The work-group's pieces: one (sequence, split) in split mode; in
+    // balanced mode the pieces of range w of the flattened block list (see
+    // range_blocks), sequence by sequence.  One call site of run.
+    constexpr bool balanced = BAL;
+    const uint32_t w = blockIdx.x / kv_groups;
+    uint32_t s = w, cu = 0, r0 = 0, r1 = 0, C = 1;
+    if constexpr (balanced) {
+        uint32_t T, unused;
+        scan_blocks(a, 0u, lane, T, unused);
+        C = range_blocks(T, a.ranges);
+        r0 = w * C;
+        if (r0 >= T)
+            return;
+        r1 = r0 + C < T ? r0 + C : T;
+        // first sequence whose blocks reach past r0, and where its blocks start
+        s = 0;
+        uint32_t base = 0;
+        for (uint32_t c = 0; c < a.S; c += 64) {
+            const uint32_t si = c + (uint32_t)lane;
+            const uint32_t nb = si < a.S ? att_blocks(a, si) : 0u;
+            uint32_t incl = nb;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t t = __shfl_up(incl, d, 64);
+                if (lane >= d)
+                    incl += t;
+            }
+            incl += base;
+            const uint64_t hit = __builtin_amdgcn_ballot_w64(si < a.S && incl > r0);
+            if (hit) {
+                const int l0 = __builtin_ctzll(hit);
+                s = c + (uint32_t)l0;
+                cu = __builtin_amdgcn_readlane(incl - nb, l0);
+                break;
+            }
+            base = __builtin_amdgcn_readlane(incl, 63);
+        }
+    }
+    const uint32_t split = blockIdx.y;
+    for (;;) {
+        if (balanced && (s >= a.S || cu >= r1))
+            break;
+        const SeqRange R = seq_range(a, s);
+        uint32_t b0, b1, nb = 0;
+        bool direct;
+        uint64_t prow_base;
+        if constexpr (balanced) {
+            nb = R.nblk > R.blo ? R.nblk - R.blo : 0u;
+            const uint32_t lo = r0 > cu ? r0 : cu;
+            const uint32_t hi = cu + nb < r1 ? cu + nb : r1;
+            if (hi <= lo) {
+                cu += nb;
+                ++s;
+                continue;
+            }
+            b0 = R.blo + (lo - cu);
+            b1 = R.blo + (hi - cu);
+            direct = cu / C == (cu + nb - 1) / C;
+            prow_base = (uint64_t)(w + s) * a.Hq;
+        } else {
+            // split y of sequence s covers chunk_blocks blocks from R.blo
+            if (split >= R.nsplit) {
+                if (R.nsplit == 0 && split == 0) {
+                    // nothing attended: zero output rows of this kv head's group
+                    for (uint32_t idx = lane; idx < a.G * D; idx += 64)
+                        a.out[((uint64_t)s * a.Hq + kvh * a.G) * D + idx] = 0.f;
+                }
+                return;
+            }
+            b0 = R.blo + split * a.chunk_blocks;
+            b1 = min(b0 + a.chunk_blocks, R.nblk);
+            direct = R.nsplit == 1;
+            prow_base = ((uint64_t)s * a.max_splits + split) * a.Hq;
+        }
+        run(s, R, b0, b1, direct, prow_base);
+        if (!balanced)
+            break;
+        cu += nb;
+        ++s;
+    }
 }
 
 // ------------------------------------------------------------------ FP32 path
@@ -810,14 +933,36 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeAr
     const uint32_t lane = threadIdx.x & 63;
     if (h >= a.Hq)
         return;
-    const uint32_t nsplit = seq_range(a, s).nsplit;
+    uint32_t nsplit;
+    uint64_t prow0;
+    const uint64_t oi = ((uint64_t)s * a.Hq + h) * DV + lane * DPL;
+    if (a.ranges) {
+        // balanced mode: the pieces of s are ranges first .. last, at slots w + s
+        uint32_t T, cu;
+        scan_blocks(a, s, lane, T, cu);
+        const uint32_t nb = att_blocks(a, s);
+        if (nb == 0) {
+            // nothing attended: a zero row (no range wrote it)
+#pragma unroll
+            for (int k = 0; k < DPL; ++k)
+                a.out[oi + k] = 0.f;
+            return;
+        }
+        const uint32_t C = range_blocks(T, a.ranges);
+        const uint32_t first = cu / C;
+        uint32_t last = (cu + nb - 1) / C;
+        last = last < a.ranges ? last : a.ranges - 1;   // always true for a consistent plan
+        nsplit = first <= last ? last - first + 1 : 0u;
+        prow0 = (uint64_t)(first + s) * a.Hq + h;
+    } else {
+        nsplit = seq_range(a, s).nsplit;
+        prow0 = (uint64_t)s * a.max_splits * a.Hq + h;
+    }
     if (nsplit <= 1)
         return;
-    const uint64_t prow0 = (uint64_t)s * a.max_splits * a.Hq + h;
     auto ml_of = [&](uint32_t i) {
         return *(const f32x2*)(a.part_ml + (prow0 + (uint64_t)i * a.Hq) * 2);
     };
-    const uint64_t oi = ((uint64_t)s * a.Hq + h) * DV + lane * DPL;
     float g[DPL];
 #pragma unroll
     for (int k = 0; k < DPL; ++k)
@@ -871,8 +1016,16 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeAr
 struct Plan {
     uint32_t chunk_blocks;
     uint32_t max_splits;
+    uint32_t ranges;        // balanced mode: block ranges per kv group (0 = split mode)
     size_t workspace;
 };
+
+// Balanced mode (MFMA path, automatic split size, no sliding window): up to
+// this many sequences per call (every wave scans seq_lens) and this many
+// ranges.  A windowed decode attends a few hundred blocks per sequence, whose
+// equal splits already balance, and measured slower in balanced mode.
+constexpr uint32_t kBalancedMaxSeqs = 1024;
+constexpr uint64_t kBalancedMaxRanges = 1u << 16;
 
 // Split plan: enough (sequence, split) work-groups to cover the chip several
 // times over, each split a whole number of blocks, at most 128 blocks (so a
@@ -881,7 +1034,7 @@ struct Plan {
 // attended blocks of every sequence.
 static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads,
                       uint32_t head_dim_v, uint32_t max_blocks_per_seq, uint32_t block_size,
-                      uint32_t sliding_window, uint32_t split_tokens)
+                      uint32_t sliding_window, uint32_t split_tokens, bool balanced_ok)
 {
     Plan p{};
     if (sliding_window > 0) {
@@ -908,6 +1061,26 @@ static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_h
     p.max_splits = ceil_div(max_blocks_per_seq, cb);
     if (p.max_splits > 1)
         p.workspace = (size_t)num_seqs * p.max_splits * num_q_heads * (head_dim_v + 2) * sizeof(float);
+    if (balanced_ok && !split_tokens && !sliding_window && num_seqs <= kBalancedMaxSeqs) {
+        // enough ranges that ceil(T / ranges) <= kMaxRange for any T up to
+        // num_seqs * max_blocks_per_seq (the attended-block bound), and the
+        // work-group target, but no more than one range per kMinChunk blocks
+        // of that bound; a single range finishes every sequence itself and
+        // needs no workspace
+        const uint32_t kv_groups = ceil_div(num_kv_heads, kKvPerGroup);
+        const uint64_t bound = (uint64_t)num_seqs * max_blocks_per_seq;
+        const uint64_t need = (bound + kMaxRange - 1) / kMaxRange;
+        uint64_t spread = (kTargetGroups + kv_groups - 1) / kv_groups;
+        const uint64_t small = (bound + kMinChunk - 1) / kMinChunk;
+        spread = spread < small ? spread : small;
+        uint64_t ranges = need > spread ? need : spread;
+        ranges = ranges < 1 ? 1 : ranges;
+        if (ranges <= kBalancedMaxRanges) {
+            p.ranges = (uint32_t)ranges;
+            p.workspace = ranges > 1
+                ? (size_t)(ranges + num_seqs) * num_q_heads * (head_dim_v + 2) * sizeof(float) : 0;
+        }
+    }
     return p;
 }
 
@@ -921,9 +1094,15 @@ extern "C" size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_h
     if (!num_seqs || !num_q_heads || !num_kv_heads || !head_dim_v || !max_blocks_per_seq ||
         !block_size)
         return 0;
-    return pkv::make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim_v, max_blocks_per_seq,
-                          block_size, sliding_window, split_tokens)
-        .workspace;
+    // the larger of the two modes' needs (the dtypes, which choose the mode,
+    // are not arguments here)
+    const size_t a = pkv::make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim_v,
+                                    max_blocks_per_seq, block_size, sliding_window, split_tokens,
+                                    false).workspace;
+    const size_t b = pkv::make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim_v,
+                                    max_blocks_per_seq, block_size, sliding_window, split_tokens,
+                                    true).workspace;
+    return a > b ? a : b;
 }
 
 extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
@@ -994,7 +1173,8 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
             return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: FP32 path needs a GQA group of 1, 2, 4 or 8");
     }
     const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim_v,
-                                max_blocks_per_seq, block_size, sliding_window, split_tokens);
+                                max_blocks_per_seq, block_size, sliding_window, split_tokens,
+                                mfma_path);
     if (plan.workspace > 0 && (workspace_bytes < plan.workspace || !workspace))
         return fail(PKV_ERR_WORKSPACE, "paged_decode_attn: workspace of %zu bytes needed, %zu given",
                     plan.workspace, workspace_bytes);
@@ -1002,12 +1182,13 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
         return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: workspace must be 16-byte aligned");
     // the split index is a grid dimension (y, or z on the FP32 path, which
     // also puts the sequence in y): both are limited to 65535
-    if (plan.max_splits > 65535u)
+    if (!plan.ranges && plan.max_splits > 65535u)
         return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: %u splits per sequence (limit 65535); use a larger split_tokens",
                     plan.max_splits);
     if (!mfma_path && num_seqs > 65535u)
         return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: FP32 caches support at most 65535 sequences per call");
-    if (mfma_path && (uint64_t)num_seqs * num_kv_heads > 0x7FFFFFFFull)
+    if (mfma_path && ((uint64_t)num_seqs * num_kv_heads > 0x7FFFFFFFull ||
+                      (uint64_t)plan.ranges * num_kv_heads > 0x7FFFFFFFull))
         return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: too many sequences for one call");
 
     DecodeArgs a{};
@@ -1020,9 +1201,11 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     a.sinks = sinks;
     a.out = out;
     a.part_o = (float*)workspace;
-    a.part_ml = plan.workspace
-                    ? (float*)workspace + (size_t)num_seqs * plan.max_splits * num_q_heads * head_dim_v
-                    : nullptr;
+    const size_t part_rows = plan.ranges ? (size_t)plan.ranges + num_seqs
+                                         : (size_t)num_seqs * plan.max_splits;
+    a.part_ml = plan.workspace ? (float*)workspace + part_rows * num_q_heads * head_dim_v : nullptr;
+    a.S = num_seqs;
+    a.ranges = plan.ranges;
     a.q_stride = q_seq_stride;
     a.M = max_blocks_per_seq;
     a.num_blocks = num_blocks;
@@ -1053,18 +1236,22 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
         while (num_kv_heads % kvpb)
             kvpb >>= 1;
         const uint32_t kvg = num_kv_heads / kvpb;
-        const dim3 grid(num_seqs * kvg, plan.max_splits);
+        // balanced mode: range-major, the kv groups of a range side by side
+        const dim3 grid = plan.ranges ? dim3(plan.ranges * kvg, 1) : dim3(num_seqs * kvg, plan.max_splits);
         const dim3 block(64 * kvpb);
         const int kt = k_dtype == PKV_FP8_E4M3;
         const int vt = is_tq(v_dtype) ? tq_bits(v_dtype) : v_dtype == PKV_FP8_E4M3;
-#define PKV_MFMA(KT, VT, D)                                                                     \
-    if (kt == KT && vt == VT && head_dim_qk == D)                                              \
-        hipLaunchKernelGGL((decode_mfma_kernel<KT, VT, D, kPrefetch>), grid, block, 0, st, a, kvg);
+#define PKV_MFMA_B(KT, VT, D, BAL)                                                              \
+    if (kt == KT && vt == VT && head_dim_qk == D && bal == BAL)                                \
+        hipLaunchKernelGGL((decode_mfma_kernel<KT, VT, D, kPrefetch, BAL>), grid, block, 0, st, a, kvg);
+#define PKV_MFMA(KT, VT, D) PKV_MFMA_B(KT, VT, D, false) PKV_MFMA_B(KT, VT, D, true)
+        const bool bal = plan.ranges != 0;
         PKV_MFMA(0, 0, 128) PKV_MFMA(0, 0, 64) PKV_MFMA(1, 0, 128) PKV_MFMA(1, 0, 64)
         PKV_MFMA(0, 1, 128) PKV_MFMA(0, 1, 64) PKV_MFMA(1, 1, 128) PKV_MFMA(1, 1, 64)
         PKV_MFMA(0, 2, 128) PKV_MFMA(0, 3, 128) PKV_MFMA(0, 4, 128)
         PKV_MFMA(1, 2, 128) PKV_MFMA(1, 3, 128) PKV_MFMA(1, 4, 128)
 #undef PKV_MFMA
+#undef PKV_MFMA_B
     } else {
         const dim3 grid(num_kv_heads, num_seqs, plan.max_splits);
 #define PKV_F32(DQK, DV, GG)                                                              \
@@ -1079,7 +1266,7 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     int rc = check_launch("paged_decode_attn");
     if (rc)
         return rc;
-    if (plan.max_splits > 1) {
+    if (plan.ranges || plan.max_splits > 1) {
         const dim3 mgrid(num_seqs, ceil_div(num_q_heads, kMergeHeads));
         if (head_dim_v == 128)
             hipLaunchKernelGGL(decode_merge_kernel<2>, mgrid, dim3(64 * kMergeHeads), 0, st, a);

@@ -92,6 +92,39 @@ def test_bf16_gqa_groups_ragged(G, D):
     assert np.isfinite(got).all() and err <= ATTN_TOL
 
 
+@pytest.mark.parametrize("case", ["many_short_some_long", "past_balanced_limit", "one_range"])
+def test_automatic_plan_modes(case):
+    """Automatic split size without a window: up to 1024 sequences take equal
+    block ranges over the whole batch (short sequences share a work-group, long
+    ones span several ranges and are merged), more sequences take one work-group
+    per (sequence, split); a batch small enough for one range needs no
+    workspace.  Empty sequences give zero rows in every mode."""
+    rng = np.random.default_rng(77)
+    if case == "many_short_some_long":
+        lens = rng.integers(0, 48, size=600)
+        lens[::97] = rng.integers(500, 3000, size=lens[::97].size)
+        lens[5] = 0
+    elif case == "past_balanced_limit":
+        lens = rng.integers(0, 40, size=1100)
+        lens[7] = 0
+    else:
+        lens = np.array([20])
+    lay = W.layout_for(2, lens)
+    Hkv, G, D, B = 2, 4, 64, 16
+    kp = W.bf16_bits(rng.standard_normal((lay.num_blocks, B, Hkv, D)).astype(np.float32))
+    vp = W.bf16_bits(rng.standard_normal((lay.num_blocks, B, Hkv, D)).astype(np.float32))
+    kp[lay.pad_block] = 0x7FC0
+    vp[lay.pad_block] = 0x7FC0
+    q = W.bf16_bits(rng.standard_normal((lens.size, Hkv * G, D)).astype(np.float32))
+    if case == "one_range":
+        assert pkv.decode_workspace_bytes(1, Hkv * G, Hkv, D, lay.max_blocks_per_seq, B) == 0
+    got, ref = run_both(2, lay, Hq=Hkv * G, Hkv=Hkv, D=D, q=q, kp=kp, vp=vp)
+    err = attn_err(got, ref)
+    say(f"  {case}: err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATTN_TOL
+    assert (got[lens == 0] == 0).all()
+
+
 def test_bf16_decode_workload_subset():
     lay = W.layout(2, num_seqs=24)
     got, ref = run_both(2, lay, Hq=32, Hkv=8, D=128)
