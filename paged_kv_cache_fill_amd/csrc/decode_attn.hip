@@ -68,6 +68,7 @@ struct DecodeArgs {
     uint32_t max_splits;
     uint32_t S;             // sequences
     uint32_t ranges;        // balanced mode: block ranges per kv group (0 = split mode)
+    uint32_t* cu;           // balanced mode, ranges > 1: [S + 1] attended blocks before s
     float qk_scale;         // scale * log2(e) (* k_scale for E4M3 K)
     float out_scale;        // output factor: v_scale (E4M3 V), 2^-15 for FP16 weights
     uint32_t window;        // sliding window in tokens, 0 = none
@@ -130,26 +131,24 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
 // an upper bound of T).  A sequence whose blocks lie in one range is finished
 // by that range's work-group; otherwise each range writes a partial row for
 // it at slot w + s (unique: every slot step is a range or a sequence start),
-// and the merge combines slots first + s .. last + s.  T and the prefix sums
-// are recomputed by every wave from seq_lens (at most 1024 sequences).
+// and the merge combines slots first + s .. last + s.  Every wave recomputes
+// T from seq_lens (at most 1024 sequences); work-group 0 also writes the
+// prefix sums to the workspace for the merge.
 __device__ __forceinline__ uint32_t range_blocks(uint32_t T, uint32_t ranges)
 {
     const uint32_t c = T == 0 ? 1u : (T + ranges - 1) / ranges;
     return c < kMaxRange ? c : kMaxRange;
 }
 
-// Total attended blocks T and the blocks before sequence `upto` (all lanes).
-__device__ __forceinline__ void scan_blocks(const DecodeArgs& a, uint32_t upto, int lane,
-                                            uint32_t& T, uint32_t& before)
+// Total attended blocks T of the batch (all lanes).
+__device__ __forceinline__ uint32_t total_blocks(const DecodeArgs& a, int lane)
 {
-    T = 0;
-    before = 0;
+    uint32_t T = 0;
     for (uint32_t c = 0; c < a.S; c += 64) {
         const uint32_t s = c + (uint32_t)lane;
-        const uint32_t nb = s < a.S ? att_blocks(a, s) : 0u;
-        T += wave_sum_u32(nb);
-        before += wave_sum_u32(s < upto ? nb : 0u);
+        T += wave_sum_u32(s < a.S ? att_blocks(a, s) : 0u);
     }
+    return T;
 }
 
 // Writes the finished or partial result of one wave.
@@ -685,8 +684,27 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     const uint32_t w = blockIdx.x / kv_groups;
     uint32_t s = w, cu = 0, r0 = 0, r1 = 0, C = 1;
     if constexpr (balanced) {
-        uint32_t T, unused;
-        scan_blocks(a, 0u, lane, T, unused);
+        const uint32_t T = total_blocks(a, lane);
+        if (a.cu && blockIdx.x == 0 && wave == 0) {
+            // the prefix sums, for the merge (which runs after this kernel)
+            uint32_t base = 0;
+            for (uint32_t c = 0; c < a.S; c += 64) {
+                const uint32_t si = c + (uint32_t)lane;
+                const uint32_t nb = si < a.S ? att_blocks(a, si) : 0u;
+                uint32_t incl = nb;
+#pragma unroll
+                for (int d = 1; d < 64; d <<= 1) {
+                    const uint32_t t = __shfl_up(incl, d, 64);
+                    if (lane >= d)
+                        incl += t;
+                }
+                if (si < a.S)
+                    a.cu[si] = base + incl - nb;
+                base += __builtin_amdgcn_readlane(incl, 63);
+            }
+            if (lane == 0)
+                a.cu[a.S] = T;
+        }
         C = range_blocks(T, a.ranges);
         r0 = w * C;
         if (r0 >= T)
@@ -937,10 +955,11 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeAr
     uint64_t prow0;
     const uint64_t oi = ((uint64_t)s * a.Hq + h) * DV + lane * DPL;
     if (a.ranges) {
-        // balanced mode: the pieces of s are ranges first .. last, at slots w + s
-        uint32_t T, cu;
-        scan_blocks(a, s, lane, T, cu);
-        const uint32_t nb = att_blocks(a, s);
+        // balanced mode: the pieces of s are ranges first .. last, at slots
+        // w + s; with one range every sequence was finished in place
+        const uint32_t T = a.cu ? a.cu[a.S] : 0u;
+        const uint32_t cu = a.cu ? a.cu[s] : 0u;
+        const uint32_t nb = a.cu ? a.cu[s + 1] - cu : att_blocks(a, s);
         if (nb == 0) {
             // nothing attended: a zero row (no range wrote it)
 #pragma unroll
@@ -948,6 +967,8 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeAr
                 a.out[oi + k] = 0.f;
             return;
         }
+        if (!a.cu)
+            return;
         const uint32_t C = range_blocks(T, a.ranges);
         const uint32_t first = cu / C;
         uint32_t last = (cu + nb - 1) / C;
@@ -1078,7 +1099,9 @@ static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_h
         if (ranges <= kBalancedMaxRanges) {
             p.ranges = (uint32_t)ranges;
             p.workspace = ranges > 1
-                ? (size_t)(ranges + num_seqs) * num_q_heads * (head_dim_v + 2) * sizeof(float) : 0;
+                ? (size_t)(ranges + num_seqs) * num_q_heads * (head_dim_v + 2) * sizeof(float) +
+                      ((size_t)num_seqs + 1) * sizeof(uint32_t)
+                : 0;
         }
     }
     return p;
@@ -1206,6 +1229,7 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     a.part_ml = plan.workspace ? (float*)workspace + part_rows * num_q_heads * head_dim_v : nullptr;
     a.S = num_seqs;
     a.ranges = plan.ranges;
+    a.cu = plan.ranges > 1 ? (uint32_t*)(a.part_ml + part_rows * num_q_heads * 2) : nullptr;
     a.q_stride = q_seq_stride;
     a.M = max_blocks_per_seq;
     a.num_blocks = num_blocks;
