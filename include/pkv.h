@@ -284,7 +284,7 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *   split_tokens  tokens per split-K piece, rounded up to whole blocks and
  *                 capped at 128 blocks; 0 = the library's choice: without a
  *                 sliding window and with at most 1024 sequences, equal ranges
- *                 (at most 256 blocks) of the batch's attended blocks taken in
+ *                 (at most 512 blocks) of the batch's attended blocks taken in
  *                 sequence order, so that short sequences share a work-group
  *                 and long ones span several; otherwise enough pieces per
  *                 sequence to cover the GPU several times over.  The result

@@ -46,7 +46,7 @@ constexpr uint64_t kTargetGroups = 768; // (sequence, split, kv group) work-grou
 constexpr uint32_t kMinChunk = 4;       // blocks per split, automatic choice: at least
 constexpr int kBtRegs = 2;              // table entries held per lane (split mode)
 constexpr uint32_t kMaxChunk = 64 * kBtRegs;  // ... so at most this many blocks per split
-constexpr int kBtRegsBal = 4;           // table entries held per lane (balanced mode)
+constexpr int kBtRegsBal = 8;           // table entries held per lane (balanced mode)
 constexpr uint32_t kMaxRange = 64 * kBtRegsBal;  // ... so at most this many blocks per range
 
 struct DecodeArgs {
@@ -127,7 +127,7 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
 
 // Balanced mode.  The attended blocks of all sequences, in sequence order,
 // form one list of T blocks; range w of every kv group is the list's blocks
-// [w C, (w + 1) C), C = ceil(T / ranges) <= 128 (the host sizes `ranges` from
+// [w C, (w + 1) C), C = ceil(T / ranges) <= kMaxRange (the host sizes `ranges` from
 // an upper bound of T).  A sequence whose blocks lie in one range is finished
 // by that range's work-group; otherwise each range writes a partial row for
 // it at slot w + s (unique: every slot step is a range or a sequence start),
