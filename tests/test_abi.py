@@ -154,6 +154,16 @@ def test_workspace_query(lib):
     assert lib.pkv_decode_workspace_bytes(2, 4, 1, 64, 128, 16, 1010, 1024) == 2 * 2 * 4 * 66 * 4
     # a window never asks for more than no window
     assert lib.pkv_decode_workspace_bytes(256, 32, 8, 128, 512, 16, 100000, 0) == n
+    # balanced plan (automatic split size, no window, <= 1024 sequences): 1024
+    # sequences of at most 8 blocks, 4 kv groups -> max(ceil(8192 / 512), 768 / 4)
+    # = 192 ranges: partial rows for ranges + sequences, plus the prefix sums;
+    # the split plan needs nothing here (one split per sequence), and with a
+    # window the split plan is the only one
+    assert lib.pkv_decode_workspace_bytes(1024, 32, 8, 128, 8, 16, 0, 0) == \
+        (192 + 1024) * 32 * 130 * 4 + 1025 * 4
+    assert lib.pkv_decode_workspace_bytes(1024, 32, 8, 128, 8, 16, 64, 0) == 0
+    # past 1024 sequences only the split plan
+    assert lib.pkv_decode_workspace_bytes(1025, 32, 8, 128, 8, 16, 0, 0) == 0
 
 
 def test_prefill_and_mla_validation(lib):
