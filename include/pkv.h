@@ -290,7 +290,10 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *                 sequence to cover the GPU several times over.  The result
  *                 does not depend on it beyond FP32 rounding.
  *   workspace     device scratch of at least
- *                 pkv_decode_workspace_bytes(...) bytes (may be NULL if that is 0)
+ *                 pkv_decode_workspace_bytes(...) bytes (may be NULL if that is 0);
+ *                 caller-owned, needs no initialisation, holds the split
+ *                 partials between the call's kernels: calls that may run at
+ *                 the same time (other streams) need workspaces of their own
  * Supported: (q, K, V) dtypes (BF16, BF16 or FP8_E4M3, BF16 or FP8_E4M3 or
  *   TQ2/3/4), (FP32, FP32, FP32); TQ V with head_dim 128; the decode of TQ V
  *   is exact (no weight-threshold skipping); num_q_heads % num_kv_heads == 0;
