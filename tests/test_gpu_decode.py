@@ -266,3 +266,46 @@ def test_kv_head_counts(Hkv, G, kv):
     err = attn_err(host(out), ref)
     say(f"  err {err:.3e}")
     assert np.isfinite(host(out)).all() and err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("kv", ["bf16/bf16", "fp8/bf16", "bf16/fp8", "bf16/tq3"])
+def test_balanced_plan_formats_gate_and_many_pieces(kv):
+    """The balanced plan (automatic split size, no window) for every MFMA-path
+    cache format, with an output gate: 8 ragged sequences get ranges of a single
+    block, so a long sequence is merged from hundreds of partial rows; gate = 1
+    is bit-identical to no gate."""
+    k_dt, v_dt = kv.split("/")
+    Hkv, G, D = 2, 4, 128
+    lens = [0, 1, 40, 300, 1000, 2500, 17, 5000]
+    lay = W.layout_for(2, lens)
+    rng = np.random.default_rng(len(kv) * 7 + ord(kv[0]))
+    shape = (lay.num_blocks, 16, Hkv, D)
+    kp = W.e4m3_codes(2, 60, shape) if k_dt == "fp8" else \
+        W.bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    if v_dt == "tq3":
+        vp = np.zeros((lay.num_blocks, oracle.tq_block_bytes(3, 16, Hkv, D)), np.uint8)
+        x = rng.standard_normal((lay.num_blocks * 16, Hkv, D)).astype(np.float32)
+        oracle.cache_write_v(x, "f32", np.arange(lay.num_blocks * 16, dtype=np.int64), vp,
+                             num_kv_heads=Hkv, head_dim_v=D, block_size=16, cache_dtype="tq3")
+    elif v_dt == "fp8":
+        vp = W.e4m3_codes(2, 61, shape)
+    else:
+        vp = W.bf16_bits(rng.standard_normal(shape).astype(np.float32))
+    q = W.bf16_bits(rng.standard_normal((len(lens), Hkv * G, D)).astype(np.float32))
+    gate = rng.uniform(0.0, 1.0, (len(lens), Hkv * G, D)).astype(np.float32)
+    ref = oracle.paged_decode(q, "bf16", kp, k_dt, vp, v_dt, lay.block_tables, lay.seq_lens,
+                              num_q_heads=Hkv * G, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=D,
+                              block_size=16, scale=D ** -0.5, k_scale=0.5, v_scale=0.25,
+                              gate=gate, nthreads=8)
+    say(f"balanced plan K={k_dt} V={v_dt} lens={lens}")
+    vdev = dev(vp, torch.uint8) if v_dt == "tq3" else dev(vp)
+    args = (dev(q), dev(kp), vdev, dev(lay.block_tables), dev(lay.seq_lens))
+    kw = dict(scale=D ** -0.5, k_scale=0.5, v_scale=0.25, v_tq_bits=3 if v_dt == "tq3" else 0)
+    got = host(pkv.paged_decode_attn(*args, gate=dev(gate), **kw))
+    err = attn_err(got, ref)
+    say(f"  err {err:.3e}")
+    assert np.isfinite(got).all() and err <= ATTN_TOL
+    assert (got[0] == 0).all()
+    plain = host(pkv.paged_decode_attn(*args, **kw))
+    ones = host(pkv.paged_decode_attn(*args, gate=dev(np.ones_like(gate)), **kw))
+    assert plain.tobytes() == ones.tobytes()
