@@ -43,6 +43,7 @@ constexpr uint32_t kKvPerGroup = 2;     // kv heads (waves) per work-group, at m
 constexpr int kPrefetch = 1;            // cache blocks loaded ahead of the one in use
 constexpr bool kKDirect = false;        // K loaded straight into the operand layout
 constexpr uint64_t kTargetGroups = 768; // (sequence, split, kv group) work-groups wanted
+constexpr uint64_t kTargetWavesF32 = 3072; // FP32 path: (sequence, kv head, split) waves wanted
 constexpr uint32_t kMinChunk = 4;       // blocks per split, automatic choice: at least
 constexpr int kBtRegs = 2;              // table entries held per lane (split mode)
 constexpr uint32_t kMaxChunk = 64 * kBtRegs;  // ... so at most this many blocks per split
@@ -1055,7 +1056,7 @@ constexpr uint64_t kBalancedMaxRanges = 1u << 16;
 // attended blocks of every sequence.
 static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads,
                       uint32_t head_dim_v, uint32_t max_blocks_per_seq, uint32_t block_size,
-                      uint32_t sliding_window, uint32_t split_tokens, bool balanced_ok)
+                      uint32_t sliding_window, uint32_t split_tokens, bool mfma)
 {
     Plan p{};
     if (sliding_window > 0) {
@@ -1067,10 +1068,13 @@ static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_h
     if (split_tokens) {
         cb = ceil_div(split_tokens, block_size);
     } else {
-        // count (sequence, kv group) pairs; FP32 path: one wave per kv head
-        const uint32_t kv_groups = ceil_div(num_kv_heads, kKvPerGroup);
+        // MFMA path: (sequence, kv group) work-groups of two waves, about
+        // kTargetGroups of them; FP32 path: one wave per (sequence, kv head,
+        // split), about kTargetWavesF32 of them
+        const uint32_t kv_groups = mfma ? ceil_div(num_kv_heads, kKvPerGroup) : num_kv_heads;
+        const uint64_t target = mfma ? kTargetGroups : kTargetWavesF32;
         const uint64_t units = (uint64_t)num_seqs * kv_groups;
-        const uint64_t want = units >= kTargetGroups ? 1 : (kTargetGroups + units - 1) / units;
+        const uint64_t want = units >= target ? 1 : (target + units - 1) / units;
         cb = ceil_div(max_blocks_per_seq, want);
         cb = cb < kMinChunk ? kMinChunk : cb;
         // equal splits: as few as the chunk cap allows, then evenly sized
@@ -1082,7 +1086,7 @@ static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_h
     p.max_splits = ceil_div(max_blocks_per_seq, cb);
     if (p.max_splits > 1)
         p.workspace = (size_t)num_seqs * p.max_splits * num_q_heads * (head_dim_v + 2) * sizeof(float);
-    if (balanced_ok && !split_tokens && !sliding_window && num_seqs <= kBalancedMaxSeqs) {
+    if (mfma && !split_tokens && !sliding_window && num_seqs <= kBalancedMaxSeqs) {
         // enough ranges that ceil(T / ranges) <= kMaxRange for any T up to
         // num_seqs * max_blocks_per_seq (the attended-block bound), and the
         // work-group target, but no more than one range per kMinChunk blocks
