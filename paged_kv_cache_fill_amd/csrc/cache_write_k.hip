@@ -54,6 +54,9 @@ struct KWriteArgs {
     uint32_t rows_per_wave; // 64 / L
     uint32_t units_per_token;
     uint32_t units_per_wave;
+    // inverse frequencies fl32(theta^(-2i/R)), i < R/2: the FP64 power is
+    // taken once per call on the host instead of twice per lane per wave
+    float invf[kMaxHalf];
 };
 
 template <int IN>
@@ -160,12 +163,9 @@ __global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(
         for (int e = 0; e < VEC; ++e)
             w[k][e] = a.norm_w ? InVec<IN>::scalar(a.norm_w, (uint64_t)(lir + a.L * k) * VEC + e)
                                : 1.0f;
-    // invf_i = fl32(theta^(-2i/R)); lane computes pairs lane and lane + 64
-    float invf0 = 0.f, invf1 = 0.f;
-    if (a.half > 0) {
-        invf0 = (float)pow((double)a.theta, -(2.0 * (double)lane) / (double)a.rot_dim);
-        invf1 = (float)pow((double)a.theta, -(2.0 * (double)(lane + 64)) / (double)a.rot_dim);
-    }
+    // invf_i = fl32(theta^(-2i/R)) (host table); lane takes pairs lane and lane + 64
+    const float invf0 = a.invf[lane];
+    const float invf1 = a.invf[lane + 64];
     const bool mrope = a.pos_h != nullptr && a.pos_w != nullptr;
     const uint32_t kp = a.half ? a.rope_chunks / a.L : 0;  // chunk-slot distance of a pair
 
@@ -483,6 +483,9 @@ extern "C" int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype,
     a.rope_chunks = pair;
     a.half = rope ? rotary_dim / 2 : 0;
     a.rot_dim = rope ? rotary_dim : 1;
+    for (uint32_t i = 0; i < (uint32_t)kMaxHalf; ++i)
+        a.invf[i] = i < a.half ? (float)std::pow((double)theta, -(2.0 * (double)i) / (double)rotary_dim)
+                               : 0.f;
     a.L = L;
     a.rows_per_wave = 64 / L;
     a.units_per_token = ceil_div(num_kv_heads, a.rows_per_wave);
