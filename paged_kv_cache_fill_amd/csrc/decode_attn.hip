@@ -77,11 +77,13 @@ struct DecodeArgs {
     // bytes of entries 0-3, 4-7, high bytes of 0-3, 4-7), and block bytes
     uint32_t tq_f16[4];
     uint32_t v_blk_bytes;
-    // query rotation (FP32 path)
+    // query rotation (FP32 path); inverse frequencies fl32(theta^(-2i/dim))
+    // from the host, as for the K write
     uint32_t q_rope;
     float q_rope_theta;
     uint32_t q_rope_offset;
     uint32_t q_rope_dim;
+    float q_invf[128];
 };
 
 // ------------------------------------------------------------------ helpers
@@ -817,9 +819,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
         const uint32_t half = a.q_rope_dim / 2;
         for (uint32_t idx = lane; idx < (uint32_t)G * half; idx += 64) {
             const uint32_t g = idx / half, i = idx % half;
-            const float invf =
-                (float)pow((double)a.q_rope_theta, -(2.0 * (double)i) / (double)a.q_rope_dim);
-            const float ang = (float)(n - 1) * invf;
+            const float ang = (float)(n - 1) * a.q_invf[i];
             float sn, cs;
             sincosf(ang, &sn, &cs);
             const float x0 = s_q[g][a.q_rope_offset + i];
@@ -1257,6 +1257,10 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     a.q_rope_theta = q_rope_theta;
     a.q_rope_offset = q_rope_offset;
     a.q_rope_dim = q_rope_dim;
+    for (uint32_t i = 0; i < 128; ++i)
+        a.q_invf[i] = a.q_rope && i < q_rope_dim / 2
+                          ? (float)std::pow((double)q_rope_theta, -(2.0 * (double)i) / (double)q_rope_dim)
+                          : 0.f;
     hipStream_t st = (hipStream_t)stream;
 
     if (mfma_path) {
