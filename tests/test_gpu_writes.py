@@ -210,11 +210,15 @@ def test_k_write_mla_style_f32_partial_rope_and_nope():
 
 
 def test_k_write_head_dims_and_partial_rotary():
-    """Other supported layouts: D 64/128/256, partial rotary, FP32 input."""
+    """Other supported layouts: D 64/128/256, partial rotary, FP32 input.  The
+    E4M3 store's lane exchange runs with 4, 8 and 16 lanes per row, 2, 4, 6 and
+    8 chunks per lane, and one lane per row (rotary_dim 48: an odd pair
+    distance in chunks)."""
     rng = np.random.default_rng(11)
     for (in_dt, D, R, off, H) in (("bf16", 64, 64, 0, 4), ("bf16", 128, 64, 0, 2),
                                   ("bf16", 256, 256, 0, 2), ("f32", 128, 128, 0, 2),
-                                  ("f32", 64, 32, 32, 8), ("bf16", 192, 64, 128, 3)):
+                                  ("f32", 64, 32, 32, 8), ("bf16", 192, 64, 128, 3),
+                                  ("bf16", 64, 48, 0, 2)):
         T = 50
         x = rng.standard_normal((T, H, D)).astype(np.float32)
         k = W.bf16_bits(x) if in_dt == "bf16" else x
