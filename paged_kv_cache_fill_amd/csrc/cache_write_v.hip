@@ -17,7 +17,12 @@
 namespace pkv {
 
 constexpr int kVThreads = 256;
-constexpr int kVRun = 4;  // tokens per thread per pass (loads in flight)
+constexpr int kVRun = 4;      // E4M3 store: tokens per thread per pass (loads in flight)
+// The plain copy: one token per thread, so the most threads, each with one
+// load in flight (population write of 1.09 M BF16 rows: 0.80 ms against
+// 0.86 ms with four tokens per thread and 0.85 ms with two; the E4M3 store,
+// which converts, was fastest with four).
+constexpr int kVRunCopy = 1;
 
 // cols = row bytes / 16; tpb = tokens handled side by side by one block
 // (kVThreads / cols when a row fits in a block, else 1 with a column loop).
@@ -31,25 +36,25 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_kernel(
     if (lane_tok >= tpb)
         return;
     const uint32_t col_step = cols < kVThreads ? cols : kVThreads;  // columns per pass
-    // Token runs: block b handles tokens [b * tpb * kVRun, (b+1) * tpb * kVRun),
+    // Token runs: block b handles tokens [b * tpb * kVRunCopy, (b+1) * tpb * kVRunCopy),
     // token = base + r * tpb + lane_tok.
-    const uint64_t base = (uint64_t)blockIdx.x * tpb * kVRun;
-    int64_t slot[kVRun];
-    uint64_t tok[kVRun];
+    const uint64_t base = (uint64_t)blockIdx.x * tpb * kVRunCopy;
+    int64_t slot[kVRunCopy];
+    uint64_t tok[kVRunCopy];
 #pragma unroll
-    for (int r = 0; r < kVRun; ++r) {
+    for (int r = 0; r < kVRunCopy; ++r) {
         tok[r] = base + (uint64_t)r * tpb + lane_tok;
         int64_t s = tok[r] < num_tokens ? slots[tok[r]] : -1;
         slot[r] = (s >= 0 && (uint64_t)s < num_slots) ? s : -1;
     }
     for (uint32_t c = col0; c < cols; c += col_step) {
-        u32x4 buf[kVRun];
+        u32x4 buf[kVRunCopy];
 #pragma unroll
-        for (int r = 0; r < kVRun; ++r)
+        for (int r = 0; r < kVRunCopy; ++r)
             if (slot[r] >= 0)
                 buf[r] = load_nt(v + tok[r] * in_stride16 + c);
 #pragma unroll
-        for (int r = 0; r < kVRun; ++r)
+        for (int r = 0; r < kVRunCopy; ++r)
             if (slot[r] >= 0)
                 store_nt(cache + (uint64_t)slot[r] * cols + c, buf[r]);
     }
@@ -333,8 +338,10 @@ extern "C" int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_
         return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: row too long");
     const uint32_t cols = (uint32_t)cols64;
     const uint32_t tpb = cols <= (uint32_t)kVThreads ? (uint32_t)kVThreads / cols : 1u;
-    const uint64_t per_block = (uint64_t)tpb * kVRun;
+    const uint64_t per_block = (uint64_t)tpb * (e4m3 ? kVRun : kVRunCopy);
     const uint64_t blocks = (num_tokens + per_block - 1) / per_block;
+    if (blocks > 0x7FFFFFFFull)
+        return fail(PKV_ERR_UNSUPPORTED, "cache_write_v: too many tokens for one call");
     const uint64_t num_slots = (uint64_t)num_blocks * block_size;
     hipStream_t st = (hipStream_t)stream;
     if (!e4m3)
