@@ -176,7 +176,8 @@ int pkv_fill_slots(int64_t* slots, const int32_t* block_tables, uint32_t max_blo
  *   pos_h, pos_w  in  int32 [num_tokens] or both NULL
  *   slot_mapping  in  int64 [num_tokens]
  *   k_cache       out [num_blocks, block_size, num_kv_heads, head_dim] of cache_dtype
- *   k_scale           FP8 only: per-tensor scale, finite and > 0
+ *   k_scale           FP8 only: per-tensor scale, finite and at least
+ *                     FLT_MIN = 2^-126 (a normal number), else PKV_ERR_INVALID
  * Supported: in_dtype BF16 or FP32; cache_dtype BF16, FP8_E4M3 or FP32;
  *   head_dim in {64, 128, 192, 256}; rotary_dim even, rope_offset +
  *   rotary_dim <= head_dim, rope_offset and rotary_dim / 2 multiples of

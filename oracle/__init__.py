@@ -83,6 +83,8 @@ def lib():
         L.pkvo_tq_codebook.restype = None
         L.pkvo_tq_block_bytes.argtypes = [I32, U32, U32, U32]
         L.pkvo_tq_block_bytes.restype = U64
+        L.pkvo_tq_encode_diag.argtypes = [P, I32, U64, U32, U32, U32, I32, P, P, P, P, P]
+        L.pkvo_tq_encode_diag.restype = None
         L.pkvo_mla_cache_assemble.argtypes = [P, P, I32, U64, U64, P, U32, U32, U32, U32, U32,
                                               U32, P, P]
         L.pkvo_mla_cache_assemble.restype = None
@@ -309,3 +311,22 @@ def tq_codebook(bits: int) -> np.ndarray:
 
 def tq_block_bytes(bits: int, block_size: int, num_kv_heads: int, head_dim_v: int) -> int:
     return int(lib().pkvo_tq_block_bytes(bits, block_size, num_kv_heads, head_dim_v))
+
+
+def tq_encode_diag(v, dtype, bits: int, *, num_kv_heads, head_dim_v, in_token_stride=None):
+    """What the TQ encoder decides each group from, for rows v [T, H, D]:
+    returns (u [T, H, D] = x / rms, ss [T, H, D/16] = sum of squares, ratio
+    [T, H, D/16] = |x| / |chosen levels|, codes [T, H, D] = sign << (b-1) |
+    magnitude index, scales [T, H, D/16] E4M3 bytes), FP64 / uint8."""
+    v = _c(v, NP_TYPES[dtype])
+    T = v.shape[0]
+    H, D = num_kv_heads, head_dim_v
+    stride = in_token_stride if in_token_stride is not None else H * D
+    u = np.empty((T, H, D), np.float64)
+    ss = np.empty((T, H, D // 16), np.float64)
+    ratio = np.empty((T, H, D // 16), np.float64)
+    codes = np.empty((T, H, D), np.uint8)
+    scales = np.empty((T, H, D // 16), np.uint8)
+    lib().pkvo_tq_encode_diag(_ptr(v), DTYPES[dtype], stride, T, H, D, bits, _ptr(u), _ptr(ss),
+                              _ptr(ratio), _ptr(codes), _ptr(scales))
+    return u, ss, ratio, codes, scales

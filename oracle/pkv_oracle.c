@@ -366,7 +366,9 @@ void pkvo_cache_write_k(const void* k_in, int in_dtype, uint64_t in_token_stride
  *    per group (scale of (t, q) at B * D * b / 8 + q * B + t).  A head's
  *    codes and scales of one block are thus contiguous (the pages fix no
  *    layout);
- *  - the encoder's decisions are taken in FP32 (stated with its code).
+ *  - the encoder's decisions follow this definition in FP64 arithmetic:
+ *    the rms, each x / rms, the nearest-level choice and the ratio of norms
+ *    are exact up to FP64 rounding, and the ratio is rounded once, to E4M3;
  *  - no rotation and no sparse skip (the decode is exact). */
 
 static double std_normal_pdf(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846); }
@@ -446,29 +448,75 @@ static double tq_elem(const void* cache, int bits, uint32_t B, uint32_t H, uint3
     return pkvo_f64_from_e4m3(sc) * v;
 }
 
-/* Writes V rows of the tokens with valid slots into a TQ cache.
- * The pages fix no precision for the encoder's decisions (the code of an
- * element, the E4M3 scale byte); they are integers decided by floating point,
- * so they are taken here in FP32 by this stated sequence:
- *   ss  = FP32 fused multiply-add sum of x_i^2, i = 0..15 in order;
- *   inv = 1 / sqrt(ss * (1/16))   (correctly rounded sqrt, then division);
- *   u_i = x_i * inv;  code_i = sign(u_i) << (b-1) | the count of thresholds
- *         (midpoints of adjacent magnitudes) that |u_i| exceeds;
- *   scale = saturating E4M3 of sqrt(ss) / sqrt(sum of chosen magnitude^2). */
+/* The E4M3 magnitudes of a TQ format and the midpoints between neighbours
+ * (exact in FP64: sums of two E4M3 values). */
+static int tq_levels(int bits, double* mags, double* thr)
+{
+    const int M = 1 << (bits - 1);
+    uint8_t mc[8];
+    pkvo_tq_codebook(bits, mc);
+    for (int j = 0; j < M; ++j)
+        mags[j] = pkvo_f64_from_e4m3(mc[j]);
+    for (int j = 0; j + 1 < M; ++j)
+        thr[j] = 0.5 * (mags[j] + mags[j + 1]);
+    return M;
+}
+
+/* One group of 16 elements, by the definition, in FP64:
+ *   rms   = sqrt(sum x_i^2 / 16);
+ *   u_i   = x_i / rms;  code_i = sign(u_i) << (b-1) | the index of the
+ *           nearest magnitude of |u_i| (on an exact midpoint the smaller
+ *           one: the count of midpoints that |u_i| strictly exceeds; -0 and
+ *           +0 are positive);
+ *   ratio = |x| / |chosen levels| (the norm correction), scale = E4M3 of it
+ *           (one rounding, nearest even, saturating at 448).
+ * An all-zero group has codes 0 and scale 0.  u, the sum of squares and
+ * the ratio are returned for callers that need to know how close a
+ * decision was. */
+static void tq_encode_group(const double* x, int bits, const double* mags, const double* thr,
+                            uint32_t* codes, uint8_t* scale, double* u_out, double* ss_out,
+                            double* ratio_out)
+{
+    const int M = 1 << (bits - 1);
+    double ss = 0.0;
+    for (int i = 0; i < 16; ++i)
+        ss += x[i] * x[i];
+    *ss_out = ss;
+    *ratio_out = 0.0;
+    *scale = 0;
+    if (!(ss > 0.0)) {
+        for (int i = 0; i < 16; ++i) {
+            codes[i] = 0;
+            u_out[i] = 0.0;
+        }
+        return;
+    }
+    const double rms = sqrt(ss / 16.0);
+    double cn = 0.0;          /* exact: at most 16 squares of E4M3 values */
+    for (int i = 0; i < 16; ++i) {
+        const double u = x[i] / rms;
+        const double au = fabs(u);
+        uint32_t m = 0;
+        while ((int)m + 1 < M && au > thr[m])
+            ++m;
+        codes[i] = (u < 0.0 ? 1u : 0u) << (bits - 1) | m;
+        cn += mags[m] * mags[m];
+        u_out[i] = u;
+    }
+    *ratio_out = sqrt(ss) / sqrt(cn);
+    *scale = pkvo_e4m3_from_f64(*ratio_out);
+}
+
+/* Writes V rows of the tokens with valid slots into a TQ cache (each group
+ * coded by tq_encode_group). */
 void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride,
                            const int64_t* slots, uint32_t num_tokens, uint32_t num_kv_heads,
                            uint32_t head_dim_v, uint32_t block_size, uint32_t num_blocks,
                            void* v_cache, int bits)
 {
     const uint32_t H = num_kv_heads, D = head_dim_v, B = block_size;
-    const int M = 1 << (bits - 1);
-    uint8_t mc[8];
     double mags[8], thr[8];
-    pkvo_tq_codebook(bits, mc);
-    for (int j = 0; j < M; ++j)
-        mags[j] = pkvo_f64_from_e4m3(mc[j]);
-    for (int j = 0; j + 1 < M; ++j)
-        thr[j] = 0.5 * (mags[j] + mags[j + 1]);
+    tq_levels(bits, mags, thr);
     uint64_t blk_bytes = pkvo_tq_block_bytes(bits, B, H, D);
     uint64_t num_slots = (uint64_t)num_blocks * B;
     for (uint64_t tok = 0; tok < num_tokens; ++tok) {
@@ -481,34 +529,12 @@ void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride
             uint8_t* base = (uint8_t*)v_cache + blk * blk_bytes + h * tq_region_bytes(bits, B, D);
             uint8_t* row = base + (uint64_t)t * D * bits / 8;
             for (uint32_t q = 0; q < D / 16; ++q) {
-                float x[16], ss = 0.0f;
-                for (int i = 0; i < 16; ++i) {
-                    /* BF16 and FP32 inputs are exact in FP32 */
-                    x[i] = (float)load_elem(v, in_dtype,
-                                            tok * in_token_stride + (uint64_t)h * D + q * 16 + i);
-                    ss = fmaf(x[i], x[i], ss);
-                }
+                double x[16], u[16], ss, ratio;
+                for (int i = 0; i < 16; ++i)
+                    x[i] = load_elem(v, in_dtype, tok * in_token_stride + (uint64_t)h * D + q * 16 + i);
                 uint32_t codes[16];
-                uint8_t scale = 0;
-                if (ss > 0.0f) {
-                    float r = sqrtf(ss * 0.0625f);
-                    float inv = 1.0f / r;
-                    double cn = 0.0;      /* exact: at most 16 squares of E4M3 values */
-                    for (int i = 0; i < 16; ++i) {
-                        float u = x[i] * inv;
-                        float au = fabsf(u);
-                        uint32_t m = 0;
-                        while ((int)m + 1 < M && (double)au > thr[m])
-                            ++m;
-                        codes[i] = (u < 0.0f ? 1u : 0u) << (bits - 1) | m;
-                        cn += mags[m] * mags[m];
-                    }
-                    float ratio = sqrtf(ss) / sqrtf((float)cn);
-                    scale = pkvo_e4m3_from_f64((double)ratio);
-                } else {
-                    for (int i = 0; i < 16; ++i)
-                        codes[i] = 0;
-                }
+                uint8_t scale;
+                tq_encode_group(x, bits, mags, thr, codes, &scale, u, &ss, &ratio);
                 uint8_t* grp = row + (uint64_t)q * 2 * bits;
                 memset(grp, 0, 2 * (size_t)bits);
                 for (int i = 0; i < 16; ++i)
@@ -520,6 +546,35 @@ void pkvo_cache_write_v_tq(const void* v, int in_dtype, uint64_t in_token_stride
             }
         }
     }
+}
+
+/* The encoder's inputs to its decisions for rows v [T, H, D] (token stride
+ * in_token_stride): u [T, H, D] = x / rms of each element's group, and per
+ * group [T, H, D/16] the sum of squares and the ratio of norms, all FP64 as
+ * tq_encode_group takes them, plus the codes [T, H, D] and scale bytes it
+ * chooses.  For tests that must tell a decision taken close to a rounding
+ * boundary from a wrong one. */
+void pkvo_tq_encode_diag(const void* v, int in_dtype, uint64_t in_token_stride,
+                         uint32_t num_tokens, uint32_t num_kv_heads, uint32_t head_dim_v,
+                         int bits, double* u_out, double* ss_out, double* ratio_out,
+                         uint8_t* codes_out, uint8_t* scales_out)
+{
+    const uint32_t H = num_kv_heads, D = head_dim_v, NG = D / 16;
+    double mags[8], thr[8];
+    tq_levels(bits, mags, thr);
+    for (uint64_t tok = 0; tok < num_tokens; ++tok)
+        for (uint32_t h = 0; h < H; ++h)
+            for (uint32_t q = 0; q < NG; ++q) {
+                double x[16];
+                for (int i = 0; i < 16; ++i)
+                    x[i] = load_elem(v, in_dtype, tok * in_token_stride + (uint64_t)h * D + q * 16 + i);
+                const uint64_t g = (tok * H + h) * NG + q;
+                uint32_t codes[16];
+                tq_encode_group(x, bits, mags, thr, codes, &scales_out[g], &u_out[g * 16],
+                                &ss_out[g], &ratio_out[g]);
+                for (int i = 0; i < 16; ++i)
+                    codes_out[g * 16 + i] = (uint8_t)codes[i];
+            }
 }
 
 /* ------------------------------------------------------------------ */

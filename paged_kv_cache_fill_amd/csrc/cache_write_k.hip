@@ -17,6 +17,8 @@
 // cos/sin of a (token, pair) angle are computed once per wave-unit by one
 // lane and shared through LDS with all rows (kv heads) of the unit, so the
 // transcendental work is per token, not per (token, head).
+#include <cfloat>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -426,8 +428,10 @@ extern "C" int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype,
     const uint32_t VEC = 16 / es;
     if ((in_token_stride * es) % 16 || !aligned16(k_in) || !aligned16(k_cache))
         return fail(PKV_ERR_UNSUPPORTED, "cache_write_k_fused: k_in/k_cache and the token stride must be 16-byte aligned");
-    if (cache_dtype == PKV_FP8_E4M3 && !(k_scale > 0.0f && k_scale < INFINITY))
-        return fail(PKV_ERR_INVALID, "cache_write_k_fused: k_scale must be finite and > 0");
+    // 1/k_scale is folded into the row factor: a subnormal k_scale would make
+    // it infinite (and 0 * inf a NaN code), so the scale must be a normal number
+    if (cache_dtype == PKV_FP8_E4M3 && !(k_scale >= FLT_MIN && k_scale < INFINITY))
+        return fail(PKV_ERR_INVALID, "cache_write_k_fused: k_scale must be finite and >= FLT_MIN (2^-126)");
     const bool rope = !nope && rotary_dim > 0;
     if (rope) {
         if (!pos_t)

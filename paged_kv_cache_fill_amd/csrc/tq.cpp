@@ -1,13 +1,16 @@
 // tq.cpp -- host side of the TurboQuant-style V formats (PKV_TQ2/3/4; page 1,
 // kv_cache.rs, reshape_and_cache_bf16k_turbo{2,3,4}v: b-bit Lloyd-Max codes
 // plus an FP8 per-group scale; page 2: one FP8 scale per 16 elements): the
-// codebook, computed once per bit width (with the decoder's FP16 level
-// table), and the block-size query.
+// codebook with the decoder's FP16 level table, and the block-size query.
 //
-// Codebook: Lloyd's iteration on the standard normal density -- cells at
-// the midpoints between levels, each level moved to its cell's conditional
-// mean (phi(a) - phi(b)) / (Phi(b) - Phi(a)) -- to a fixed point; the
-// positive levels are then rounded to E4M3 (round to nearest even).
+// Codebook: the positive levels of the 2^b-level Lloyd-Max quantiser of the
+// standard normal distribution (the classical optimum tabulated by J. Max,
+// "Quantizing for minimum distortion", IRE Trans. Inform. Theory, 1960:
+// b = 2: 0.4528, 1.510; b = 3: 0.2451, 0.7560, 1.344, 2.152; b = 4: 0.1284,
+// 0.3881, 0.6568, 0.9424, 1.256, 1.618, 2.069, 2.733), each rounded to the
+// nearest E4M3 value (the closest to a rounding midpoint, 0.45278 against
+// 0.453125, is 3e-4 clear of it), stored as E4M3 codes.  A decoded value, level x E4M3 scale, is then a
+// product of two E4M3 numbers.
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -15,32 +18,6 @@
 #include "pkv_internal.h"
 
 namespace pkv {
-
-// E4M3FN code of a finite x >= 0, round to nearest even, saturating at 448.
-static uint8_t e4m3_code(double x)
-{
-    if (!(x > 0.0))
-        return 0;
-    if (x >= 448.0)
-        return 0x7E;
-    int e2;
-    std::frexp(x, &e2);                  // x = f * 2^e2, f in [0.5, 1)
-    int E = e2 - 1;                      // x in [2^E, 2^(E+1))
-    if (E < -6)
-        E = -6;                          // subnormal range: quantum 2^-9
-    const double quantum = std::ldexp(1.0, E - 3);
-    double m = std::nearbyint(x / quantum);   // default mode: ties to even
-    if (m >= 16.0) {                     // rounded up into the next binade
-        m = 8.0;
-        ++E;
-    }
-    if (m < 8.0)                         // subnormal (E == -6)
-        return (uint8_t)m;
-    const int field = E + 7;
-    if (field > 15 || (field == 15 && m > 14.0))
-        return 0x7E;
-    return (uint8_t)((field << 3) | ((int)m - 8));
-}
 
 static double e4m3_value(uint8_t c)
 {
@@ -63,29 +40,13 @@ static uint16_t f16_bits(double v)
     return (uint16_t)(sign | field << 10 | man);
 }
 
-static void lloyd_max(int bits, double* lv)
-{
-    const int L = 1 << bits;
-    for (int k = 0; k < L; ++k)
-        lv[k] = -3.0 + 6.0 * (k + 0.5) / L;
-    const double inv_sqrt2pi = 0.3989422804014326779;
-    auto pdf = [&](double x) { return std::isinf(x) ? 0.0 : inv_sqrt2pi * std::exp(-0.5 * x * x); };
-    auto cdf = [](double x) { return 0.5 * std::erfc(-x * 0.70710678118654752440); };
-    for (int it = 0; it < 100000; ++it) {
-        double next[16], worst = 0.0, lo = -INFINITY;
-        for (int k = 0; k < L; ++k) {
-            const double hi = k + 1 < L ? 0.5 * (lv[k] + lv[k + 1]) : INFINITY;
-            next[k] = (pdf(lo) - pdf(hi)) / (cdf(hi) - cdf(lo));
-            lo = hi;
-        }
-        for (int k = 0; k < L; ++k) {
-            worst = std::fmax(worst, std::fabs(next[k] - lv[k]));
-            lv[k] = next[k];
-        }
-        if (worst < 1e-15)
-            break;
-    }
-}
+// E4M3 codes of the positive magnitudes, ascending (b = 2, 3, 4):
+// 0x2E 0.4375, 0x3C 1.5; 0x28 0.25, 0x34 0.75, 0x3B 1.375, 0x41 2.25;
+// 0x20 0.125, 0x2C 0.375, 0x33 0.6875, 0x37 0.9375, 0x3A 1.25, 0x3D 1.625,
+// 0x40 2, 0x43 2.75.
+static const uint8_t kMagCodes2[2] = {0x2E, 0x3C};
+static const uint8_t kMagCodes3[4] = {0x28, 0x34, 0x3B, 0x41};
+static const uint8_t kMagCodes4[8] = {0x20, 0x2C, 0x33, 0x37, 0x3A, 0x3D, 0x40, 0x43};
 
 const TqCodebook& tq_codebook(int bits)
 {
@@ -97,10 +58,9 @@ const TqCodebook& tq_codebook(int bits)
         std::memset(&b, 0, sizeof b);
         b.bits = bits;
         b.mags_count = 1 << (bits - 1);
-        double lv[16];
-        lloyd_max(bits, lv);
+        const uint8_t* codes = bits == 2 ? kMagCodes2 : bits == 3 ? kMagCodes3 : kMagCodes4;
         for (int j = 0; j < b.mags_count; ++j) {
-            b.codes[j] = e4m3_code(lv[b.mags_count + j]);
+            b.codes[j] = codes[j];
             b.mags[j] = (float)e4m3_value(b.codes[j]);
         }
         for (int j = 0; j + 1 < b.mags_count; ++j)

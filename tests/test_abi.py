@@ -102,9 +102,13 @@ def test_bad_dtypes_and_shapes(lib):
     # pos_h without pos_w
     assert lib.pkv_cache_write_k_fused(FAKE, 0, 1024, None, 1e-6, FAKE, FAKE, None, 1e4, 0,
                                        128, 0, FAKE, 10, 8, 128, 16, 4, FAKE, 0, 1.0, None) == -1
-    # FP8 store needs a positive finite k_scale
-    assert lib.pkv_cache_write_k_fused(FAKE, 0, 1024, None, 1e-6, FAKE, None, None, 1e4, 0,
-                                       128, 0, FAKE, 10, 8, 128, 16, 4, FAKE, 1, 0.0, None) == -1
+    # FP8 store needs a positive finite k_scale that is a normal number (its
+    # reciprocal is folded into the row factor); FLT_MIN itself is accepted
+    # up to the launch, which this fake pointer set never reaches
+    for bad in (0.0, -1.0, float("inf"), float("nan"), 2.0 ** -127, 2.0 ** -149):
+        assert lib.pkv_cache_write_k_fused(FAKE, 0, 1024, None, 1e-6, FAKE, None, None, 1e4, 0,
+                                           128, 0, FAKE, 10, 8, 128, 16, 4, FAKE, 1, bad,
+                                           None) == -1, bad
     # token stride smaller than a row
     assert lib.pkv_cache_write_k_fused(FAKE, 0, 512, None, 1e-6, FAKE, None, None, 1e4, 0,
                                        128, 0, FAKE, 10, 8, 128, 16, 4, FAKE, 0, 1.0, None) == -1

@@ -23,7 +23,7 @@ import bench
 import oracle
 import paged_kv_cache_fill_amd as pkv
 import pkv_workloads as W
-from _util import ATTN_TOL, attn_err, bf16_ok, e4m3_ok, host, say
+from _util import ATTN_TOL, attn_err, bf16_ok, e4m3_ok, host, say, tq_compare, tq_rows_by_slot
 
 pytestmark = pytest.mark.gpu
 
@@ -49,27 +49,17 @@ def _check_k_rows(k_in, pos, got, cfg, w, cache_dtype, k_scale):
                          eps=cfg["eps"], pos_t=pos, theta=cfg["theta"], k_scale=k_scale,
                          nthreads=8)
     ref = ref.reshape(-1, H, D)[:n]
-    ok = bf16_ok(got, ref) if cache_dtype == "bf16" else e4m3_ok(got, ref)
+    st = {}
+    ok = bf16_ok(got, ref, stats=st) if cache_dtype == "bf16" else e4m3_ok(got, ref)
+    if st:
+        say(f"  BF16 K: {st['n']} elements, {st['exact']} exact, {st['floor_only']} more than "
+            f"1 ulp apart within the 2^-20 row floor")
     assert ok.all(), f"{int((~ok).sum())} K elements outside the bar"
-
-
-def _tq_token_bytes(block_rows, t, bits, H, D):
-    """Bytes of token t (codes, then its scale of each group) of every head
-    region, from cache blocks [n, block_bytes]."""
-    region = B * (D * bits // 8 + D // 16)
-    cb = D * bits // 8
-    out = []
-    for h in range(H):
-        r = block_rows[:, h * region:(h + 1) * region]
-        codes = r[:, t * cb:(t + 1) * cb]
-        scales = r[:, B * cb + np.arange(D // 16) * B + t]
-        out.append(np.concatenate([codes, scales], axis=1))
-    return np.concatenate(out, axis=1)
 
 
 def _check_v_rows(v_in, got_rows, v_kind, H, D):
     """v_in [n, H, D] BF16 bits; got_rows: [n, H, D] (copy / E4M3) or, for
-    TQ, [n, bytes] of each token's bytes in slot order."""
+    TQ, (codes [n, H, D], scale bytes [n, H, D/16]) in slot order."""
     n = v_in.shape[0]
     if v_kind == "bf16":
         assert (got_rows == v_in).all()
@@ -80,24 +70,17 @@ def _check_v_rows(v_in, got_rows, v_kind, H, D):
                              head_dim_v=D, block_size=B, cache_dtype="fp8", v_scale=V_SCALE)
         assert (got_rows == ref.reshape(-1, H, D)[:n]).all()
         return
-    bits = int(v_kind[2])
-    nb = (n + B - 1) // B
-    ref = np.zeros((nb, oracle.tq_block_bytes(bits, B, H, D)), np.uint8)
-    oracle.cache_write_v(v_in, "bf16", np.arange(n, dtype=np.int64), ref, num_kv_heads=H,
-                         head_dim_v=D, block_size=B, cache_dtype=v_kind)
-    want = np.stack([_tq_token_bytes(ref[i // B:i // B + 1], i % B, bits, H, D)[0]
-                     for i in range(n)])
-    assert (got_rows == want).all()
+    st = tq_compare(got_rows[0], got_rows[1], v_in, "bf16", int(v_kind[2]), H, D)
+    say(f"  TQ rows: {st}")
 
 
 def _gather_rows(pool, slots, v_kind, H, D):
     """Rows at the given slots from a device pool (numpy, cache dtype)."""
     s = torch.from_numpy(np.asarray(slots, np.int64)).cuda()
     if v_kind is not None and v_kind.startswith("tq"):
-        bits = int(v_kind[2])
         blocks = _bits(pool.index_select(0, s // B))
-        return np.stack([_tq_token_bytes(blocks[i:i + 1], int(slots[i]) % B, bits, H, D)[0]
-                         for i in range(len(slots))])
+        local = np.arange(len(slots)) * B + np.asarray(slots, np.int64) % B
+        return tq_rows_by_slot(blocks, local, int(v_kind[2]), H, D)
     flat = pool.view(-1, H, D)
     return _bits(flat.index_select(0, s))
 

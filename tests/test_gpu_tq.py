@@ -2,8 +2,11 @@
 E4M3 scale per 16 elements): the write kernel and the decode attention that
 reads it, against the CPU oracle.
 
-Bars: the written pool is bit-exact (codes and scales are integers that
-both sides decide by the same stated FP32 sequence); attention within 2e-3
+Bars: the oracle takes the encoder's decisions (codes, E4M3 scale bytes) in
+FP64 from the definition and the kernel in FP32, so the written pool is
+compared tie-aware: codes and scale bytes equal except where the FP64
+decision lies within FP32 rounding of its boundary (there one step apart at
+most), bytes outside the written slots untouched; attention within 2e-3
 row-relative (FP32 output), as for the other caches."""
 import os
 
@@ -14,7 +17,8 @@ import torch
 import oracle
 import paged_kv_cache_fill_amd as pkv
 import pkv_workloads as W
-from _util import ATTN_TOL, attn_err, dev, host, say, tq_scale_mask
+from _util import (ATTN_TOL, attn_err, dev, host, say, tq_compare, tq_rows_by_slot,
+                   tq_scale_mask, tq_written_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,8 +42,20 @@ def _write_both(v, in_dt, slots, H, D, nblk, bits, stride=None):
     return host(pool), ref
 
 
+def _check_write(got, ref, v, in_dt, slots, H, D, bits, stride=None):
+    """Bytes outside the written slots untouched; the written slots' codes
+    and scales tie-aware against the oracle's FP64 encoder."""
+    keep = (slots >= 0) & (slots < got.shape[0] * 16)
+    written = tq_written_mask(got.shape[0], bits, H, D, slots[keep])
+    assert (got[~written] == ref[~written]).all(), "bytes outside the written slots changed"
+    gc, gs = tq_rows_by_slot(got, slots[keep], bits, H, D)
+    st = tq_compare(gc, gs, v[keep], in_dt, bits, H, D, in_token_stride=stride)
+    say(f"  {st}")
+    return st
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_tq_population_write_whole_pool_bit_exact(bits):
+def test_tq_population_write(bits):
     lay = W.layout(3, num_seqs=6, len_hi=3000)
     start, cu, _ = W.positions_all(lay)
     T = int(cu[-1])
@@ -49,8 +65,8 @@ def test_tq_population_write_whole_pool_bit_exact(bits):
     v = W.kv_tokens(3, T, "v")
     say(f"TQ{bits} V population write: T={T} blocks={lay.num_blocks}")
     got, ref = _write_both(v, "bf16", slots, 8, 128, lay.num_blocks, bits)
-    bad = np.argwhere(got != ref)
-    assert bad.size == 0, f"{len(bad)} bytes differ, first at {bad[:4].tolist()}"
+    st = _check_write(got, ref, v, "bf16", slots, 8, 128, bits)
+    assert st["groups_out_of_fp32_range"] == 0
 
 
 def _special_rows(T, H, D, seed):
@@ -71,7 +87,7 @@ def _special_rows(T, H, D, seed):
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_tq_write_fp32_strided_special_groups_bit_exact(bits):
+def test_tq_write_fp32_strided_special_groups(bits):
     T, H, D = 37, 4, 64
     stride = H * D + 64
     x = _special_rows(T, H, D, bits)
@@ -81,13 +97,15 @@ def test_tq_write_fp32_strided_special_groups_bit_exact(bits):
     slots = np.random.default_rng(3).permutation(48)[:T].astype(np.int64)
     say(f"TQ{bits} V write from strided FP32 rows: T={T} H={H} D={D}")
     got, ref = _write_both(v, "f32", slots, H, D, 3, bits, stride=stride)
-    assert (got == ref).all()
+    _check_write(got, ref, v, "f32", slots, H, D, bits, stride=stride)
 
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_tq_write_extreme_magnitudes_bit_exact(bits):
+def test_tq_write_extreme_magnitudes(bits):
     """Groups whose sum of squares is subnormal, underflows to 0, or
-    overflows to infinity (BF16 input spans the whole FP32 range)."""
+    overflows to infinity in FP32 (BF16 input spans the whole FP32 range):
+    their scale bytes (0, or saturated at 448) equal the definition's; codes
+    are compared only where the FP32 sum of squares is a normal number."""
     T, H, D = 8, 2, 32
     rng = np.random.default_rng(40 + bits)
     x = rng.standard_normal((T, H, D)).astype(np.float32)
@@ -101,7 +119,8 @@ def test_tq_write_extreme_magnitudes_bit_exact(bits):
     slots = np.arange(T, dtype=np.int64)[::-1].copy()
     say(f"TQ{bits} V write of extreme magnitudes")
     got, ref = _write_both(v, "bf16", slots, H, D, 1, bits)
-    assert (got == ref).all()
+    st = _check_write(got, ref, v, "bf16", slots, H, D, bits)
+    assert st["groups_out_of_fp32_range"] > 0
 
 
 def test_tq3_write_of_the_hand_worked_ties_group():
@@ -231,8 +250,8 @@ def test_tq_decode_window_and_sinks(bits):
 
 
 def test_tq_write_then_decode_round_trip():
-    """The library's own write feeds its decode; the oracle decodes the
-    oracle's write of the same rows (bit-identical pools)."""
+    """The library's own write feeds its decode; the write is held to the
+    tie-aware bar, and the oracle decodes the pool the library wrote."""
     lay = W.layout_for(2, [70, 513])
     start, cu, _ = W.positions_all(lay)
     T = int(cu[-1])
@@ -246,9 +265,11 @@ def test_tq_write_then_decode_round_trip():
     pkv.cache_write_v(dev(v), dev(slots), pool, tq_bits=3)
     kp = _k_pool(lay, 8, 128, "bf16", 831)
     q = W.queries(2, lay.num_seqs)
-    ref = oracle.paged_decode(q, "bf16", kp, "bf16", ref_pool, "tq3", lay.block_tables,
-                              lay.seq_lens, num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
-                              head_dim_v=128, block_size=16, scale=128 ** -0.5, nthreads=8)
     got = host(pkv.paged_decode_attn(dev(q), dev(kp), pool, dev(lay.block_tables),
                                      dev(lay.seq_lens), scale=128 ** -0.5, v_tq_bits=3))
-    assert (host(pool) == ref_pool).all() and attn_err(got, ref) <= ATTN_TOL
+    gpool = host(pool)
+    _check_write(gpool, ref_pool, v, "bf16", slots, 8, 128, 3)
+    ref = oracle.paged_decode(q, "bf16", kp, "bf16", gpool, "tq3", lay.block_tables,
+                              lay.seq_lens, num_q_heads=32, num_kv_heads=8, head_dim_qk=128,
+                              head_dim_v=128, block_size=16, scale=128 ** -0.5, nthreads=8)
+    assert attn_err(got, ref) <= ATTN_TOL

@@ -131,8 +131,11 @@ def check_k(got, ref, slots_np, cache_dtype, sentinel_check=True):
         assert rows_g[~written].tobytes() == rows_r[~written].tobytes(), "rows outside the slots changed"
     g, r = rows_g[written], rows_r[written]
     if cache_dtype == "bf16":
-        ok = bf16_ok(g, r)
+        st = {}
+        ok = bf16_ok(g, r, stats=st)
         exact = float((g == r).mean())
+        say(f"  BF16 K: {st['n']} elements, {st['floor_only']} more than 1 ulp apart within "
+            f"the 2^-20 row floor")
     elif cache_dtype == "fp8":
         ok = e4m3_ok(g, r)
         exact = float((g == r).mean())

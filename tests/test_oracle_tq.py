@@ -22,7 +22,7 @@ from scipy.stats import norm
 
 import oracle
 import pkv_workloads as W
-from _util import tq_scale_mask
+from _util import tq_compare, tq_scale_mask, tq_unpack
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -106,12 +106,10 @@ def test_group_codes_are_nearest_levels_and_norm_is_corrected(bits):
                 # by the scale and find each element's level
                 scale = np.linalg.norm(d) / np.linalg.norm(levels[np.argmin(dist, axis=1)])
                 chosen = np.argmin(np.abs(d[:, None] / scale - levels[None, :]), axis=1)
-                # each element's level is a nearest level of x / rms (ties, and
-                # the FP32 rounding of x / rms in the decision, allowed)
-                assert np.allclose(dist[np.arange(16), chosen], dist.min(axis=1),
-                                   atol=1e-6 * np.abs(u).max())
+                # each element's level is a nearest level of x / rms (ties allowed)
+                assert np.allclose(dist[np.arange(16), chosen], dist.min(axis=1), atol=1e-9)
                 assert np.sign(d[g != 0]).tolist() == np.sign(g[g != 0]).tolist()
-                assert abs(np.linalg.norm(d) / np.linalg.norm(g) - 1) <= 2.0 ** -4 + 1e-6
+                assert abs(np.linalg.norm(d) / np.linalg.norm(g) - 1) <= 2.0 ** -4 + 1e-12
 
 
 def test_power_of_two_scaling_only_scales():
@@ -190,3 +188,55 @@ def test_hand_worked_ties_example():
     enc = _encode(x, 3)
     assert bytes(enc[:6]) == bytes(int(b, 16) for b in rows["bytes"])
     assert enc[16 * 6] == int(rows["scale"][0], 16)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_encoder_diagnostics_match_the_written_pool_and_the_unpacker(bits):
+    """tq_encode_diag's codes and scales are those the oracle writes, read
+    back by the tests' unpacker of the documented layout; its u is x / rms."""
+    rng = np.random.default_rng(20 + bits)
+    T, H, D = 40, 3, 48
+    x = (rng.standard_normal((T, H, D)) * np.exp(rng.uniform(-3, 3, (T, H, 1)))).astype(np.float32)
+    x[7, 1, 16:32] = 0.0
+    pool = _encode(x, bits).reshape(-1, oracle.tq_block_bytes(bits, 16, H, D))
+    codes, scales = tq_unpack(pool, bits, H, D)
+    u, ss, ratio, dc, ds = oracle.tq_encode_diag(x, "f32", bits, num_kv_heads=H, head_dim_v=D)
+    assert (codes.reshape(-1, H, D)[:T] == dc).all()
+    assert (scales.reshape(-1, H, D // 16)[:T] == ds).all()
+    g = x.astype(np.float64).reshape(T, H, D // 16, 16)
+    assert np.allclose(ss, (g * g).sum(-1), rtol=1e-14, atol=0)
+    rms = np.sqrt((g * g).mean(-1, keepdims=True))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        want_u = np.where(rms > 0, g / rms, 0.0)
+    assert np.allclose(u.reshape(g.shape), want_u, rtol=1e-14, atol=0)
+    assert ((ratio == 0) == (ss == 0)).all()
+
+
+@pytest.mark.parametrize("bits", [3, 4])
+def test_tie_aware_comparison_accepts_the_oracle_and_rejects_planted_errors(bits):
+    rng = np.random.default_rng(30 + bits)
+    T, H, D = 64, 2, 64
+    x = rng.standard_normal((T, H, D)).astype(np.float32)
+    _, _, _, codes, scales = oracle.tq_encode_diag(x, "f32", bits, num_kv_heads=H, head_dim_v=D)
+    st = tq_compare(codes, scales, x, "f32", bits, H, D)
+    assert st["scales_differ"] == 0 and st["near_tie_codes_differ"] == 0
+    u = oracle.tq_encode_diag(x, "f32", bits, num_kv_heads=H, head_dim_v=D)[0]
+    # a code moved one magnitude where |u| is far from every midpoint
+    mags = oracle.f64_from_e4m3(oracle.tq_codebook(bits))
+    thr = (mags[1:] + mags[:-1]) / 2
+    far = np.abs(np.abs(u)[..., None] - thr).min(-1) > 0.05
+    t, h, d = np.argwhere(far & ((codes & ((1 << (bits - 1)) - 1)) == 1))[0]
+    bad = codes.copy()
+    bad[t, h, d] -= 1
+    with pytest.raises(AssertionError):
+        tq_compare(bad, scales, x, "f32", bits, H, D)
+    # a sign flipped
+    bad = codes.copy()
+    bad[t, h, d] ^= 1 << (bits - 1)
+    with pytest.raises(AssertionError):
+        tq_compare(bad, scales, x, "f32", bits, H, D)
+    # a scale byte one step off, away from an E4M3 midpoint
+    bad = scales.copy()
+    bad[0, 0, 0] += 1
+    with pytest.raises(AssertionError):
+        tq_compare(codes, bad, x, "f32", bits, H, D)
