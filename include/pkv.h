@@ -9,6 +9,9 @@
  *   pkv_cache_write_v       V reshape-and-cache copy (or E4M3 / TurboQuant-style
  *                           b-bit store) into the V pool
  *   pkv_paged_decode_attn   one-query-token GQA attention through the tables
+ *   pkv_paged_decode_attn_noalloc  the same, its split partials in a device
+ *                           scratch of the library (for callers that cannot
+ *                           allocate)
  *   pkv_paged_prefill_attn  causal attention of N new tokens per sequence
  *   pkv_mla_cache_assemble  MLA cache rows [latent | k_rope] -> K, [latent | 0] -> V
  *
@@ -25,7 +28,8 @@
  * Pointers.  Every array argument is DEVICE memory owned by the caller (for
  *   example a torch tensor's data pointer).  The library never allocates,
  *   frees, copies between host and device, synchronises, or keeps state
- *   between calls.  `stream` is a hipStream_t (NULL = the null stream).
+ *   between calls (pkv_paged_decode_attn_noalloc excepted: it keeps one
+ *   device scratch array per GPU, allocated with the code object).  `stream` is a hipStream_t (NULL = the null stream).
  * Pool layout ("NHD"), [p1] doc of reshape_and_cache_fp8 and [p2] module
  *   invariants: a pool is [num_blocks, block_size, num_kv_heads, head_dim],
  *   row-major, addressed from its base.  A slot is a flat row index
@@ -319,6 +323,43 @@ int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_strid
                           uint32_t q_rope_dim, const float* gate, float* out,
                           uint32_t split_tokens, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * pkv_paged_decode_attn_noalloc -- pkv_paged_decode_attn without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, computation, supported set and status codes as
+ * pkv_paged_decode_attn (same kernels and split plan, so the output is
+ * bit-identical to it), except that the split-K partials live in a device
+ * scratch array of PKV_DECODE_SCRATCH_BYTES held by the library (one per GPU,
+ * kept until the process ends; its address is looked up on the first call
+ * on a device, with that device current).  The call allocates nothing and
+ * calls no allocating routine.
+ *   Limit: when pkv_decode_workspace_bytes(...) for these sizes exceeds
+ *   PKV_DECODE_SCRATCH_BYTES (32 MiB: e.g. 256 sequences x 32 query heads
+ *   need ~8.5 MiB, 64 x 64 ~10.6 MiB), PKV_ERR_WORKSPACE before any launch.
+ *   The scratch needs no initialisation and keeps the last call's contents.
+ *   Calls on one GPU that may overlap in time (other streams, other host
+ *   threads with other streams) share it and RACE: serialise them on one
+ *   stream, or use pkv_paged_decode_attn with workspaces of their own.
+ *   `stream`, when not NULL, must belong to the current device, else
+ *   PKV_ERR_INVALID.
+ */
+#define PKV_DECODE_SCRATCH_BYTES (32u << 20)
+
+int pkv_paged_decode_attn_noalloc(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
+                                  const void* k_cache, pkv_dtype k_dtype, float k_scale,
+                                  const void* v_cache, pkv_dtype v_dtype, float v_scale,
+                                  const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                                  const int32_t* seq_lens, uint32_t num_seqs,
+                                  uint32_t num_blocks, uint32_t num_q_heads,
+                                  uint32_t num_kv_heads, uint32_t head_dim_qk,
+                                  uint32_t head_dim_v, uint32_t block_size, float scale,
+                                  uint32_t sliding_window, const float* sinks,
+                                  int q_rope, float q_rope_theta, uint32_t q_rope_offset,
+                                  uint32_t q_rope_dim, const float* gate, float* out,
+                                  uint32_t split_tokens, void* stream);
 
 /*
  * pkv_paged_prefill_attn -- [p1] "batched prefill variants (N tokens)" of

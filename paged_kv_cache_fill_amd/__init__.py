@@ -9,7 +9,7 @@ every call raises ``RuntimeError``.
 
 Functions (same names as the C calls without the ``pkv_`` prefix):
   fill_slots, cache_write_k_fused, cache_write_v, decode_workspace_bytes,
-  paged_decode_attn, paged_prefill_attn, mla_cache_assemble
+  paged_decode_attn, paged_decode_attn_noalloc, paged_prefill_attn, mla_cache_assemble
 """
 from __future__ import annotations
 
@@ -19,13 +19,14 @@ import os
 import torch
 
 __all__ = ["fill_slots", "cache_write_k_fused", "cache_write_v", "decode_workspace_bytes",
-           "paged_decode_attn", "paged_prefill_attn", "mla_cache_assemble", "v_block_bytes",
+           "paged_decode_attn", "paged_decode_attn_noalloc", "paged_prefill_attn", "mla_cache_assemble", "v_block_bytes",
            "tq_codebook", "library_path", "load", "PkvError"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libpkv.so")
 
 BF16, FP8_E4M3, FP32 = 0, 1, 2
+DECODE_SCRATCH_BYTES = 32 << 20          # PKV_DECODE_SCRATCH_BYTES
 TQ2, TQ3, TQ4 = 3, 4, 5                  # TurboQuant-style V cache formats (see pkv.h)
 _DT = {torch.bfloat16: BF16, torch.float8_e4m3fn: FP8_E4M3, torch.uint8: FP8_E4M3,
        torch.float32: FP32}
@@ -44,6 +45,9 @@ _SIGNATURES = {
     "pkv_paged_decode_attn": ([_P, _I32, _U64, _P, _I32, _F32, _P, _I32, _F32, _P, _U32, _P,
                                _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32, _U32, _P, _I32,
                                _F32, _U32, _U32, _P, _P, _U32, _P, _SZ, _P], _I32),
+    "pkv_paged_decode_attn_noalloc": ([_P, _I32, _U64, _P, _I32, _F32, _P, _I32, _F32, _P, _U32,
+                                       _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32, _U32,
+                                       _P, _I32, _F32, _U32, _U32, _P, _P, _U32, _P], _I32),
     "pkv_paged_prefill_attn": ([_P, _I32, _U64, _P, _U32, _U32, _P, _I32, _F32, _P, _I32, _F32,
                                 _P, _U32, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32,
                                 _U32, _P, _P, _P], _I32),
@@ -239,20 +243,12 @@ def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim_v, max_
                                                  sliding_window, split_tokens))
 
 
-def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: float,
-                      k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0,
-                      sinks=None, gate=None, out=None, q_rope: bool = False,
-                      q_rope_theta: float = 10000.0, q_rope_offset: int = 0,
-                      q_rope_dim: int = 0, split_tokens: int = 0, workspace=None,
-                      v_tq_bits: int = 0):
-    """One-query-token paged decode attention (pkv_paged_decode_attn).
-
-    q [S, Hq, Dqk]; k_cache [nb, B, Hkv, Dqk]; v_cache [nb, B, Hkv, Dv];
-    block_tables int32 [S, M]; seq_lens int32 [S]; sinks FP32 [Hq] or None;
-    gate FP32 [S, Hq, Dv] or None.  Returns out FP32 [S, Hq, Dv].
-    ``workspace`` (uint8 device tensor) is allocated here when not given.
-    """
-    _dev(q, k_cache, v_cache, block_tables, seq_lens, sinks, gate, out, workspace)
+def _decode_args(q, k_cache, v_cache, block_tables, seq_lens, *, scale, k_scale, v_scale,
+                 sliding_window, sinks, gate, out, q_rope, q_rope_theta, q_rope_offset,
+                 q_rope_dim, split_tokens, v_tq_bits, alloc_out):
+    """Checks the decode arguments; returns (leading C arguments up to and
+    including split_tokens, out, (S, Hq, Hkv, Dv, M, B))."""
+    _dev(q, k_cache, v_cache, block_tables, seq_lens, sinks, gate, out)
     nb, B, Hkv, Dqk = _pool(k_cache, "k_cache")
     if v_tq_bits:
         Dv = Dqk
@@ -279,21 +275,63 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: flo
                               not sinks.is_contiguous()):
         raise ValueError("sinks must be FP32 [Hq] contiguous")
     if out is None:
+        if not alloc_out:
+            raise ValueError("out must be given (FP32 [S, Hq, Dv])")
         out = torch.empty((S, Hq, Dv), dtype=torch.float32, device=q.device)
     elif out.dtype != torch.float32 or out.shape != (S, Hq, Dv) or not out.is_contiguous():
         raise ValueError("out must be FP32 [S, Hq, Dv] contiguous")
     M = block_tables.shape[1]
+    q_stride = q.stride(0) if S > 1 else Hq * Dqk
+    args = (_ptr(q), _dtype(q), q_stride, _ptr(k_cache), _dtype(k_cache), k_scale,
+            _ptr(v_cache), v_dt, v_scale, _ptr(block_tables), M, _ptr(seq_lens), S, nb, Hq, Hkv,
+            Dqk, Dv, B, scale, sliding_window, _ptr(sinks), int(bool(q_rope)), q_rope_theta,
+            q_rope_offset, q_rope_dim, _ptr(gate), _ptr(out), split_tokens)
+    return args, out, (S, Hq, Hkv, Dv, M, B)
+
+
+def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: float,
+                      k_scale: float = 1.0, v_scale: float = 1.0, sliding_window: int = 0,
+                      sinks=None, gate=None, out=None, q_rope: bool = False,
+                      q_rope_theta: float = 10000.0, q_rope_offset: int = 0,
+                      q_rope_dim: int = 0, split_tokens: int = 0, workspace=None,
+                      v_tq_bits: int = 0):
+    """One-query-token paged decode attention (pkv_paged_decode_attn).
+
+    q [S, Hq, Dqk]; k_cache [nb, B, Hkv, Dqk]; v_cache [nb, B, Hkv, Dv];
+    block_tables int32 [S, M]; seq_lens int32 [S]; sinks FP32 [Hq] or None;
+    gate FP32 [S, Hq, Dv] or None.  Returns out FP32 [S, Hq, Dv].
+    ``workspace`` (uint8 device tensor) is allocated here when not given.
+    """
+    _dev(workspace)
+    args, out, (S, Hq, Hkv, Dv, M, B) = _decode_args(
+        q, k_cache, v_cache, block_tables, seq_lens, scale=scale, k_scale=k_scale,
+        v_scale=v_scale, sliding_window=sliding_window, sinks=sinks, gate=gate, out=out,
+        q_rope=q_rope, q_rope_theta=q_rope_theta, q_rope_offset=q_rope_offset,
+        q_rope_dim=q_rope_dim, split_tokens=split_tokens, v_tq_bits=v_tq_bits, alloc_out=True)
     need = decode_workspace_bytes(S, Hq, Hkv, Dv, M, B, split_tokens, sliding_window) if S else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    q_stride = q.stride(0) if S > 1 else Hq * Dqk
-    _check(load().pkv_paged_decode_attn(
-        _ptr(q), _dtype(q), q_stride, _ptr(k_cache), _dtype(k_cache), k_scale, _ptr(v_cache),
-        v_dt, v_scale, _ptr(block_tables), M, _ptr(seq_lens), S, nb, Hq, Hkv, Dqk, Dv,
-        B, scale, sliding_window, _ptr(sinks), int(bool(q_rope)), q_rope_theta, q_rope_offset,
-        q_rope_dim, _ptr(gate), _ptr(out),
-        split_tokens, _ptr(workspace), ws_bytes, _stream()))
+    _check(load().pkv_paged_decode_attn(*args, _ptr(workspace), ws_bytes, _stream()))
+    return out
+
+
+def paged_decode_attn_noalloc(q, k_cache, v_cache, block_tables, seq_lens, *, out,
+                              scale: float, k_scale: float = 1.0, v_scale: float = 1.0,
+                              sliding_window: int = 0, sinks=None, gate=None,
+                              q_rope: bool = False, q_rope_theta: float = 10000.0,
+                              q_rope_offset: int = 0, q_rope_dim: int = 0,
+                              split_tokens: int = 0, v_tq_bits: int = 0):
+    """paged_decode_attn with the split partials in the library's device
+    scratch (pkv_paged_decode_attn_noalloc): allocates nothing, so ``out``
+    must be given.  Calls that may overlap on one GPU share the scratch and
+    race; at most PKV_DECODE_SCRATCH_BYTES (32 MiB) of partials."""
+    args, out, _ = _decode_args(
+        q, k_cache, v_cache, block_tables, seq_lens, scale=scale, k_scale=k_scale,
+        v_scale=v_scale, sliding_window=sliding_window, sinks=sinks, gate=gate, out=out,
+        q_rope=q_rope, q_rope_theta=q_rope_theta, q_rope_offset=q_rope_offset,
+        q_rope_dim=q_rope_dim, split_tokens=split_tokens, v_tq_bits=v_tq_bits, alloc_out=False)
+    _check(load().pkv_paged_decode_attn_noalloc(*args, _stream()))
     return out
 
 

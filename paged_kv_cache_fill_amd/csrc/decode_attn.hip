@@ -33,6 +33,8 @@
 //
 // FP32 caches (VALU path).  Four tokens per wave step (16 lanes per token
 // row, 16-byte loads), one online-softmax stream per row, merged at the end.
+#include <mutex>
+
 #include "attn_common.h"
 
 namespace pkv {
@@ -1111,6 +1113,50 @@ static Plan make_plan(uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_h
     return p;
 }
 
+// Device scratch of pkv_paged_decode_attn_noalloc: the split partials live
+// here instead of in a caller workspace.  Each GPU the library runs on holds
+// its own copy for the life of the process.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address): the address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[PKV_DECODE_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on the first
+// call on that device, with the device current).  `stream`, when not NULL,
+// must belong to the current device.
+static int scratch_address(hipStream_t stream, void** out)
+{
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(PKV_ERR_HIP, "paged_decode_attn_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn_noalloc: device %d beyond %d", dev, kMaxDevices);
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess)
+            return fail(PKV_ERR_HIP, "paged_decode_attn_noalloc: hipStreamGetDevice: %s", hipGetErrorString(e));
+        if (sdev != dev)
+            return fail(PKV_ERR_INVALID, "paged_decode_attn_noalloc: the stream belongs to device %d, the current device is %d",
+                        (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(PKV_ERR_HIP, "paged_decode_attn_noalloc: hipGetSymbolAddress(scratch): %s",
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return PKV_OK;
+}
+
 }  // namespace pkv
 
 extern "C" size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
@@ -1132,21 +1178,22 @@ extern "C" size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_h
     return a > b ? a : b;
 }
 
-extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
-                                     const void* k_cache, pkv_dtype k_dtype, float k_scale,
-                                     const void* v_cache, pkv_dtype v_dtype, float v_scale,
-                                     const int32_t* block_tables, uint32_t max_blocks_per_seq,
-                                     const int32_t* seq_lens, uint32_t num_seqs,
-                                     uint32_t num_blocks, uint32_t num_q_heads,
-                                     uint32_t num_kv_heads, uint32_t head_dim_qk,
-                                     uint32_t head_dim_v, uint32_t block_size, float scale,
-                                     uint32_t sliding_window, const float* sinks,
-                                     int q_rope, float q_rope_theta, uint32_t q_rope_offset,
-                                     uint32_t q_rope_dim, const float* gate, float* out,
-                                     uint32_t split_tokens, void* workspace,
-                                     size_t workspace_bytes, void* stream)
+namespace pkv {
+
+// The decode call; with `static_scratch` the split partials go to the
+// library's device scratch instead of `workspace` (which is then ignored).
+static int paged_decode(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
+                        const void* k_cache, pkv_dtype k_dtype, float k_scale,
+                        const void* v_cache, pkv_dtype v_dtype, float v_scale,
+                        const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
+                        uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
+                        uint32_t head_dim_v, uint32_t block_size, float scale,
+                        uint32_t sliding_window, const float* sinks, int q_rope,
+                        float q_rope_theta, uint32_t q_rope_offset, uint32_t q_rope_dim,
+                        const float* gate, float* out, uint32_t split_tokens, void* workspace,
+                        size_t workspace_bytes, bool static_scratch, void* stream)
 {
-    using namespace pkv;
     clear_error();
     if (num_seqs == 0)
         return PKV_OK;
@@ -1202,7 +1249,17 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     const Plan plan = make_plan(num_seqs, num_q_heads, num_kv_heads, head_dim_v,
                                 max_blocks_per_seq, block_size, sliding_window, split_tokens,
                                 mfma_path);
-    if (plan.workspace > 0 && (workspace_bytes < plan.workspace || !workspace))
+    if (static_scratch) {
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (plan.workspace > PKV_DECODE_SCRATCH_BYTES)
+            return fail(PKV_ERR_WORKSPACE, "paged_decode_attn_noalloc: the split partials need %zu bytes, the "
+                        "library's scratch holds %zu; call pkv_paged_decode_attn with a workspace",
+                        plan.workspace, (size_t)PKV_DECODE_SCRATCH_BYTES);
+    }
+    // the remaining checks need no device; the scratch address is looked up
+    // only once they have passed
+    if (!static_scratch && plan.workspace > 0 && (workspace_bytes < plan.workspace || !workspace))
         return fail(PKV_ERR_WORKSPACE, "paged_decode_attn: workspace of %zu bytes needed, %zu given",
                     plan.workspace, workspace_bytes);
     if (plan.workspace > 0 && !aligned16(workspace))
@@ -1217,6 +1274,12 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
     if (mfma_path && ((uint64_t)num_seqs * num_kv_heads > 0x7FFFFFFFull ||
                       (uint64_t)plan.ranges * num_kv_heads > 0x7FFFFFFFull))
         return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: too many sequences for one call");
+    if (static_scratch && plan.workspace > 0) {
+        const int rc = scratch_address((hipStream_t)stream, &workspace);
+        if (rc)
+            return rc;
+        workspace_bytes = PKV_DECODE_SCRATCH_BYTES;
+    }
 
     DecodeArgs a{};
     a.q = q;
@@ -1307,4 +1370,46 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
         rc = check_launch("paged_decode_attn merge");
     }
     return rc;
+}
+
+}  // namespace pkv
+
+extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
+                                     const void* k_cache, pkv_dtype k_dtype, float k_scale,
+                                     const void* v_cache, pkv_dtype v_dtype, float v_scale,
+                                     const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                                     const int32_t* seq_lens, uint32_t num_seqs,
+                                     uint32_t num_blocks, uint32_t num_q_heads,
+                                     uint32_t num_kv_heads, uint32_t head_dim_qk,
+                                     uint32_t head_dim_v, uint32_t block_size, float scale,
+                                     uint32_t sliding_window, const float* sinks,
+                                     int q_rope, float q_rope_theta, uint32_t q_rope_offset,
+                                     uint32_t q_rope_dim, const float* gate, float* out,
+                                     uint32_t split_tokens, void* workspace,
+                                     size_t workspace_bytes, void* stream)
+{
+    return pkv::paged_decode(q, q_dtype, q_seq_stride, k_cache, k_dtype, k_scale, v_cache,
+                             v_dtype, v_scale, block_tables, max_blocks_per_seq, seq_lens,
+                             num_seqs, num_blocks, num_q_heads, num_kv_heads, head_dim_qk,
+                             head_dim_v, block_size, scale, sliding_window, sinks, q_rope,
+                             q_rope_theta, q_rope_offset, q_rope_dim, gate, out, split_tokens,
+                             workspace, workspace_bytes, false, stream);
+}
+
+extern "C" int pkv_paged_decode_attn_noalloc(
+    const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride, const void* k_cache,
+    pkv_dtype k_dtype, float k_scale, const void* v_cache, pkv_dtype v_dtype, float v_scale,
+    const int32_t* block_tables, uint32_t max_blocks_per_seq, const int32_t* seq_lens,
+    uint32_t num_seqs, uint32_t num_blocks, uint32_t num_q_heads, uint32_t num_kv_heads,
+    uint32_t head_dim_qk, uint32_t head_dim_v, uint32_t block_size, float scale,
+    uint32_t sliding_window, const float* sinks, int q_rope, float q_rope_theta,
+    uint32_t q_rope_offset, uint32_t q_rope_dim, const float* gate, float* out,
+    uint32_t split_tokens, void* stream)
+{
+    return pkv::paged_decode(q, q_dtype, q_seq_stride, k_cache, k_dtype, k_scale, v_cache,
+                             v_dtype, v_scale, block_tables, max_blocks_per_seq, seq_lens,
+                             num_seqs, num_blocks, num_q_heads, num_kv_heads, head_dim_qk,
+                             head_dim_v, block_size, scale, sliding_window, sinks, q_rope,
+                             q_rope_theta, q_rope_offset, q_rope_dim, gate, out, split_tokens,
+                             nullptr, 0, true, stream);
 }

@@ -145,6 +145,38 @@ def test_decode_validation(lib):
     assert "65535 sequences" in _err(lib)
 
 
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode rejects, before any device call, what the
+    workspace entry point rejects, and a plan whose split partials exceed
+    the library's static scratch."""
+    def call(**kw):
+        a = dict(q=FAKE, qd=0, qs=32 * 128, k=FAKE, kd=0, ks=1.0, v=FAKE, vd=0, vs=1.0, bt=FAKE,
+                 M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1, win=0,
+                 sinks=None, qr=0, qt=1e4, qo=0, qdim=0, gate=None, out=FAKE, split=0)
+        a.update(kw)
+        return lib.pkv_paged_decode_attn_noalloc(*a.values(), None)
+    assert call(S=0) == 0                         # no work: nothing launched
+    assert call(Hq=30) == -1
+    assert call(B=32) == -2
+    assert call(scale=float("nan")) == -1
+    # 1024 sequences x 64 query heads x 4096-block tables: the balanced plan's
+    # partials are far beyond 32 MiB
+    need = lib.pkv_decode_workspace_bytes(1024, 64, 8, 128, 4096, 16, 0, 0)
+    assert need > pkv.DECODE_SCRATCH_BYTES
+    assert call(S=1024, Hq=64, qs=64 * 128, M=4096) == -3
+    assert "scratch" in _err(lib)
+    # an explicit split size too (FP32 path, 16-token splits of a long table)
+    assert lib.pkv_decode_workspace_bytes(64, 64, 64, 128, 65535, 16, 0, 16) > \
+        pkv.DECODE_SCRATCH_BYTES
+    assert call(S=64, Hq=64, Hkv=64, qs=64 * 128, M=65535, split=16, qd=2, kd=2, vd=2) == -3
+
+
+def test_decode_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define PKV_DECODE_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pkv.DECODE_SCRATCH_BYTES
+
+
 def test_workspace_query(lib):
     assert lib.pkv_decode_workspace_bytes(1, 4, 2, 64, 4, 16, 0, 0) == 0     # one split
     n = lib.pkv_decode_workspace_bytes(256, 32, 8, 128, 512, 16, 0, 0)
