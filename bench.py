@@ -84,6 +84,10 @@ def parse():
     p.add_argument("--workload", default="decode_bf16_256seq",
                    choices=sorted(WORKLOADS) + sorted(PREFILL_WORKLOADS) + sorted(AUX_WORKLOADS))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--only", action="store_true",
+                   help="with the default workload, leave out the second bar configuration "
+                        "(decode_fp8k_64seq_long), which is otherwise run after it and "
+                        "reported in the same line")
     p.add_argument("--split-tokens", type=int, default=0)
     p.add_argument("--no-graph", action="store_true",
                    help="time the decode step as eager launches only (by default also as a "
@@ -182,13 +186,29 @@ def main():
         run_aux(args)
         return
 
+    result = run_decode(args.workload, args)
+    if args.workload == "decode_bf16_256seq" and not args.only:
+        # the second bar configuration in the same line: long-context decode
+        # over an E4M3 K cache (64 sequences, U[16384, 32768])
+        import torch
+        torch.cuda.empty_cache()
+        second = run_decode("decode_fp8k_64seq_long", args)
+        result["decode_fp8k_64seq_long"] = {
+            k: second[k] for k in ("config", "dtype", "value", "unit", "ms_per_step",
+                                   "step_launch", "decode_attn", "cache_write", "roofline",
+                                   "cpu_baseline")}
+    print(json.dumps(result), flush=True)
+
+
+def run_decode(name, args):
+    """The decode-step benchmark of one workload; returns its result dict."""
     import torch
 
     import paged_kv_cache_fill_amd as pkv
     import pkv_workloads as W
 
     pkv.load()
-    idx, v_kind, window, use_sinks = WORKLOADS[args.workload]
+    idx, v_kind, window, use_sinks = WORKLOADS[name]
     v_fp8 = v_kind == "fp8"
     tq = int(v_kind[2]) if v_kind.startswith("tq") else 0
     vb = v_elem_bytes(v_kind)
@@ -199,7 +219,7 @@ def main():
     fp8 = cfg["k_cache_dtype"] == "fp8"
     dev = torch.device("cuda")
     stream = torch.cuda.current_stream()
-    log(f"workload {args.workload}: {S} seqs, {lay.total_tokens} tokens, pool {lay.num_blocks} blocks")
+    log(f"workload {name}: {S} seqs, {lay.total_tokens} tokens, pool {lay.num_blocks} blocks")
 
     # ---------------- pools and the population write ----------------
     lens = lay.seq_lens.astype(np.int64)
@@ -350,7 +370,7 @@ def main():
               + vwrite_bytes(S, Hkv, Dv, 2, vb) + slots_bytes(S, S))
     value = step_b / (ms_per_step * 1e-3) / 1e9
     achieved = dec_b / (attn_ms * 1e-3) / 1e9
-    traffic = traffic_from_profile(kernel_source_hash(), args.workload)
+    traffic = traffic_from_profile(kernel_source_hash(), name)
 
     result = {
         "metric": "paged decode-attn KV GB/s + cache-write tokens/s (fraction of HBM peak)",
@@ -371,7 +391,7 @@ def main():
                       v_kind, f" / {tq}-bit TQ V (e4m3 scale per 16)")
                   + ", f32 accumulate"),
         "data": "synthetic (seeded)",
-        "config": {"workload": args.workload, "num_seqs": S, "seq_len_range": [cfg["len_lo"], cfg["len_hi"]],
+        "config": {"workload": name, "num_seqs": S, "seq_len_range": [cfg["len_lo"], cfg["len_hi"]],
                    "total_tokens": int(lens.sum()), "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim": D, "block_size": B, "sliding_window": window,
                    "sinks": use_sinks, "parallelism": "single GPU"},
@@ -395,7 +415,7 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(idx, lay, k_scale, v_kind, v_scale, window,
                                               None if sinks is None else sinks.cpu().numpy())
-    print(json.dumps(result), flush=True)
+    return result
 
 
 def prefill_flops(lens, qlens, Hq, D, Dv):
@@ -510,7 +530,7 @@ def run_prefill(args):
         "vs_baseline": None,
         "dtype": "bf16 q/K/V, f32 accumulate",
         "data": "synthetic (seeded)",
-        "config": {"workload": args.workload, "num_seqs": S, "chunk": chunk,
+        "config": {"workload": name, "num_seqs": S, "chunk": chunk,
                    "new_tokens": Tc, "total_tokens": int(lens.sum()), "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": B,
                    "parallelism": "single GPU"},
@@ -547,7 +567,6 @@ def run_aux(args):
     cfg = lay.cfg
     Hkv, D, Dv, B = cfg["num_kv_heads"], cfg["head_dim"], cfg["head_dim_v"], 16
     bt = torch.from_numpy(lay.block_tables).to(dev)
-    cores = max(1, min(16, os.cpu_count() or 1))
 
     def timed(fn):
         for _ in range(args.warmup):
@@ -604,17 +623,18 @@ def run_aux(args):
         # the oracle on the same inputs: slots, K write, V write
         kc = np.zeros((lay.num_blocks, B, Hkv, D), np.uint16)
         vc = np.zeros_like(kc)
-        t0 = time.perf_counter()
-        s_ref = oracle.fill_slots(lay.block_tables, start, cu, T, B)
-        oracle.cache_write_k(k_h, "bf16", s_ref, kc, "bf16", num_kv_heads=Hkv, head_dim=D,
-                             block_size=B, norm_weight=w_h, eps=cfg["eps"], pos_t=pos,
-                             theta=cfg["theta"], nthreads=cores)
-        oracle.cache_write_v(v_h, "bf16", s_ref, vc, num_kv_heads=Hkv, head_dim_v=D,
-                             block_size=B)
-        dt = time.perf_counter() - t0
-        cpu = {"value": round(step_b / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-               "kind": "oracle", "sample": f"slots, K write and V write of all {T} tokens, "
-                                           f"{dt:.2f} s"}
+
+        def run(threads):
+            t0 = time.perf_counter()
+            s_ref = oracle.fill_slots(lay.block_tables, start, cu, T, B)
+            oracle.cache_write_k(k_h, "bf16", s_ref, kc, "bf16", num_kv_heads=Hkv, head_dim=D,
+                                 block_size=B, norm_weight=w_h, eps=cfg["eps"], pos_t=pos,
+                                 theta=cfg["theta"], nthreads=threads)
+            oracle.cache_write_v(v_h, "bf16", s_ref, vc, num_kv_heads=Hkv, head_dim_v=D,
+                                 block_size=B)
+            return time.perf_counter() - t0
+
+        cpu = oracle_timing(run, step_b, f"slots, K write and V write of all {T} tokens")
         config = {"workload": args.workload, "num_seqs": S, "tokens": T, "num_kv_heads": Hkv,
                   "head_dim": D, "block_size": B, "pool_blocks": lay.num_blocks,
                   "parallelism": "single GPU"}
@@ -666,15 +686,17 @@ def run_aux(args):
         dom, dom_b = "decode_call", dec_b
         # the oracle: attention over the same pools (copied to the host)
         kp_h, vp_h = kp.cpu().numpy(), vp.cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.paged_decode(q_h, "f32", kp_h, "f32", vp_h, "f32", lay.block_tables,
-                            lay.seq_lens, num_q_heads=H, num_kv_heads=Hkv, head_dim_qk=D,
-                            head_dim_v=Dv, block_size=B, scale=D ** -0.5, q_rope=True,
-                            q_rope_theta=cfg["theta"], q_rope_offset=cfg["rope_offset"],
-                            q_rope_dim=cfg["rotary_dim"], gate=g_h, nthreads=cores)
-        dt = time.perf_counter() - t0
-        cpu = {"value": round(dec_b / dt / 1e9, 4), "unit": "GB/s", "cores": cores,
-               "kind": "oracle", "sample": f"gated decode attention over {n} tokens, {dt:.2f} s"}
+
+        def run(threads):
+            t0 = time.perf_counter()
+            oracle.paged_decode(q_h, "f32", kp_h, "f32", vp_h, "f32", lay.block_tables,
+                                lay.seq_lens, num_q_heads=H, num_kv_heads=Hkv, head_dim_qk=D,
+                                head_dim_v=Dv, block_size=B, scale=D ** -0.5, q_rope=True,
+                                q_rope_theta=cfg["theta"], q_rope_offset=cfg["rope_offset"],
+                                q_rope_dim=cfg["rotary_dim"], gate=g_h, nthreads=threads)
+            return time.perf_counter() - t0
+
+        cpu = oracle_timing(run, dec_b, f"gated decode attention over {n} tokens")
         config = {"workload": args.workload, "num_seqs": 1, "seq_len": n, "num_heads": H,
                   "head_dim_qk": D, "head_dim_v": Dv, "rope_dim": cfg["rotary_dim"],
                   "theta": cfg["theta"], "parallelism": "single GPU"}
@@ -703,83 +725,135 @@ def run_aux(args):
     print(json.dumps(result), flush=True)
 
 
+# tokens of the bounded CPU sample per workload: the first sequences of the
+# workload, in its order, until this many tokens (about 4 s of one-thread
+# oracle work on a 2.7 GHz Xeon core; BF16 K costs ~28 us a token, E4M3 K
+# with 64 query heads ~100 us)
+CPU_SAMPLE_TOKENS = {2: 131072, 3: 40960}
+
+
+def host_cpu():
+    """CPU model, logical CPUs of the host, and the CPUs this process may
+    use (its affinity mask)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return model, os.cpu_count() or 1, usable
+
+
+def oracle_timing(run, nbytes, sample, unit_scale=1e9, unit="GB/s"):
+    """Times run(threads) -- one pass of the oracle over a sample -- on one
+    thread and on all threads this process may use (at most 16, the CPU
+    share of one GPU on the benchmark hosts), median of 3 runs each; nbytes
+    (or flops) / time in `unit`."""
+    model, logical, usable = host_cpu()
+    cores = max(1, min(16, usable))
+    t1 = float(np.median([run(1) for _ in range(3)]))
+    tn = float(np.median([run(cores) for _ in range(3)]))
+    log(f"cpu baseline ({sample}): 1 thread {t1:.3f} s, {cores} threads {tn:.3f} s")
+    return {"value": round(nbytes / tn / unit_scale, 4), "unit": unit, "cores": cores,
+            "kind": "oracle", "value_1thread": round(nbytes / t1 / unit_scale, 4),
+            "value_all": round(nbytes / tn / unit_scale, 4), "seconds_1thread": round(t1, 4),
+            "seconds_all": round(tn, 4), "cpu_model": model, "host_logical_cpus": logical,
+            "usable_cpus": usable, "sample": f"{sample}; median of 3 runs on 1 thread and on "
+                                             f"{cores}"}
+
+
 def cpu_baseline(idx, lay, k_scale, v_kind="bf16", v_scale=1.0, window=0, sinks=None):
-    """The oracle, as it stands, timed on this host on the decode step of the
-    whole workload (slots, K write, V write, attention over every sequence).
-    Pools are drawn on the device by the seeded generator and copied to the
-    host; nothing in them comes from the HIP path."""
+    """The oracle, as it stands, timed on this host on a bounded sample of the
+    decode step: the first sequences of the workload (in its order) up to
+    CPU_SAMPLE_TOKENS tokens -- slots, K write and V write of their new
+    tokens, attention over their whole histories -- on one thread and on
+    all the threads this process may use (at most 16, the CPU share of one
+    GPU on the benchmark hosts), median of 3 runs each.  The sampled
+    sequences' blocks are drawn by the seeded generator on the device and
+    copied to the host; nothing in them comes from the HIP path."""
     import torch
 
     import oracle
     import pkv_workloads as W
-    cores = max(1, min(16, os.cpu_count() or 1))
     cfg = lay.cfg
     Hq, Hkv, D, Dv = cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], cfg["head_dim_v"]
     fp8 = cfg["k_cache_dtype"] == "fp8"
-    shape = (lay.num_blocks, 16, Hkv, D)
-    if fp8:
+    lens_all = lay.seq_lens.astype(np.int64)
+    S = int(np.searchsorted(np.cumsum(lens_all), CPU_SAMPLE_TOKENS.get(idx, 1 << 17)) + 1)
+    S = min(S, lay.num_seqs)
+    lens = lay.seq_lens[:S].copy()
+    nblk = (lens.astype(np.int64) + 15) // 16
+    M = int(nblk.max())
+    ids = np.unique(np.concatenate([lay.block_tables[s, :nblk[s]] for s in range(S)]))
+    remap = np.zeros(lay.num_blocks, np.int32)
+    remap[ids] = np.arange(ids.size, dtype=np.int32)
+    bt = np.zeros((S, M), np.int32)
+    for s in range(S):
+        bt[s, :nblk[s]] = remap[lay.block_tables[s, :nblk[s]]]
+    nb = int(ids.size)
+    shape = (nb, 16, Hkv, D)
+    vshape = (nb, 16, Hkv, Dv)
+
+    def codes(stream, shp):
         g = torch.Generator(device="cuda")
-        g.manual_seed(W.seed_of(idx) * 1000 + W.S_POOLK)
-        mag = torch.randint(0, 0x50, shape, dtype=torch.uint8, device="cuda", generator=g)
-        sign = torch.randint(0, 2, shape, dtype=torch.uint8, device="cuda", generator=g) << 7
-        kp = (mag | sign).cpu().numpy()
-        del mag, sign
+        g.manual_seed(W.seed_of(idx) * 1000 + stream)
+        mag = torch.randint(0, 0x50, shp, dtype=torch.uint8, device="cuda", generator=g)
+        sign = torch.randint(0, 2, shp, dtype=torch.uint8, device="cuda", generator=g) << 7
+        return (mag | sign).cpu().numpy()
+
+    if fp8:
+        kp = codes(W.S_POOLK, shape)
     else:
         kp = W.device_normal(idx, W.S_POOLK, shape, torch.bfloat16, "cuda").view(torch.int16) \
             .cpu().numpy().view(np.uint16)
-    vshape = (lay.num_blocks, 16, Hkv, Dv)
-    v_fp8 = v_kind == "fp8"
     vb = v_elem_bytes(v_kind)
     if v_kind.startswith("tq"):
         # random code bytes and random finite E4M3 scales; a block is one
         # region per kv head: 16 code rows, then Dv / 16 scale rows of 16 bytes
         bits = int(v_kind[2])
-        codes_b, scales_b = 16 * Dv * bits // 8, 16 * Dv // 16
-        g = torch.Generator(device="cuda")
-        g.manual_seed(W.seed_of(idx) * 1000 + W.S_POOLV)
-        codes = torch.randint(0, 256, (lay.num_blocks, Hkv, codes_b), dtype=torch.uint8,
-                              device="cuda", generator=g)
-        scales = torch.randint(0, 0x50, (lay.num_blocks, Hkv, scales_b), dtype=torch.uint8,
-                               device="cuda", generator=g)
-        vp = torch.cat([codes, scales], dim=2).reshape(lay.num_blocks, -1).cpu().numpy()
-        del codes, scales
-    elif v_fp8:
-        g = torch.Generator(device="cuda")
-        g.manual_seed(W.seed_of(idx) * 1000 + W.S_POOLV)
-        mag = torch.randint(0, 0x50, vshape, dtype=torch.uint8, device="cuda", generator=g)
-        sign = torch.randint(0, 2, vshape, dtype=torch.uint8, device="cuda", generator=g) << 7
-        vp = (mag | sign).cpu().numpy()
-        del mag, sign
+        cb, sb = 16 * Dv * bits // 8, 16 * Dv // 16
+        vp = np.concatenate([codes(W.S_POOLV, (nb, Hkv, cb)),
+                             codes(W.S_POOLV + 1, (nb, Hkv, sb)) & 0x7F], axis=2).reshape(nb, -1)
+    elif v_kind == "fp8":
+        vp = codes(W.S_POOLV, vshape)
     else:
         vp = W.device_normal(idx, W.S_POOLV, vshape, torch.bfloat16, "cuda") \
             .view(torch.int16).cpu().numpy().view(np.uint16)
-    vdt = v_kind
     torch.cuda.empty_cache()
-    S = lay.num_seqs
-    q = W.queries(idx, S)
-    k_new = W.kv_tokens(idx, S, "k")
-    v_new = W.kv_tokens(idx, S, "v")
+    q = W.queries(idx, lay.num_seqs)[:S]
+    k_new = W.kv_tokens(idx, lay.num_seqs, "k")[:S]
+    v_new = W.kv_tokens(idx, lay.num_seqs, "v")[:S]
     w = W.norm_weight(idx)
-    start, cu, pos = W.positions_decode(lay)
-    t0 = time.perf_counter()
-    slots = oracle.fill_slots(lay.block_tables, start, cu, S, 16)
-    oracle.cache_write_k(k_new, "bf16", slots, kp, cfg["k_cache_dtype"], num_kv_heads=Hkv,
-                         head_dim=D, block_size=16, norm_weight=w, eps=cfg["eps"], pos_t=pos,
-                         theta=cfg["theta"], k_scale=k_scale, nthreads=cores)
-    oracle.cache_write_v(v_new, "bf16", slots, vp, num_kv_heads=Hkv, head_dim_v=Dv, block_size=16,
-                         cache_dtype=vdt, v_scale=v_scale)
-    oracle.paged_decode(q, "bf16", kp, cfg["k_cache_dtype"], vp, vdt, lay.block_tables,
-                        lay.seq_lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D,
-                        head_dim_v=Dv, block_size=16, scale=D ** -0.5, k_scale=k_scale,
-                        v_scale=v_scale, sliding_window=window, sinks=sinks, nthreads=cores)
-    dt = time.perf_counter() - t0
-    b = (decode_bytes(lay.seq_lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, vb, 2,
-                      window=window, sinks=sinks is not None)
+    sub = W.Layout(idx, lens, bt, nb, -1, 16, cfg)
+    start, cu, pos = W.positions_decode(sub)
+
+    def run(threads):
+        t0 = time.perf_counter()
+        slots = oracle.fill_slots(bt, start, cu, S, 16)
+        oracle.cache_write_k(k_new, "bf16", slots, kp, cfg["k_cache_dtype"], num_kv_heads=Hkv,
+                             head_dim=D, block_size=16, norm_weight=w, eps=cfg["eps"], pos_t=pos,
+                             theta=cfg["theta"], k_scale=k_scale, nthreads=threads)
+        oracle.cache_write_v(v_new, "bf16", slots, vp, num_kv_heads=Hkv, head_dim_v=Dv,
+                             block_size=16, cache_dtype=v_kind, v_scale=v_scale)
+        oracle.paged_decode(q, "bf16", kp, cfg["k_cache_dtype"], vp, v_kind, bt, lens,
+                            num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=Dv,
+                            block_size=16, scale=D ** -0.5, k_scale=k_scale, v_scale=v_scale,
+                            sliding_window=window, sinks=sinks, nthreads=threads)
+        return time.perf_counter() - t0
+
+    b = (decode_bytes(lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, vb, 2, window=window,
+                      sinks=sinks is not None)
          + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2)
          + vwrite_bytes(S, Hkv, Dv, 2, vb) + slots_bytes(S, S))
-    return {"value": round(b / dt / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"the whole decode step of all {S} sequences "
-                      f"({int(lay.seq_lens.astype(np.int64).sum())} tokens), {dt:.2f} s"}
+    return oracle_timing(run, b, f"decode step (slots, K and V write of the new token, "
+                                 f"attention over the whole history) of the first {S} of "
+                                 f"{lay.num_seqs} sequences, {int(lens.sum())} tokens")
 
 
 if __name__ == "__main__":
