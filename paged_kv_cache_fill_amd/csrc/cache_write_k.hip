@@ -241,12 +241,8 @@ __global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(
 #pragma unroll
                 for (int e = 0; e < VEC; ++e)
                     ss = __builtin_fmaf(y[k][e], y[k][e], ss);
-            // butterfly over the row's L lanes (L <= 16), unrolled; the
-            // predicate is wave-uniform
-#pragma unroll
-            for (int m = 1; m < 16; m <<= 1)
-                if ((uint32_t)m < a.L)
-                    ss += __shfl_xor(ss, m, 64);
+            // sum over the row's L lanes (L <= 16, aligned): DPP adds
+            ss = group_sum(ss, a.L);
             const float r = rsqrtf(__builtin_fmaf(ss, a.inv_d, a.eps)) * a.inv_k_scale;
 #pragma unroll
             for (int k = 0; k < NC; ++k)

@@ -45,7 +45,11 @@ constexpr uint32_t kKvPerGroup = 2;     // kv heads (waves) per work-group, at m
 constexpr int kPrefetch = 1;            // cache blocks loaded ahead of the one in use
 constexpr bool kKDirect = false;        // K loaded straight into the operand layout
 constexpr uint64_t kTargetGroups = 768; // (sequence, split, kv group) work-groups wanted
-constexpr uint64_t kTargetWavesF32 = 3072; // FP32 path: (sequence, kv head, split) waves wanted
+// FP32 path: (sequence, kv head, split) waves wanted -- about one per CU.
+// Long splits stream faster here than many short ones: on the 64-head,
+// 4096-token MLA-style workload the call took 58.9 / 60.0 / 61.4 / 63.8 us
+// with 1024- / 512- / 256- / 96-token splits (256 to 2752 waves).
+constexpr uint64_t kTargetWavesF32 = 256;
 constexpr uint32_t kMinChunk = 4;       // blocks per split, automatic choice: at least
 constexpr int kBtRegs = 2;              // table entries held per lane (split mode)
 constexpr uint32_t kMaxChunk = 64 * kBtRegs;  // ... so at most this many blocks per split
@@ -122,12 +126,17 @@ __device__ __forceinline__ uint32_t att_blocks(const DecodeArgs& a, uint32_t s)
     return r.nblk > r.blo ? r.nblk - r.blo : 0u;
 }
 
+// Sum over the wave (DPP within rows, then the gfx950 row swaps).
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v)
 {
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1)
-        v += __shfl_xor(v, d, 64);
-    return v;
+    v += dpp_u32<kDppXor1>(v);
+    v += dpp_u32<kDppXor2>(v);
+    v += dpp_u32<kDppHalfMirror>(v);
+    v += dpp_u32<kDppMirror>(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = a[0] + a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return b[0] + b[1];
 }
 
 // Balanced mode.  The attended blocks of all sequences, in sequence order,
@@ -678,7 +687,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         compute_block(b, st[u % NS]);
     }
 
-    l = wave_sum_xor16_32(l);
+    l = row_sum_xor16_32(l);
     emit_mfma<D>(a, s, kvh, direct, prow_base, lane, o, m, l);
     };
 
@@ -785,11 +794,35 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
 
 // ------------------------------------------------------------------ FP32 path
 
+// Maximum and sum over the 16 lanes of each row (DPP), then over the four
+// rows (gfx950 row swaps): the result is in every lane of the wave.
+__device__ __forceinline__ float row16_max(float v)
+{
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    return v;
+}
+__device__ __forceinline__ float wave_max64(float v) { return row_max_xor16_32(row16_max(v)); }
+__device__ __forceinline__ float wave_sum64(float v) { return row_sum_xor16_32(row16_sum(v)); }
+
+// One wavefront per (sequence, kv head, split).  Lane row r = lane / 16
+// holds tokens 4 i + r (i = 0..3) of each 16-token cache block, 16 lanes per
+// row: lane c of the row reads 16 bytes at 16 c + 256 j of the head's K and V
+// slices (JK and JV loads per token).  A block's whole load set is issued one
+// block ahead (two register stages); each block gets buffer resources built
+// in scalar registers from its table entry, the split's entries having been
+// read once into lanes; an unmapped or past-the-split block gets a record
+// count of 0, so its loads return zeros and move no data.  Per row, a block's
+// four scores come from a DPP row reduction, and the row's softmax stream is
+// rescaled once per block; the four row streams merge at the end.
 template <int DQK, int DV, int G>
 __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
 {
-    constexpr int JK = DQK / 64;               // float4 loads of K per lane
-    constexpr int JV = DV / 64;                // float4 loads of V per lane
+    constexpr int JK = DQK / 64;               // 16-byte loads of a K slice per lane
+    constexpr int JV = DV / 64;                // 16-byte loads of a V slice per lane
+    constexpr bool QREG = G * JK <= 12;        // q in registers, else read from LDS
     __shared__ float s_q[G][DQK];
 
     const int lane = threadIdx.x;
@@ -812,6 +845,15 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
     }
     const uint32_t b1 = min(b0 + a.chunk_blocks, R.nblk);
 
+    // block-table entries of the split, kBtRegs per lane (entry i at lane
+    // i % 64 of bt_lane[i / 64]; lanes past the split re-read its last one)
+    int32_t bt_lane[kBtRegs];
+#pragma unroll
+    for (int h = 0; h < kBtRegs; ++h) {
+        const uint32_t idx = b0 + 64 * h + lane;
+        bt_lane[h] = a.bt[(uint64_t)s * a.M + (idx < b1 ? idx : b1 - 1)];
+    }
+
     // q rows of the group into LDS, rotated at position n - 1 if asked
     const float* qsrc = (const float*)a.q + (uint64_t)s * a.q_stride + (uint64_t)kvh * G * DQK;
     for (int idx = lane; idx < G * DQK; idx += 64)
@@ -831,12 +873,20 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
         }
         __syncthreads();
     }
-    f32x4 qv[G][JK];
+    f32x4 qv[QREG ? G : 1][QREG ? JK : 1];
+    if constexpr (QREG) {
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g)
 #pragma unroll
-        for (int j = 0; j < JK; ++j)
-            qv[g][j] = *(const f32x4*)&s_q[g][64 * j + 4 * c];
+            for (int j = 0; j < JK; ++j)
+                qv[g][j] = *(const f32x4*)&s_q[g][64 * j + 4 * c];
+    }
+    auto q_chunk = [&](int g, int j) -> f32x4 {
+        if constexpr (QREG)
+            return qv[g][j];
+        else
+            return *(const f32x4*)&s_q[g][64 * j + 4 * c];
+    };
 
     float m[G], l[G];
     f32x4 o[G][JV];
@@ -849,66 +899,131 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
             o[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const float* kb = (const float*)a.k_cache;
-    const float* vb = (const float*)a.v_cache;
-    const uint64_t krs = (uint64_t)a.Hkv * DQK, vrs = (uint64_t)a.Hkv * DV;
-    const uint32_t t_end = min((uint32_t)n, b1 * kBS);
-    for (uint32_t t0 = b0 * kBS; t0 < t_end; t0 += 4) {
-        const uint32_t t = t0 + row;
-        const int32_t pb = a.bt[(uint64_t)s * a.M + t / kBS];
-        const bool ok = t < t_end && (int32_t)t >= R.lo && pb >= 0 && (uint32_t)pb < a.num_blocks;
-        f32x4 kv[JK], vv[JV];
-        if (ok) {
-            const uint64_t r = (uint64_t)pb * kBS + t % kBS;
+    const uint8_t* kbase = (const uint8_t*)a.k_cache;
+    const uint8_t* vbase = (const uint8_t*)a.v_cache;
+    const uint32_t krow = a.Hkv * DQK * 4u, vrow = a.Hkv * DV * 4u;     // bytes per cache row
+    const uint32_t kblk = kBS * krow, vblk = kBS * vrow;
+    const uint32_t koff = row * krow + kvh * DQK * 4u + 16u * c;
+    const uint32_t voff = row * vrow + kvh * DV * 4u + 16u * c;
+
+    struct Stage {
+        f32x4 k[4][JK];
+        f32x4 v[4][JV];
+    };
+    auto block_ok = [&](uint32_t bi) -> int32_t {
+        int32_t r = bt_lane[0];
+#pragma unroll
+        for (int h = 1; h < kBtRegs; ++h)
+            r = bi - b0 >= 64u * h ? bt_lane[h] : r;        // wave-uniform choice
+        const int32_t pb = __builtin_amdgcn_readlane(r, (int)((bi - b0) & 63));
+        return (bi < b1 && pb >= 0 && (uint32_t)pb < a.num_blocks) ? pb : -1;
+    };
+    auto load_block = [&](uint32_t bi, Stage& st) {
+        const int32_t pb = block_ok(bi);
+        const uint64_t p = pb >= 0 ? (uint64_t)pb : 0;
+        const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(kbase + p * kblk), 0, pb >= 0 ? (int)kblk : 0, kBufferFlags);
+        const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(vbase + p * vblk), 0, pb >= 0 ? (int)vblk : 0, kBufferFlags);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int j = 0; j < JK; ++j)
-                kv[j] = __builtin_nontemporal_load((const f32x4*)(kb + r * krs + (uint64_t)kvh * DQK + 64 * j + 4 * c));
+                st.k[i][j] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff + 256u * j, 4u * i * krow, kNT));
 #pragma unroll
             for (int j = 0; j < JV; ++j)
-                vv[j] = __builtin_nontemporal_load((const f32x4*)(vb + r * vrs + (uint64_t)kvh * DV + 64 * j + 4 * c));
-        } else {
+                st.v[i][j] = __builtin_bit_cast(
+                    f32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, voff + 256u * j, 4u * i * vrow, kNT));
+        }
+    };
+    auto compute_block = [&](uint32_t bi, Stage& st) {
+        // tokens 4 i + row of the block; an unmapped block loaded zeros
+        const int32_t t0 = (int32_t)(bi * kBS) + row;
+        const bool full = block_ok(bi) >= 0 && (int32_t)(bi * kBS) >= R.lo &&
+                          (int32_t)(bi * kBS) + kBS <= n;
+        bool ok[4];
 #pragma unroll
-            for (int j = 0; j < JK; ++j) kv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 4; ++i) {
+            const int32_t t = t0 + 4 * i;
+            ok[i] = full || (block_ok(bi) >= 0 && t < n && t >= R.lo);
+            if (!full && !ok[i]) {
 #pragma unroll
-            for (int j = 0; j < JV; ++j) vv[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int j = 0; j < JV; ++j)
+                    st.v[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};   // rows past n may hold anything
+            }
         }
 #pragma unroll
         for (int g = 0; g < G; ++g) {
-            float d = 0.f;
+            float sc[4];
 #pragma unroll
-            for (int j = 0; j < JK; ++j)
-                d += qv[g][j].x * kv[j].x + qv[g][j].y * kv[j].y + qv[g][j].z * kv[j].z +
-                     qv[g][j].w * kv[j].w;
-            d += __shfl_xor(d, 1, 64);
-            d += __shfl_xor(d, 2, 64);
-            d += __shfl_xor(d, 4, 64);
-            d += __shfl_xor(d, 8, 64);
-            const float sc = ok ? d * a.qk_scale : -INFINITY;
-            const float m_new = fmaxf(m[g], sc);
+            for (int i = 0; i < 4; ++i) {
+                float d = 0.f;
+#pragma unroll
+                for (int j = 0; j < JK; ++j) {
+                    const f32x4 qq = q_chunk(g, j);
+                    d += qq.x * st.k[i][j].x + qq.y * st.k[i][j].y + qq.z * st.k[i][j].z +
+                         qq.w * st.k[i][j].w;
+                }
+                d = row16_sum(d);
+                sc[i] = ok[i] ? d * a.qk_scale : -INFINITY;
+            }
+            const float mb = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            const float m_new = fmaxf(m[g], mb);
             if (m_new != -INFINITY) {
                 const float alpha = __builtin_amdgcn_exp2f(m[g] - m_new);
-                const float p = __builtin_amdgcn_exp2f(sc - m_new);
-                l[g] = l[g] * alpha + p;
+                float p[4];
 #pragma unroll
-                for (int j = 0; j < JV; ++j)
-                    o[g][j] = o[g][j] * alpha + vv[j] * p;
+                for (int i = 0; i < 4; ++i)
+                    p[i] = __builtin_amdgcn_exp2f(sc[i] - m_new);
+                l[g] = l[g] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+#pragma unroll
+                for (int j = 0; j < JV; ++j) {
+                    f32x4 acc = o[g][j] * alpha;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc = acc + st.v[i][j] * p[i];
+                    o[g][j] = acc;
+                }
                 m[g] = m_new;
             }
         }
+    };
+
+    // two register stages, one block ahead: the main loop's loads are
+    // unconditional (so the wait before each block covers only that block's
+    // loads), and a tail takes the last one or two blocks; every load issued
+    // is consumed
+    Stage sa, sb;
+    load_block(b0, sa);
+    uint32_t bi = b0;
+    for (; bi + 2 < b1; bi += 2) {
+        load_block(bi + 1, sb);
+        compute_block(bi, sa);
+        load_block(bi + 2, sa);
+        compute_block(bi + 1, sb);
     }
+    if (bi + 1 < b1) {
+        load_block(bi + 1, sb);
+        compute_block(bi, sa);
+        compute_block(bi + 1, sb);
+    } else {
+        compute_block(bi, sa);
+    }
+
     // merge the four row streams
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-        const float mt = wave_max_xor16_32(m[g]);
+        const float mt = row_max_xor16_32(m[g]);
         const float f = mt == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[g] - mt);
-        float lt = wave_sum_xor16_32(l[g] * f);
+        float lt = row_sum_xor16_32(l[g] * f);
 #pragma unroll
         for (int j = 0; j < JV; ++j) {
             f32x4 v = o[g][j] * f;
-            v.x = wave_sum_xor16_32(v.x);
-            v.y = wave_sum_xor16_32(v.y);
-            v.z = wave_sum_xor16_32(v.z);
-            v.w = wave_sum_xor16_32(v.w);
+            v.x = row_sum_xor16_32(v.x);
+            v.y = row_sum_xor16_32(v.y);
+            v.z = row_sum_xor16_32(v.z);
+            v.w = row_sum_xor16_32(v.w);
             o[g][j] = v;
         }
         if (row != 0)
@@ -996,9 +1111,7 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeAr
     float M = ml0[0];
     for (uint32_t i = lane + 64; i < nsplit; i += 64)
         M = fmaxf(M, ml_of(i)[0]);
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1)
-        M = fmaxf(M, __shfl_xor(M, d, 64));
+    M = wave_max64(M);
     const float Mref = M == -INFINITY ? 0.f : M;
 
     float L = 0.f;
@@ -1012,21 +1125,35 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeAr
         const float w = __builtin_amdgcn_exp2f(ml[0] - Mref);
         L = __builtin_fmaf(w, ml[1], L);
         const uint32_t n = nsplit - i0 < 64u ? nsplit - i0 : 64u;
-        for (uint32_t j = 0; j < n; ++j) {
-            const float wj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), (int)j));
-            const float* orow = a.part_o + (prow0 + (uint64_t)(i0 + j) * a.Hq) * DV + lane * DPL;
-            if constexpr (DPL == 2) {
-                const f32x2 o = *(const f32x2*)orow;
-                acc[0] = __builtin_fmaf(wj, o[0], acc[0]);
-                acc[1] = __builtin_fmaf(wj, o[1], acc[1]);
-            } else {
-                acc[0] = __builtin_fmaf(wj, orow[0], acc[0]);
+        // eight partial rows in flight at a time (rows past n re-read row
+        // n - 1, which exists, and are not accumulated)
+        for (uint32_t j0 = 0; j0 < n; j0 += 8) {
+            float o[8][DPL];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const uint32_t j = j0 + u < n ? j0 + u : n - 1;
+                const float* orow = a.part_o + (prow0 + (uint64_t)(i0 + j) * a.Hq) * DV + lane * DPL;
+                if constexpr (DPL == 2) {
+                    const f32x2 t = *(const f32x2*)orow;
+                    o[u][0] = t[0];
+                    o[u][1] = t[1];
+                } else {
+                    o[u][0] = orow[0];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                if (j0 + u < n) {
+                    const float wj = __int_as_float(
+                        __builtin_amdgcn_readlane(__float_as_int(w), (int)(j0 + u)));
+#pragma unroll
+                    for (int k = 0; k < DPL; ++k)
+                        acc[k] = __builtin_fmaf(wj, o[u][k], acc[k]);
+                }
             }
         }
     }
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1)
-        L += __shfl_xor(L, d, 64);
+    L = wave_sum64(L);
     const float inv = norm_factor(M, L, a.sinks, h, a.out_scale);
     if constexpr (DPL == 2) {
         *(f32x2*)(a.out + oi) = f32x2{acc[0] * inv * g[0], acc[1] * inv * g[1]};

@@ -132,6 +132,38 @@ __device__ __forceinline__ f32x2 unpack_e4m3x2(uint32_t w, bool hi)
               : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
 }
 
+// DPP row operations (gfx9 encodings): lane i of each 16-lane row takes the
+// value of lane i ^ 1, i ^ 2 (quad permutes), 7 - i within its half-row, or
+// 15 - i within its row.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+// Sum over aligned groups of L = 2, 4, 8 or 16 consecutive lanes, left in
+// every lane of the group (pairs, quads, mirrored half-rows, mirrored rows:
+// one DPP add each, no LDS); L is wave-uniform.
+__device__ __forceinline__ float group_sum(float v, uint32_t L)
+{
+    if (L >= 2)
+        v += dpp_f32<kDppXor1>(v);
+    if (L >= 4)
+        v += dpp_f32<kDppXor2>(v);
+    if (L >= 8)
+        v += dpp_f32<kDppHalfMirror>(v);
+    if (L >= 16)
+        v += dpp_f32<kDppMirror>(v);
+    return v;
+}
+__device__ __forceinline__ float row16_sum(float v) { return group_sum(v, 16); }
+
 // Streaming (read-once / write-once) 16-byte accesses.
 __device__ __forceinline__ u32x4 load_nt(const u32x4* p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_nt(u32x4* p, u32x4 v) { __builtin_nontemporal_store(v, p); }
