@@ -247,19 +247,7 @@ def run_decode(name, args):
 
     k_scale = 1.0
     if fp8:
-        # k_scale = max |stored FP32 K| / 448 over the whole history (the
-        # K path's FP32 output, computed in chunks through the FP32 store)
-        amax = torch.zeros((), dtype=torch.float32, device=dev)
-        chunk = 1 << 16
-        tmp = torch.empty((chunk // B, B, Hkv, D), dtype=torch.float32, device=dev)
-        ident = torch.arange(chunk, dtype=torch.int64, device=dev)
-        for t0 in range(0, Th, chunk):
-            t1 = min(Th, t0 + chunk)
-            pkv.cache_write_k_fused(k_hist[t0:t1], ident[:t1 - t0], tmp, norm_weight=w,
-                                    eps=cfg["eps"], pos_t=pos_h_t[t0:t1], theta=cfg["theta"])
-            amax = torch.maximum(amax, tmp.view(-1)[:(t1 - t0) * Hkv * D].abs().max())
-        k_scale = float(amax.item()) / 448.0
-        del tmp
+        k_scale = history_k_scale(k_hist, pos_h_t, w, cfg)
         log(f"k_scale = {k_scale:.6g}")
     v_scale = 1.0
     if v_fp8:
@@ -416,6 +404,27 @@ def run_decode(name, args):
         result["cpu_baseline"] = cpu_baseline(idx, lay, k_scale, v_kind, v_scale, window,
                                               None if sinks is None else sinks.cpu().numpy())
     return result
+
+
+def history_k_scale(k_hist, pos, w, cfg, B=16):
+    """k_scale = max |stored FP32 K| / 448 over a history K [T, Hkv, D]: the K
+    path's FP32 output (RMSNorm and RoPE through the library's FP32 store),
+    computed in chunks."""
+    import torch
+
+    import paged_kv_cache_fill_amd as pkv
+    T, Hkv, D = k_hist.shape
+    dev = k_hist.device
+    amax = torch.zeros((), dtype=torch.float32, device=dev)
+    chunk = 1 << 16
+    tmp = torch.empty((chunk // B, B, Hkv, D), dtype=torch.float32, device=dev)
+    ident = torch.arange(chunk, dtype=torch.int64, device=dev)
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        pkv.cache_write_k_fused(k_hist[t0:t1], ident[:t1 - t0], tmp, norm_weight=w,
+                                eps=cfg["eps"], pos_t=pos[t0:t1], theta=cfg["theta"])
+        amax = torch.maximum(amax, tmp.view(-1)[:(t1 - t0) * Hkv * D].abs().max())
+    return float(amax.item()) / 448.0
 
 
 def prefill_flops(lens, qlens, Hq, D, Dv):

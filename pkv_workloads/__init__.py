@@ -241,6 +241,16 @@ def e4m3_codes(index: int, stream: int, shape) -> np.ndarray:
     return (mag | sign).astype(np.uint8)
 
 
+def e4m3_finite_codes(index: int, stream: int, shape) -> np.ndarray:
+    """Random finite E4M3 codes over the whole range: magnitude codes
+    0x00..0x7E (0 to 448: every exponent field, subnormals included), random
+    sign."""
+    r = rng(index, stream)
+    mag = r.integers(0, 0x7F, size=shape).astype(np.uint8)
+    sign = (r.integers(0, 2, size=shape).astype(np.uint8) << 7).astype(np.uint8)
+    return (mag | sign).astype(np.uint8)
+
+
 def random_pools(index: int, lay: Layout, poison_pad: bool = True, v_dtype: str = None):
     """K and V pools [num_blocks, B, Hkv, D] filled directly with random
     values (decode tested on its own).  K is N(0,1) (BF16 or FP32; the FP8

@@ -28,8 +28,7 @@ from _util import ATTN_TOL, attn_err, bf16_ok, e4m3_ok, host, say, tq_compare, t
 pytestmark = pytest.mark.gpu
 
 B = 16
-K_SCALE = 0.0625            # an input scalar; parity does not depend on its value
-V_SCALE = 0.02
+V_SCALE = 0.02              # an input scalar; parity does not depend on its value
 
 
 def _i32(a):
@@ -115,7 +114,6 @@ def test_full_size_decode_step_sampled(name):
     S, Hq, Hkv, D = lay.num_seqs, cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"]
     fp8 = cfg["k_cache_dtype"] == "fp8"
     k_dt = "fp8" if fp8 else "bf16"
-    k_scale = K_SCALE if fp8 else 1.0
     v_scale = V_SCALE if v_kind == "fp8" else 1.0
     say(f"full-size decode step {name}: {S} seqs, {lay.total_tokens} tokens, "
         f"pool {lay.num_blocks} blocks")
@@ -142,6 +140,10 @@ def test_full_size_decode_step_sampled(name):
     v_hist = W.device_normal(idx, W.S_V, (Th, Hkv, D), torch.bfloat16, dev)
     slots_h = torch.empty(Th, dtype=torch.int64, device=dev)
     pkv.fill_slots(slots_h, bt, _i32(start_h), _i32(cu_h), B)
+    # the benchmark's k_scale: max |stored FP32 K| / 448 over the history
+    k_scale = bench.history_k_scale(k_hist, _i32(pos_h), w, cfg) if fp8 else 1.0
+    if fp8:
+        say(f"  k_scale = {k_scale:.6g} (the benchmark's)")
     pkv.cache_write_k_fused(k_hist, slots_h, k_pool, norm_weight=w, eps=cfg["eps"],
                             pos_t=_i32(pos_h), theta=cfg["theta"], k_scale=k_scale)
     pkv.cache_write_v(v_hist, slots_h, v_pool, v_scale=v_scale, tq_bits=tq)
@@ -170,16 +172,22 @@ def test_full_size_decode_step_sampled(name):
     ref_slots = oracle.fill_slots(lay.block_tables, start_d, cu_d, S, B)
     assert (host(slots_d) == ref_slots).all()
 
-    # K and V rows: sampled history tokens and the new tokens of sampled sequences
+    # K and V rows: sampled history tokens and the new tokens of every
+    # sequence (with E4M3 K at the benchmark's k_scale, where a new token can
+    # saturate)
     rng = np.random.default_rng(idx)
     hist_tok = np.sort(rng.choice(Th, size=96, replace=False))
     seqs = _sample_seqs(lens, 4, 100 + idx)
     tok_idx = torch.from_numpy(hist_tok).to(dev)
     h_slots = host(slots_h)[hist_tok]
+    if fp8:
+        new_codes = _gather_rows(k_pool, ref_slots, None, Hkv, D)
+        say(f"  new tokens' K: {int(((new_codes & 0x7F) == 0x7E).sum())} of {new_codes.size} "
+            f"codes saturated")
     for rows_k, rows_v, slots, pos in (
             (_bits(k_hist.index_select(0, tok_idx)), _bits(v_hist.index_select(0, tok_idx)),
              h_slots, pos_h[hist_tok]),
-            (_bits(k_new)[seqs], _bits(v_new)[seqs], ref_slots[seqs], pos_d[seqs])):
+            (_bits(k_new), _bits(v_new), ref_slots, pos_d)):
         _check_k_rows(rows_k, pos, _gather_rows(k_pool, slots, None, Hkv, D), cfg, w_np,
                       k_dt, k_scale)
         _check_v_rows(rows_v, _gather_rows(v_pool, slots, v_kind, Hkv, D), v_kind, Hkv, D)
