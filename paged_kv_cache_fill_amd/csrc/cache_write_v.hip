@@ -17,7 +17,11 @@
 namespace pkv {
 
 constexpr int kVThreads = 256;
-constexpr int kVRun = 4;      // E4M3 store: tokens per thread per pass (loads in flight)
+// E4M3 store: tokens per thread per pass.  With the row loads independent of
+// the slot loads, one token per thread measured fastest (64-sequence
+// population write, 1.58 M tokens: 0.905 / 0.910 / 0.927 / 0.951 ms with
+// 1 / 2 / 4 / 8 tokens per thread).
+constexpr int kVRun = 1;
 // The plain copy: one token per thread, so the most threads, each with one
 // load in flight (population write of 1.09 M BF16 rows: 0.80 ms against
 // 0.86 ms with four tokens per thread and 0.85 ms with two; the E4M3 store,
@@ -47,11 +51,13 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_kernel(
         int64_t s = tok[r] < num_tokens ? slots[tok[r]] : -1;
         slot[r] = (s >= 0 && (uint64_t)s < num_slots) ? s : -1;
     }
+    // the row loads depend only on the token existing, not on its slot, so
+    // they are in flight together with the slot loads
     for (uint32_t c = col0; c < cols; c += col_step) {
         u32x4 buf[kVRunCopy];
 #pragma unroll
         for (int r = 0; r < kVRunCopy; ++r)
-            if (slot[r] >= 0)
+            if (tok[r] < num_tokens)
                 buf[r] = load_nt(v + tok[r] * in_stride16 + c);
 #pragma unroll
         for (int r = 0; r < kVRunCopy; ++r)
@@ -60,15 +66,35 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_kernel(
     }
 }
 
+// v / d for 2^-64 <= d <= 2^64 from the correctly rounded reciprocal
+// r = RN(1/d): q0 = RN(x r), then one residual correction
+// RN(q0 + (x - q0 d) r), the residual exact by FMA while it does not
+// underflow (Markstein's division step).  For such d its E4M3 code (after
+// the +-448 clamp) equals that of the correctly rounded quotient for every
+// FP32 x: checked exhaustively over all 2^32 x for divisors across and at
+// the ends of that range, an all-ones significand among them (near FLT_MIN
+// the residual of tiny x underflows and some codes differ, hence the
+// range); quotients of |q0| >= 1e30 saturate either way and are not
+// corrected; the sign of q0 is kept so that -0 stays -0.
+__device__ __forceinline__ float div_by_scale(float x, float d, float r)
+{
+    const float q0 = x * r;
+    const float e = __builtin_fmaf(-q0, d, x);
+    const float q1 = __builtin_fmaf(e, r, q0);
+    return __builtin_copysignf(__builtin_fabsf(q0) < 1e30f ? q1 : q0, q0);
+}
+
 // E4M3 store: each thread owns 16 consecutive elements of the row (one
 // 16-byte column of the E4M3 row; 2 or 4 16-byte loads of the input) and
-// walks kVRun tokens the same way.  v / v_scale is a correctly rounded FP32
-// division, so the stored code is the E4M3 rounding of fl32(v / v_scale).
-template <int IN>   // 0 = BF16 input, 2 = FP32 input
+// walks kVRun tokens the same way.  The stored code is the E4M3 rounding of
+// fl32(v / v_scale): with FAST (2^-64 <= v_scale <= 2^64), by div_by_scale
+// from the host's correctly rounded reciprocal; otherwise by the correctly
+// rounded FP32 division.
+template <int IN, bool FAST>   // IN: 0 = BF16 input, 2 = FP32 input
 __global__ __launch_bounds__(kVThreads) void cache_write_v_e4m3_kernel(
     const u32x4* __restrict__ v, uint64_t in_stride16, const int64_t* __restrict__ slots,
     uint32_t num_tokens, uint32_t cols, uint32_t tpb, uint64_t num_slots, float v_scale,
-    u32x4* __restrict__ cache)
+    float v_rcp, u32x4* __restrict__ cache)
 {
     constexpr int NLD = IN == 0 ? 2 : 4;                // input loads per 16 elements
     const uint32_t lane_tok = threadIdx.x / cols;
@@ -89,7 +115,7 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_e4m3_kernel(
         u32x4 buf[kVRun][NLD];
 #pragma unroll
         for (int r = 0; r < kVRun; ++r)
-            if (slot[r] >= 0)
+            if (tok[r] < num_tokens)                    // independent of the slot loads
 #pragma unroll
                 for (int j = 0; j < NLD; ++j)
                     buf[r][j] = load_nt(v + tok[r] * in_stride16 + (uint64_t)c * NLD + j);
@@ -111,9 +137,13 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_e4m3_kernel(
                 }
             u32x4 w;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                w[q] = e4m3_sat_x4(x[4 * q] / v_scale, x[4 * q + 1] / v_scale,
-                                   x[4 * q + 2] / v_scale, x[4 * q + 3] / v_scale);
+            for (int q = 0; q < 4; ++q) {
+                float y[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    y[e] = FAST ? div_by_scale(x[4 * q + e], v_scale, v_rcp) : x[4 * q + e] / v_scale;
+                w[q] = e4m3_sat_x4(y[0], y[1], y[2], y[3]);
+            }
             store_nt(cache + (uint64_t)slot[r] * cols + c, w);
         }
     }
@@ -146,9 +176,8 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
     const uint32_t h = blockIdx.y;
     if (q >= groups || tok >= num_tokens)
         return;
+    // slot and row loads in flight together (the row does not depend on it)
     const int64_t slot = slots[tok];
-    if (slot < 0 || (uint64_t)slot >= num_slots)
-        return;
 
     float x[16];
     const uint8_t* src = v + (uint64_t)tok * in_stride_bytes + ((uint64_t)h * D + 16u * q) * (IN == 0 ? 2 : 4);
@@ -171,9 +200,12 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
                 x[4 * j + e] = __uint_as_float(w[e]);
         }
     }
+    if (slot < 0 || (uint64_t)slot >= num_slots)
+        return;
     // The decisions below follow the FP32 sequence stated with pkv_dtype
     // (in-order fused sum of squares, one reciprocal of the rms, one product
-    // per element), so that codes and scales are reproducible bit for bit.
+    // per element); they equal the exact definition's except within FP32
+    // rounding of a decision boundary.
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -348,13 +380,22 @@ extern "C" int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_
         hipLaunchKernelGGL(cache_write_v_kernel, dim3((uint32_t)blocks), dim3(kVThreads), 0, st,
                            (const u32x4*)v, stride_bytes / 16, slot_mapping, num_tokens, cols,
                            tpb, num_slots, (u32x4*)v_cache);
-    else if (in_dtype == PKV_BF16)
-        hipLaunchKernelGGL(cache_write_v_e4m3_kernel<0>, dim3((uint32_t)blocks), dim3(kVThreads),
-                           0, st, (const u32x4*)v, stride_bytes / 16, slot_mapping, num_tokens,
-                           cols, tpb, num_slots, v_scale, (u32x4*)v_cache);
-    else
-        hipLaunchKernelGGL(cache_write_v_e4m3_kernel<2>, dim3((uint32_t)blocks), dim3(kVThreads),
-                           0, st, (const u32x4*)v, stride_bytes / 16, slot_mapping, num_tokens,
-                           cols, tpb, num_slots, v_scale, (u32x4*)v_cache);
+    else {
+        // the correctly rounded reciprocal: the double quotient is within
+        // 2^-53 of 1/v_scale, which is never that close to a float midpoint
+        // without being one, so rounding it to float rounds 1/v_scale once
+        const float v_rcp = (float)(1.0 / (double)v_scale);
+        const bool fast = v_scale >= 0x1p-64f && v_scale <= 0x1p64f;
+#define PKV_E4V(IN, FAST)                                                                       \
+    hipLaunchKernelGGL((cache_write_v_e4m3_kernel<IN, FAST>), dim3((uint32_t)blocks),          \
+                       dim3(kVThreads), 0, st, (const u32x4*)v, stride_bytes / 16, slot_mapping, \
+                       num_tokens, cols, tpb, num_slots, v_scale, v_rcp, (u32x4*)v_cache)
+        if (in_dtype == PKV_BF16) {
+            if (fast) PKV_E4V(0, true); else PKV_E4V(0, false);
+        } else {
+            if (fast) PKV_E4V(2, true); else PKV_E4V(2, false);
+        }
+#undef PKV_E4V
+    }
     return check_launch("cache_write_v");
 }

@@ -47,12 +47,17 @@ def test_e4m3_v_population_write_whole_pool_bit_exact():
     assert (got == ref).all()
 
 
-@pytest.mark.parametrize("v_scale", [1.0, 0.0364877, 3.0, 31.999998092651367])
+@pytest.mark.parametrize("v_scale", [1.0, 0.0364877, 3.0, 31.999998092651367, 2.0 ** -64,
+                                     2.0 ** 64, 2.0 ** -126, 2.0 ** -130, 2.0 ** 127])
 def test_e4m3_v_store_every_bf16_pattern_bit_exact(v_scale):
     """All 65536 BF16 patterns (NaN, +-inf, -0, subnormals, saturation) as V
     input, 64 tokens of 8 x 128.  31.999998... = 32 (1 - 2^-24) has an
-    all-ones significand, where a reciprocal multiply with one correction step
-    is not the correctly rounded quotient (-4096 / it is -128.00002 in FP32)."""
+    all-ones significand, where a reciprocal multiply with one correction
+    step from the hardware's approximate reciprocal is not the correctly
+    rounded quotient (-4096 / it is -128.00002 in FP32).  2^-64 and 2^64 are
+    the ends of the scales whose quotient comes from the host's correctly
+    rounded reciprocal and one residual correction; 2^-126, 2^-130 (a
+    subnormal) and 2^127 take the full division."""
     pats = np.arange(65536, dtype=np.uint16).reshape(64, 8, 128)
     slots = np.random.default_rng(9).permutation(64).astype(np.int64)
     say(f"E4M3 V store of every BF16 pattern, v_scale={v_scale}")
