@@ -539,7 +539,7 @@ def run_prefill(args):
         "vs_baseline": None,
         "dtype": "bf16 q/K/V, f32 accumulate",
         "data": "synthetic (seeded)",
-        "config": {"workload": name, "num_seqs": S, "chunk": chunk,
+        "config": {"workload": args.workload, "num_seqs": S, "chunk": chunk,
                    "new_tokens": Tc, "total_tokens": int(lens.sum()), "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": B,
                    "parallelism": "single GPU"},
