@@ -9,7 +9,7 @@
 // head) pairs of one kv head's GQA group, token-major (row = i * G + g).  A
 // work-group takes 128 consecutive rows of one (sequence, kv head), four
 // wavefronts of two 16-row tiles each, and walks the keys [lo_min, end_max)
-// of its rows in steps of two cache blocks.  Each step's K and V blocks are
+// of its rows in steps of four cache blocks (two pairs).  Each step's K and V blocks are
 // loaded once per work-group (one 16-byte chunk of each per thread and
 // block), written to LDS -- K in the swizzled MFMA operand layout of KFrag, V
 // row-major with a 16-byte pad per row -- and read by all four waves; the
@@ -29,7 +29,10 @@
 namespace pkv {
 
 constexpr int kPWaves = 4;                   // waves per work-group
-constexpr int kPStep = 2;                    // cache blocks per step
+// cache blocks per step (pairs of blocks, each pair one PV k span): four
+// halve the barriers of two (612 against 592 TFLOP/s on the chunk-256
+// workload); eight need 256 VGPRs, one wave per SIMD (397)
+constexpr int kPStep = 4;
 constexpr int kPPre = 1;                     // steps whose loads are in flight
 constexpr int kPTiles = 2;                   // 16-row tiles per wave
 constexpr int kXcds = 8;                     // XCDs work-groups are dealt to
@@ -239,8 +242,9 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
         lds_r[jj] = KF::lds_off(ln, KF::op_chunk(jj, kg));
     const uint32_t v_rd = KTILE + (4 * kg) * VROW + DPL * ln * VES;
 
-    static_assert(kPStep == 2, "a step is one pair of blocks along the PV k");
-    auto compute_step = [&](int buf, uint32_t b0) {
+    static_assert(kPStep % 2 == 0, "a step is whole pairs of blocks along the PV k");
+    // one pair of blocks (j0, j0 + 1 of the step's LDS buffer)
+    auto compute_pair = [&](int buf, int j0, uint32_t b0) {
         if (!wave_live)
             return;
         bool blk_ok[2], inner[2];
@@ -267,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
 #pragma unroll
             for (int t = 0; t < RT; ++t)
                 sacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const uint8_t* kt = &lds[buf][j][0];
+            const uint8_t* kt = &lds[buf][j0 + j][0];
             u32x4 kop[NL];
 #pragma unroll
             for (int jj = 0; jj < NL; ++jj)
@@ -338,7 +342,7 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
         uint32_t vr[2][4][VW];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint8_t* vt = &lds[buf][h][0] + v_rd;
+            const uint8_t* vt = &lds[buf][j0 + h][0] + v_rd;
             if (inner[h]) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
@@ -451,6 +455,12 @@ __global__ __launch_bounds__(64 * NW) void prefill_mfma_kernel(PrefillArgs a,
                 o[t][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo[t], bv[nt], o[t][nt], 0, 0, 0);
             }
         }
+    };
+
+    auto compute_step = [&](int buf, uint32_t b0) {
+#pragma unroll
+        for (int j0 = 0; j0 < kPStep; j0 += 2)
+            compute_pair(buf, j0, b0 + j0);
     };
 
     if (nblk > blo) {
