@@ -146,11 +146,12 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
 
 
-def traffic_from_profile(kernel_src_hash: str, workload: str, kernel: str = "decode_attn"):
+def traffic_from_profile(kernel_src_hash: str, workload: str, kernel: str = "decode_attn",
+                         suffix: str = "_pmc"):
     """HBM bytes per call measured with rocprofv3 --pmc (FETCH_SIZE and
     WRITE_SIZE, scaled by a plain copy's counters), stored in profiles/ with the
     hash of the kernel source they were taken on; None when stale or absent."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.md")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}{suffix}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -629,6 +630,8 @@ def run_aux(args):
         step_b = slots_bytes(T, S) + kwrite_bytes(T, Hkv, D, 2, 2) + vwrite_bytes(T, Hkv, D, 2, 2)
         dom = "k_fused"
         dom_b = kwrite_bytes(T, Hkv, D, 2, 2)
+        traffic = traffic_from_profile(kernel_source_hash("cache_write_k.hip"), args.workload,
+                                       kernel="cache_write", suffix="")
         # the oracle on the same inputs: slots, K write, V write
         kc = np.zeros((lay.num_blocks, B, Hkv, D), np.uint16)
         vc = np.zeros_like(kc)
@@ -693,6 +696,7 @@ def run_aux(args):
                               "frac_of_hbm_peak": round(dec_b / dmsv / 1e6 / HBM_PEAK_GBS, 4)}
         step_ms, step_b = res["rope"]["ms"], dec_b
         dom, dom_b = "decode_call", dec_b
+        traffic = traffic_from_profile(kernel_source_hash(), args.workload)
         # the oracle: attention over the same pools (copied to the host)
         kp_h, vp_h = kp.cpu().numpy(), vp.cpu().numpy()
 
@@ -728,7 +732,7 @@ def run_aux(args):
         "calls": res,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": dom},
+                     "traffic": traffic, "kernel": dom},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

@@ -1060,6 +1060,10 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a)
 // (m = -inf, o = 0) gets weight 0; with every split empty the reference is 0
 // instead of M, so no weight is NaN and the row stays zero.
 constexpr uint32_t kMergeHeads = 4;
+// Partial rows loaded together: 1 / 4 / 8 gave 5.6 / 5.8 / 6.9 us on the
+// BF16 workload (a sequence has 1-3 pieces under the balanced plan) and
+// 5.8 / 5.4 / 5.5 us on the E4M3-K one (4-8 pieces).
+constexpr int kMergeRows = 4;
 template <int DPL>
 __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeArgs a)
 {
@@ -1125,12 +1129,12 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeAr
         const float w = __builtin_amdgcn_exp2f(ml[0] - Mref);
         L = __builtin_fmaf(w, ml[1], L);
         const uint32_t n = nsplit - i0 < 64u ? nsplit - i0 : 64u;
-        // eight partial rows in flight at a time (rows past n re-read row
-        // n - 1, which exists, and are not accumulated)
-        for (uint32_t j0 = 0; j0 < n; j0 += 8) {
-            float o[8][DPL];
+        // kMergeRows partial rows in flight at a time (rows past n re-read
+        // row n - 1, which exists, and are not accumulated)
+        for (uint32_t j0 = 0; j0 < n; j0 += kMergeRows) {
+            float o[kMergeRows][DPL];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kMergeRows; ++u) {
                 const uint32_t j = j0 + u < n ? j0 + u : n - 1;
                 const float* orow = a.part_o + (prow0 + (uint64_t)(i0 + j) * a.Hq) * DV + lane * DPL;
                 if constexpr (DPL == 2) {
@@ -1142,7 +1146,7 @@ __global__ __launch_bounds__(64 * kMergeHeads) void decode_merge_kernel(DecodeAr
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
+            for (int u = 0; u < kMergeRows; ++u) {
                 if (j0 + u < n) {
                     const float wj = __int_as_float(
                         __builtin_amdgcn_readlane(__float_as_int(w), (int)(j0 + u)));
