@@ -84,19 +84,25 @@ __device__ __forceinline__ float div_by_scale(float x, float d, float r)
     return __builtin_copysignf(__builtin_fabsf(q0) < 1e30f ? q1 : q0, q0);
 }
 
-// E4M3 store: each thread owns 16 consecutive elements of the row (one
-// 16-byte column of the E4M3 row; 2 or 4 16-byte loads of the input) and
-// walks kVRun tokens the same way.  The stored code is the E4M3 rounding of
-// fl32(v / v_scale): with FAST (2^-64 <= v_scale <= 2^64), by div_by_scale
-// from the host's correctly rounded reciprocal; otherwise by the correctly
-// rounded FP32 division.
+// E4M3 store: each thread owns 16 elements of the row, taken so that every
+// load and store instruction of a wave covers consecutive bytes: with cols
+// the row's 16-byte output columns, thread column c converts input chunks
+// c + j * cols (j < 2 for BF16, 8 elements each; j < 4 for FP32, 4 each)
+// and stores their codes as the 8- or 4-byte pieces c + j * cols of the
+// output row.  (Two 16-byte loads per thread from one 32-byte span would
+// make each load instruction touch every line of the row at half use.)
+// Each thread walks kVRun tokens the same way.  The stored code is the E4M3
+// rounding of fl32(v / v_scale): with FAST (2^-64 <= v_scale <= 2^64), by
+// div_by_scale from the host's correctly rounded reciprocal; otherwise by
+// the correctly rounded FP32 division.
 template <int IN, bool FAST>   // IN: 0 = BF16 input, 2 = FP32 input
 __global__ __launch_bounds__(kVThreads) void cache_write_v_e4m3_kernel(
     const u32x4* __restrict__ v, uint64_t in_stride16, const int64_t* __restrict__ slots,
     uint32_t num_tokens, uint32_t cols, uint32_t tpb, uint64_t num_slots, float v_scale,
-    float v_rcp, u32x4* __restrict__ cache)
+    float v_rcp, uint8_t* __restrict__ cache)
 {
-    constexpr int NLD = IN == 0 ? 2 : 4;                // input loads per 16 elements
+    constexpr int NLD = IN == 0 ? 2 : 4;                // input chunks per thread and column
+    constexpr int EPC = 16 / NLD;                       // elements (output bytes) per chunk
     const uint32_t lane_tok = threadIdx.x / cols;
     const uint32_t col0 = threadIdx.x % cols;
     if (lane_tok >= tpb)
@@ -111,6 +117,7 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_e4m3_kernel(
         int64_t s = tok[r] < num_tokens ? slots[tok[r]] : -1;
         slot[r] = (s >= 0 && (uint64_t)s < num_slots) ? s : -1;
     }
+    const uint64_t row_bytes = (uint64_t)cols * 16;
     for (uint32_t c = col0; c < cols; c += col_step) {
         u32x4 buf[kVRun][NLD];
 #pragma unroll
@@ -118,33 +125,37 @@ __global__ __launch_bounds__(kVThreads) void cache_write_v_e4m3_kernel(
             if (tok[r] < num_tokens)                    // independent of the slot loads
 #pragma unroll
                 for (int j = 0; j < NLD; ++j)
-                    buf[r][j] = load_nt(v + tok[r] * in_stride16 + (uint64_t)c * NLD + j);
+                    buf[r][j] = load_nt(v + tok[r] * in_stride16 + c + (uint64_t)j * cols);
 #pragma unroll
         for (int r = 0; r < kVRun; ++r) {
             if (slot[r] < 0)
                 continue;
-            float x[16];
+            uint8_t* dst = cache + (uint64_t)slot[r] * row_bytes;
 #pragma unroll
-            for (int j = 0; j < NLD; ++j)
+            for (int j = 0; j < NLD; ++j) {
+                float x[EPC];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if constexpr (IN == 0) {
-                        x[8 * j + 2 * e] = bf16_lo(buf[r][j][e]);
-                        x[8 * j + 2 * e + 1] = bf16_hi(buf[r][j][e]);
+                        x[2 * e] = bf16_lo(buf[r][j][e]);
+                        x[2 * e + 1] = bf16_hi(buf[r][j][e]);
                     } else {
-                        x[4 * j + e] = __uint_as_float(buf[r][j][e]);
+                        x[e] = __uint_as_float(buf[r][j][e]);
                     }
                 }
-            u32x4 w;
+                float y[EPC];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float y[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    y[e] = FAST ? div_by_scale(x[4 * q + e], v_scale, v_rcp) : x[4 * q + e] / v_scale;
-                w[q] = e4m3_sat_x4(y[0], y[1], y[2], y[3]);
+                for (int e = 0; e < EPC; ++e)
+                    y[e] = FAST ? div_by_scale(x[e], v_scale, v_rcp) : x[e] / v_scale;
+                const uint64_t off = ((uint64_t)c + (uint64_t)j * cols) * EPC;
+                if constexpr (IN == 0)
+                    __builtin_nontemporal_store(u32x2{e4m3_sat_x4(y[0], y[1], y[2], y[3]),
+                                                      e4m3_sat_x4(y[4], y[5], y[6], y[7])},
+                                                (u32x2*)(dst + off));
+                else
+                    __builtin_nontemporal_store(e4m3_sat_x4(y[0], y[1], y[2], y[3]),
+                                                (uint32_t*)(dst + off));
             }
-            store_nt(cache + (uint64_t)slot[r] * cols + c, w);
         }
     }
 }
@@ -389,7 +400,7 @@ extern "C" int pkv_cache_write_v(const void* v, pkv_dtype in_dtype, uint64_t in_
 #define PKV_E4V(IN, FAST)                                                                       \
     hipLaunchKernelGGL((cache_write_v_e4m3_kernel<IN, FAST>), dim3((uint32_t)blocks),          \
                        dim3(kVThreads), 0, st, (const u32x4*)v, stride_bytes / 16, slot_mapping, \
-                       num_tokens, cols, tpb, num_slots, v_scale, v_rcp, (u32x4*)v_cache)
+                       num_tokens, cols, tpb, num_slots, v_scale, v_rcp, (uint8_t*)v_cache)
         if (in_dtype == PKV_BF16) {
             if (fast) PKV_E4V(0, true); else PKV_E4V(0, false);
         } else {
