@@ -24,8 +24,7 @@ constexpr int kVThreads = 256;
 constexpr int kVRun = 1;
 // The plain copy: one token per thread, so the most threads, each with one
 // load in flight (population write of 1.09 M BF16 rows: 0.80 ms against
-// 0.86 ms with four tokens per thread and 0.85 ms with two; the E4M3 store,
-// which converts, was fastest with four).
+// 0.86 ms with four tokens per thread and 0.85 ms with two).
 constexpr int kVRunCopy = 1;
 
 // cols = row bytes / 16; tpb = tokens handled side by side by one block
