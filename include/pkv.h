@@ -80,9 +80,12 @@ extern "C" {
  *     decoded group (scale x level) keeps the input's L2 norm up to the
  *     scale's rounding; an all-zero group has scale 0.  These decisions are
  *     taken in FP32 in this order: ss = fused multiply-add sum of x_i^2,
- *     i = 0..15; u_i = x_i * (1 / sqrt(ss * 1/16)); magnitude index = the
- *     number of midpoints between adjacent magnitudes that |u_i| exceeds;
- *     sign = u_i < 0; scale = E4M3(sqrt(ss) / sqrt(sum of chosen m^2));
+ *     i = 0..15; u_i = x_i * rsq(ss * 1/16); magnitude index = the number
+ *     of midpoints between adjacent magnitudes that |u_i| exceeds; sign =
+ *     u_i < 0; scale = E4M3(sqrt(ss * rcp(sum of chosen m^2))), with rsq,
+ *     rcp and sqrt the hardware's approximations (about an ulp each), so a
+ *     decision can differ from the exact one only within ~2^-20 (relative)
+ *     of its boundary;
  *   - a cache block of B tokens holds one region of B * (D * b / 8 + D / 16)
  *     bytes per kv head h, in head order: the code rows of tokens 0..B-1
  *     (token t at t * D * b / 8, group q at 2 b bytes each, element i at

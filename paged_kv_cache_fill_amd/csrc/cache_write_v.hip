@@ -212,10 +212,12 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
     }
     if (slot < 0 || (uint64_t)slot >= num_slots)
         return;
-    // The decisions below follow the FP32 sequence stated with pkv_dtype
-    // (in-order fused sum of squares, one reciprocal of the rms, one product
-    // per element); they equal the exact definition's except within FP32
-    // rounding of a decision boundary.
+    // The decisions below are taken in FP32 (in-order fused sum of squares,
+    // the hardware reciprocal square root of the mean square, one product
+    // per element, the scale from the hardware reciprocal and square root):
+    // about a dozen roundings of at most an ulp or two each, so they equal
+    // the exact definition's except within ~2^-20 (relative) of a decision
+    // boundary.
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -224,16 +226,25 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
     uint32_t w[2] = {0u, 0u};                           // codes of elements 0-7, 8-15
     uint32_t scale = 0;
     if (ss > 0.f) {
-        const float inv_r = 1.0f / sqrtf(ss * 0.0625f);
+        // +inf for a mean square below the normal range (those groups' scale
+        // rounds to zero), 0 for ss = +inf (codes 0, scale saturated)
+        const float inv_r = __builtin_amdgcn_rsqf(ss * 0.0625f);
         [[maybe_unused]] float cn4 = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const float u = x[i] * inv_r;
             const float au = fabsf(u);
+            // magnitude index: the number of midpoints below |u| (ties stay
+            // on the smaller magnitude), by binary search over the midpoints
             uint32_t m = 0;
 #pragma unroll
-            for (int j = 0; j + 1 < M; ++j)
-                m += au > cb.thr[j] ? 1u : 0u;          // ties stay on the smaller magnitude
+            for (int step = M / 2; step >= 1; step /= 2) {
+                float t = cb.thr[step - 1];
+#pragma unroll
+                for (int base = 2 * step; base + step - 1 < M - 1; base += 2 * step)
+                    t = m == (uint32_t)base ? cb.thr[base + step - 1] : t;
+                m += au > t ? (uint32_t)step : 0u;
+            }
             if constexpr (BITS == 4) {
                 const float mag = unpack_e4m3x2(__builtin_amdgcn_perm(cb.mag_hi, cb.mag_lo, m), false).x;
                 cn4 = fmaf(mag, mag, cn4);
@@ -266,7 +277,8 @@ __global__ __launch_bounds__(256) void cache_write_v_tq_kernel(
             cn = cn4;
         }
         // the norm correction: scale so that |scale x levels| = |x|
-        scale = e4m3_sat_x4(sqrtf(ss) / sqrtf(cn), 0.f, 0.f, 0.f) & 0xFFu;
+        const float ratio = __builtin_amdgcn_sqrtf(ss * __builtin_amdgcn_rcpf(cn));
+        scale = e4m3_sat_x4(ratio, 0.f, 0.f, 0.f) & 0xFFu;
     }
     // head h's region of the block: B code rows of D * BITS / 8 bytes, then
     // D / 16 scale rows (one per group) of B bytes
