@@ -189,11 +189,11 @@ __global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(
     const uint64_t u0 = gwave * a.units_per_wave;
     const uint64_t u1 = u0 + a.units_per_wave < a.num_units ? u0 + a.units_per_wave : a.num_units;
 
-    // Software pipeline over the wave's units: the next unit's row is loaded
-    // while the current one is computed and stored.  Loads are unconditional
-    // (rows past Hkv re-read the last head's row), so the compiler's wait
-    // before each unit covers only that unit's loads.
-    // a unit's row, slot and positions, all loaded one unit ahead
+    // Software pipeline over the wave's units: the rows, slots and positions
+    // of the next two units are loaded while the current one is computed and
+    // stored.  Loads are unconditional (rows past Hkv re-read the last head's
+    // row), so the compiler's wait before each unit covers only that unit's
+    // loads.
     struct Raw {
         u32x4 w[NC];
         int64_t slot;
@@ -360,28 +360,40 @@ __global__ __launch_bounds__(kKThreads) void cache_write_k_kernel(
             }
         };
         const uint32_t n = (uint32_t)(u1 - u0);
-        Raw ra, rb;
+        // loads run two units ahead of processing (a ring of three rows)
+        Raw ra, rb, rc;
         load_unit(lt, lg, ra);
         next(lt, lg);
-        convert_weights();
-        uint32_t i = 0;
-        for (; i + 2 < n; i += 2) {                     // both successors exist
+        if (n > 1) {
             load_unit(lt, lg, rb);
             next(lt, lg);
-            process(pt, pg, ra);
-            next(pt, pg);
-            load_unit(lt, lg, ra);
-            next(lt, lg);
-            process(pt, pg, rb);
-            next(pt, pg);
         }
-        if (i + 1 < n) {
-            load_unit(lt, lg, rb);
+        convert_weights();
+        for (uint32_t i = 0;;) {
+            if (i + 2 < n) {
+                load_unit(lt, lg, rc);
+                next(lt, lg);
+            }
             process(pt, pg, ra);
             next(pt, pg);
+            if (++i == n)
+                break;
+            if (i + 2 < n) {
+                load_unit(lt, lg, ra);
+                next(lt, lg);
+            }
             process(pt, pg, rb);
-        } else {
-            process(pt, pg, ra);
+            next(pt, pg);
+            if (++i == n)
+                break;
+            if (i + 2 < n) {
+                load_unit(lt, lg, rb);
+                next(lt, lg);
+            }
+            process(pt, pg, rc);
+            next(pt, pg);
+            if (++i == n)
+                break;
         }
     }
 }
@@ -513,14 +525,15 @@ extern "C" int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype,
     a.units_per_token = ceil_div(num_kv_heads, a.rows_per_wave);
     a.num_units = (uint64_t)num_tokens * a.units_per_token;
     // units per wave: one for BF16 and FP32 stores (the most waves in
-    // flight), up to four for E4M3 stores, whose lane exchange does more per
+    // flight), up to eight for E4M3 stores, whose lane exchange does more per
     // unit.  Population writes of 1.09 M (BF16) / 1.58 M (E4M3) tokens:
     // 0.812 / 0.852 / 0.866 / 0.871 ms (BF16) with at most 1 / 8 / 4 / 16
     // units, 1.036 / 0.913 / 0.918 / 0.946 ms (E4M3) with at most 1 / 2 /
-    // 4 / 16 (one run each); after the slot and positions moved to the row's
-    // loads, 0.929 / 0.921 ms (E4M3) with at most 2 / 4 (two runs).
+    // 4 / 16 (one run each, rows loaded one unit ahead); with the slot and
+    // positions loaded with the row and rows two units ahead, 0.920 / 0.919 /
+    // 0.909 ms (E4M3) with at most 2 / 4 / 8 (means of two runs).
     const uint64_t target_waves = 256ull * 32;
-    const uint64_t max_upw = cache_dtype == PKV_FP8_E4M3 ? 4 : 1;
+    const uint64_t max_upw = cache_dtype == PKV_FP8_E4M3 ? 8 : 1;
     uint64_t upw = a.num_units / target_waves;
     upw = upw < 1 ? 1 : upw > max_upw ? max_upw : upw;
     a.units_per_wave = (uint32_t)upw;
