@@ -525,15 +525,16 @@ extern "C" int pkv_cache_write_k_fused(const void* k_in, pkv_dtype in_dtype,
     a.units_per_token = ceil_div(num_kv_heads, a.rows_per_wave);
     a.num_units = (uint64_t)num_tokens * a.units_per_token;
     // units per wave: one for BF16 and FP32 stores (the most waves in
-    // flight), up to eight for E4M3 stores, whose lane exchange does more per
-    // unit.  Population writes of 1.09 M (BF16) / 1.58 M (E4M3) tokens:
+    // flight), up to sixteen for E4M3 stores, whose lane exchange does more
+    // per unit.  Population writes of 1.09 M (BF16) / 1.58 M (E4M3) tokens:
     // 0.812 / 0.852 / 0.866 / 0.871 ms (BF16) with at most 1 / 8 / 4 / 16
     // units, 1.036 / 0.913 / 0.918 / 0.946 ms (E4M3) with at most 1 / 2 /
     // 4 / 16 (one run each, rows loaded one unit ahead); with the slot and
     // positions loaded with the row and rows two units ahead, 0.920 / 0.919 /
-    // 0.909 ms (E4M3) with at most 2 / 4 / 8 (means of two runs).
+    // 0.909 / 0.895 ms (E4M3) with at most 2 / 4 / 8 / 16 (means of two runs)
+    // and 0.814 / 0.845 / 0.870 ms (BF16) with at most 1 / 2 / 4.
     const uint64_t target_waves = 256ull * 32;
-    const uint64_t max_upw = cache_dtype == PKV_FP8_E4M3 ? 8 : 1;
+    const uint64_t max_upw = cache_dtype == PKV_FP8_E4M3 ? 16 : 1;
     uint64_t upw = a.num_units / target_waves;
     upw = upw < 1 ? 1 : upw > max_upw ? max_upw : upw;
     a.units_per_wave = (uint32_t)upw;
