@@ -78,6 +78,23 @@ def test_e4m3_v_store_fp32_strided_input_bit_exact():
     assert (got == ref).all()
 
 
+@pytest.mark.parametrize("in_dt,H,D", [("bf16", 6, 128), ("bf16", 40, 128), ("f32", 3, 112),
+                                        ("f32", 24, 192)])
+def test_e4m3_v_store_row_shapes(in_dt, H, D):
+    """Rows whose 16-byte output columns do not divide a work-group (48 and 21
+    columns: tokens side by side with idle threads) or exceed it (320 and 288
+    columns: a column loop), from BF16 and FP32 input, with padding slots."""
+    T = 300
+    v = W.normal(4, 91 + H, (T, H * D)) * 30.0
+    if in_dt == "bf16":
+        v = W.bf16_bits(v)
+    slots = np.random.default_rng(H + D).permutation(20 * 16)[:T].astype(np.int64)
+    slots[::13] = -1
+    say(f"E4M3 V store of {in_dt} rows: H={H} D={D}")
+    got, ref = _v_store_both(v.reshape(T, H, D), in_dt, slots, H, D, 20, 0.37)
+    assert (got == ref).all()
+
+
 # ---------------------------------------------------------------- decode
 
 def _decode_both(q, q_dt, kp, k_dt, vp, v_dt, lay, *, Hq, Hkv, scale, k_scale=1.0, v_scale=1.0,

@@ -241,6 +241,34 @@ def test_k_write_head_dims_and_partial_rotary():
             check_k(host(g), ref, slots_np, cdt)
 
 
+@pytest.mark.parametrize("T,H,D", [(140_003, 3, 128), (140_003, 5, 64), (24_581, 3, 128)])
+def test_k_write_fp8_many_units_per_wave(T, H, D):
+    """E4M3 stores from BF16 rows with enough tokens that a wave takes several
+    (token, head-group) units (16 for the first two cases, 3 for the last:
+    the rows of the next two units are in flight while one is stored), with
+    an odd head count (rows past the last head in every unit), 1% padding
+    slots and a last wave with fewer units; the whole pool is compared."""
+    rng = np.random.default_rng(T + H)
+    x = rng.standard_normal((T, H, D)).astype(np.float32)
+    k = W.bf16_bits(x)
+    w = W.bf16_bits(rng.uniform(0.5, 1.5, D).astype(np.float32))
+    nb = (int(T * 1.02) + 15) // 16
+    slots_np = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots_np[rng.random(T) < 0.01] = -1
+    pos = rng.integers(0, 32768, T).astype(np.int32)
+    ref = np.full((nb, 16, H, D), 0x5A, np.uint8)
+    oracle.cache_write_k(k, "bf16", slots_np, ref, "fp8", num_kv_heads=H, head_dim=D,
+                         block_size=16, norm_weight=w, pos_t=pos, theta=10000.0, rotary_dim=D,
+                         k_scale=0.01, nthreads=16)
+    g = dev(np.full_like(ref, 0x5A))
+    say(f"E4M3 K write, {T} tokens, H={H}, D={D}")
+    pkv.cache_write_k_fused(dev(k), dev(slots_np), g, norm_weight=dev(w), pos_t=dev(pos),
+                            theta=10000.0, rotary_dim=D, k_scale=0.01)
+    got = host(g)
+    check_k(got, ref, slots_np, "fp8")
+    assert (got == 0x7E).any() or (got == 0xFE).any()     # some rows saturate
+
+
 def _stratified_patterns():
     hi = np.arange(1 << 16, dtype=np.uint32) << 16
     lows = np.array([0x0000, 0x0001, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x1234, 0xC000], np.uint32)
