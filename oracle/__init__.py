@@ -74,6 +74,10 @@ def lib():
                                         U32, U32, U32, U32, U32, U32, F32, U32, P, I32, F32,
                                         U32, U32, P, P, I32]
         L.pkvo_paged_decode.restype = None
+        L.pkvo_paged_decode_sparse_v.argtypes = [P, I32, U64, P, I32, F32, P, I32, F32, P, U32,
+                                                 P, U32, U32, U32, U32, U32, U32, U32, F32, U32,
+                                                 P, P, ctypes.c_double, P, P, I32]
+        L.pkvo_paged_decode_sparse_v.restype = None
         L.pkvo_paged_prefill.argtypes = [P, I32, U64, P, P, I32, F32, P, I32, F32, P, U32, P, U32,
                                          U32, U32, U32, U32, U32, U32, F32, U32, P, P, I32]
         L.pkvo_paged_prefill.restype = None
@@ -243,6 +247,37 @@ def paged_decode(q, q_dtype, k_cache, k_dtype, v_cache, v_dtype, block_tables, s
                             q_rope_theta, q_rope_offset,
                             q_rope_dim, _ptr(g), _ptr(out), nthreads)
     return out
+
+
+def paged_decode_sparse_v(q, q_dtype, k_cache, k_dtype, v_cache, v_dtype, block_tables,
+                          seq_lens, *, num_q_heads, num_kv_heads, head_dim_qk, head_dim_v,
+                          block_size, scale, tau, k_scale=1.0, v_scale=1.0, sliding_window=0,
+                          sinks=None, gate=None, nthreads=1):
+    """Decode attention with the sparse-V skip at threshold ``tau``: returns
+    (out, bound), FP32 [num_seqs, num_q_heads, head_dim_v] each.  ``out`` sums
+    w_t v_t over the positions whose softmax weight w_t exceeds tau, ``bound``
+    sums w_t |v_t| over the others (times the gate, |gate|), so that any
+    decode skipping a subset of the latter lies within ``bound`` of ``out``."""
+    q = _c(q, NP_TYPES[q_dtype])
+    bt = _c(block_tables, np.int32)
+    if bt.ndim == 1:
+        bt = bt.reshape(1, -1)
+    sl = _c(seq_lens, np.int32)
+    S = sl.size
+    kc = _c(k_cache, NP_TYPES[k_dtype])
+    vc = _c(v_cache, NP_TYPES[v_dtype])
+    num_blocks = kc.size // (block_size * num_kv_heads * head_dim_qk)
+    g = _c(gate, np.float32)
+    sk = _c(sinks, np.float32)
+    out = np.empty((S, num_q_heads, head_dim_v), np.float32)
+    bound = np.empty_like(out)
+    lib().pkvo_paged_decode_sparse_v(_ptr(q), DTYPES[q_dtype], num_q_heads * head_dim_qk,
+                                     _ptr(kc), DTYPES[k_dtype], k_scale, _ptr(vc),
+                                     DTYPES[v_dtype], v_scale, _ptr(bt), bt.shape[1], _ptr(sl),
+                                     S, num_blocks, num_q_heads, num_kv_heads, head_dim_qk,
+                                     head_dim_v, block_size, scale, sliding_window, _ptr(sk),
+                                     _ptr(g), float(tau), _ptr(out), _ptr(bound), nthreads)
+    return out, bound
 
 
 def paged_prefill(q, q_dtype, cu_q, k_cache, k_dtype, v_cache, v_dtype, block_tables, seq_lens, *,

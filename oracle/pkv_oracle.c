@@ -369,7 +369,8 @@ void pkvo_cache_write_k(const void* k_in, int in_dtype, uint64_t in_token_stride
  *  - the encoder's decisions follow this definition in FP64 arithmetic:
  *    the rms, each x / rms, the nearest-level choice and the ratio of norms
  *    are exact up to FP64 rounding, and the ratio is rounded once, to E4M3;
- *  - no rotation and no sparse skip (the decode is exact). */
+ *  - no rotation; the decode is exact, and its sparse-V variant is
+ *    pkvo_paged_decode_sparse_v. */
 
 static double std_normal_pdf(double x) { return exp(-0.5 * x * x) / sqrt(2.0 * 3.14159265358979323846); }
 static double std_normal_cdf(double x) { return 0.5 * erfc(-x / sqrt(2.0)); }
@@ -633,6 +634,8 @@ typedef struct {
     int q_rope; float q_rope_theta; uint32_t q_rope_offset, q_rope_dim;
     const float* gate; float* out;
     double tq_mags[8];          /* decoded codebook magnitudes of a TQ V cache */
+    double spv_tau;             /* sparse-V threshold (with spv_bound) */
+    float* spv_bound;           /* NULL: exact decode; else the sparse-V bound rows */
 } decode_ctx;
 
 /* Dequantised cache element: BF16 and FP32 exactly, E4M3 exactly times its
@@ -654,24 +657,13 @@ static void tq_fill_mags(decode_ctx* c)
         c->tq_mags[j] = pkvo_f64_from_e4m3(mc[j]);
 }
 
-/* Attention of one query vector q (kv head g, query head h) of sequence s
- * over the positions [lo, end) of its cache, written to dst[Dv]:
- *   softmax over s_t = scale * <q, k_t> (t attended), times v_t, summed.
- * Tokens of an unmapped block or past the table are excluded; with no
- * attended token the row is zero. */
-static void attend(const decode_ctx* c, uint32_t s, uint32_t g, uint32_t h, int32_t end,
-                   int32_t lo, const double* q, double* o, const float* gate_row, float* dst)
+/* Scores of one query vector q (kv head g) of sequence s over the positions
+ * [lo, end): sc[t] = scale * <q, k_t> for the attended t (ok[t] = 1);
+ * tokens outside the window, of an unmapped block or past the table are
+ * excluded (ok[t] = 0).  Returns the largest score (-inf if none). */
+static double score_pass(const decode_ctx* c, uint32_t s, uint32_t g, int32_t end, int32_t lo,
+                         const double* q, double* sc, unsigned char* ok)
 {
-    for (uint32_t d = 0; d < c->Dv; ++d)
-        o[d] = 0.0;
-    if (end <= 0) {
-        for (uint32_t d = 0; d < c->Dv; ++d)
-            dst[d] = 0.0f;
-        return;
-    }
-    /* pass 1: scores and their maximum */
-    double* sc = (double*)malloc(sizeof(double) * (size_t)end);
-    unsigned char* ok = (unsigned char*)malloc((size_t)end);
     double m = -INFINITY;
     for (int32_t t = 0; t < end; ++t) {
         uint32_t b = (uint32_t)t / c->B;
@@ -692,21 +684,49 @@ static void attend(const decode_ctx* c, uint32_t s, uint32_t g, uint32_t h, int3
         ok[t] = 1;
         if (sc[t] > m) m = sc[t];
     }
+    return m;
+}
+
+/* Element d of the V row of position t (kv head g) of sequence s, whose
+ * block is mapped. */
+static double v_value(const decode_ctx* c, uint32_t s, int32_t t, uint32_t g, uint32_t d)
+{
+    uint32_t b = (uint32_t)t / c->B;
+    int32_t blk = c->block_tables[(uint64_t)s * c->max_blocks_per_seq + b];
+    if (is_tq(c->v_dtype))
+        return tq_elem(c->v_cache, tq_bits(c->v_dtype), c->B, c->Hkv, c->Dv, c->tq_mags,
+                       (uint64_t)blk, (uint32_t)t % c->B, g, d);
+    uint64_t row = (uint64_t)blk * c->B + (uint32_t)t % c->B;
+    return cache_elem(c->v_cache, c->v_dtype, c->v_scale, (row * c->Hkv + g) * c->Dv + d);
+}
+
+/* Attention of one query vector q (kv head g, query head h) of sequence s
+ * over the positions [lo, end) of its cache, written to dst[Dv]:
+ *   softmax over s_t = scale * <q, k_t> (t attended), times v_t, summed.
+ * Tokens of an unmapped block or past the table are excluded; with no
+ * attended token the row is zero. */
+static void attend(const decode_ctx* c, uint32_t s, uint32_t g, uint32_t h, int32_t end,
+                   int32_t lo, const double* q, double* o, const float* gate_row, float* dst)
+{
+    for (uint32_t d = 0; d < c->Dv; ++d)
+        o[d] = 0.0;
+    if (end <= 0) {
+        for (uint32_t d = 0; d < c->Dv; ++d)
+            dst[d] = 0.0f;
+        return;
+    }
+    /* pass 1: scores and their maximum */
+    double* sc = (double*)malloc(sizeof(double) * (size_t)end);
+    unsigned char* ok = (unsigned char*)malloc((size_t)end);
+    const double m = score_pass(c, s, g, end, lo, q, sc, ok);
     /* pass 2: softmax weights and the weighted sum of V rows */
     double l = 0.0;
     for (int32_t t = 0; t < end; ++t) {
         if (!ok[t]) continue;
-        uint32_t b = (uint32_t)t / c->B;
-        int32_t blk = c->block_tables[(uint64_t)s * c->max_blocks_per_seq + b];
-        uint64_t row = (uint64_t)blk * c->B + (uint32_t)t % c->B;
-        uint64_t voff = (row * c->Hkv + g) * c->Dv;
         double pt = exp(sc[t] - m);
         l += pt;
         for (uint32_t d = 0; d < c->Dv; ++d)
-            o[d] += pt * (is_tq(c->v_dtype)
-                              ? tq_elem(c->v_cache, tq_bits(c->v_dtype), c->B, c->Hkv, c->Dv,
-                                        c->tq_mags, (uint64_t)blk, (uint32_t)t % c->B, g, d)
-                              : cache_elem(c->v_cache, c->v_dtype, c->v_scale, voff + d));
+            o[d] += pt * v_value(c, s, t, g, d);
     }
     /* Attention sink (p1 mla_paged_decode_fp8 takes a `sinks` pointer,
      * semantics unstated; our reading): one logit per query head, in the
@@ -732,6 +752,63 @@ static void attend(const decode_ctx* c, uint32_t s, uint32_t g, uint32_t h, int3
     free(ok);
 }
 
+/* Sparse-V skip (p1 Turbo-V decode docs: V loaded and dequantised "sparse"
+ * on the batched and remainder paths; p2 paged_decode_attn_fp8k_turbo3v:
+ * a position's V load and dequantisation are skipped when its attention
+ * weight is at most TQ_PLUS_SPARSE_V_THRESHOLD, a value the pages do not
+ * give).  Reading taken: the attention weight of position t is its softmax
+ * weight w_t = exp(s_t) / Z with Z the exact decode's denominator (sinks
+ * included); a skipped position leaves the sum over V and stays in Z (its
+ * score is computed either way).  With threshold tau, for query head h:
+ *   dst[d]  = sum over attended t with w_t >  tau of w_t v_t[d]   (x gate[d])
+ *   bdst[d] = sum over attended t with w_t <= tau of w_t |v_t[d]| (x |gate[d]|)
+ * so that the exact output differs from dst by at most bdst, and so does
+ * the result of leaving out any subset of the positions with w_t <= tau.
+ * tau = 0 gives the exact decode (every weight is positive). */
+static void attend_sparse_v(const decode_ctx* c, double tau, uint32_t s, uint32_t g, uint32_t h,
+                            int32_t end, int32_t lo, const double* q, double* o, double* bnd,
+                            const float* gate_row, float* dst, float* bdst)
+{
+    for (uint32_t d = 0; d < c->Dv; ++d)
+        o[d] = bnd[d] = 0.0;
+    if (end > 0) {
+        double* sc = (double*)malloc(sizeof(double) * (size_t)end);
+        unsigned char* ok = (unsigned char*)malloc((size_t)end);
+        const double m = score_pass(c, s, g, end, lo, q, sc, ok);
+        int any = 0;
+        for (int32_t t = 0; t < end; ++t)
+            any |= ok[t];
+        if (any) {
+            /* Z relative to the larger of the top score and the sink */
+            double mm = m;
+            if (c->sinks && (double)c->sinks[h] > mm)
+                mm = (double)c->sinks[h];
+            double z = c->sinks ? exp((double)c->sinks[h] - mm) : 0.0;
+            for (int32_t t = 0; t < end; ++t)
+                if (ok[t])
+                    z += exp(sc[t] - mm);
+            for (int32_t t = 0; t < end; ++t) {
+                if (!ok[t]) continue;
+                const double w = exp(sc[t] - mm) / z;
+                for (uint32_t d = 0; d < c->Dv; ++d) {
+                    const double v = v_value(c, s, t, g, d);
+                    if (w > tau)
+                        o[d] += w * v;
+                    else
+                        bnd[d] += w * fabs(v);
+                }
+            }
+        }
+        free(sc);
+        free(ok);
+    }
+    for (uint32_t d = 0; d < c->Dv; ++d) {
+        const double gd = gate_row ? (double)gate_row[d] : 1.0;
+        dst[d] = (float)(o[d] * gd);
+        bdst[d] = (float)(bnd[d] * fabs(gd));
+    }
+}
+
 /* Sliding window of W tokens (p1/p3 decode launchers take a sliding_window
  * argument, semantics unstated; our reading): a query at position p sees the
  * W most recent positions, [p + 1 - W, p + 1); W = 0 means no window. */
@@ -746,6 +823,7 @@ static void decode_range(void* p, uint64_t u0, uint64_t u1)
     const uint32_t G = c->Hq / c->Hkv;
     double* q = (double*)malloc(sizeof(double) * c->Dqk);
     double* o = (double*)malloc(sizeof(double) * c->Dv);
+    double* bnd = (double*)malloc(sizeof(double) * c->Dv);
     for (uint64_t u = u0; u < u1; ++u) {
         uint32_t s = (uint32_t)(u / c->Hq), h = (uint32_t)(u % c->Hq);
         uint32_t g = h / G;                      /* GQA: contiguous groups */
@@ -758,11 +836,16 @@ static void decode_range(void* p, uint64_t u0, uint64_t u1)
             int32_t pos3[3] = {n - 1, n - 1, n - 1};
             rope_rotate(q, c->q_rope_offset, c->q_rope_dim, c->q_rope_theta, pos3);
         }
-        attend(c, s, g, h, n, window_start(c->window, n), q, o, c->gate ? c->gate + orow : NULL,
-               c->out + orow);
+        if (c->spv_bound)
+            attend_sparse_v(c, c->spv_tau, s, g, h, n, window_start(c->window, n), q, o, bnd,
+                            c->gate ? c->gate + orow : NULL, c->out + orow, c->spv_bound + orow);
+        else
+            attend(c, s, g, h, n, window_start(c->window, n), q, o,
+                   c->gate ? c->gate + orow : NULL, c->out + orow);
     }
     free(q);
     free(o);
+    free(bnd);
 }
 
 void pkvo_paged_decode(const void* q, int q_dtype, uint64_t q_seq_stride,
@@ -780,7 +863,28 @@ void pkvo_paged_decode(const void* q, int q_dtype, uint64_t q_seq_stride,
                     v_scale, block_tables, max_blocks_per_seq, seq_lens, num_blocks,
                     num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, block_size, scale,
                     sliding_window, sinks, q_rope, q_rope_theta, q_rope_offset, q_rope_dim, gate, out,
-                    {0}};
+                    {0}, 0.0, NULL};
+    tq_fill_mags(&c);
+    parallel_for((uint64_t)num_seqs * num_q_heads, nthreads, decode_range, &c);
+}
+
+/* The decode with the sparse-V skip at threshold tau >= 0 (attend_sparse_v):
+ * out as for pkvo_paged_decode but summing only the positions whose weight
+ * exceeds tau, bound[S, Hq, Dv] the weighted |V| of the others. */
+void pkvo_paged_decode_sparse_v(const void* q, int q_dtype, uint64_t q_seq_stride,
+                                const void* k_cache, int k_dtype, float k_scale,
+                                const void* v_cache, int v_dtype, float v_scale,
+                                const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
+                                uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
+                                uint32_t head_dim_v, uint32_t block_size, float scale,
+                                uint32_t sliding_window, const float* sinks, const float* gate,
+                                double tau, float* out, float* bound, int nthreads)
+{
+    decode_ctx c = {q, q_dtype, q_seq_stride, k_cache, k_dtype, k_scale, v_cache, v_dtype,
+                    v_scale, block_tables, max_blocks_per_seq, seq_lens, num_blocks,
+                    num_q_heads, num_kv_heads, head_dim_qk, head_dim_v, block_size, scale,
+                    sliding_window, sinks, 0, 0.0f, 0, 0, gate, out, {0}, tau, bound};
     tq_fill_mags(&c);
     parallel_for((uint64_t)num_seqs * num_q_heads, nthreads, decode_range, &c);
 }
@@ -842,7 +946,7 @@ void pkvo_paged_prefill(const void* q, int q_dtype, uint64_t q_token_stride, con
     decode_ctx d = {q, q_dtype, 0, k_cache, k_dtype, k_scale, v_cache, v_dtype, v_scale,
                     block_tables, max_blocks_per_seq, seq_lens, num_blocks, num_q_heads,
                     num_kv_heads, head_dim_qk, head_dim_v, block_size, scale, sliding_window,
-                    sinks, 0, 0.0f, 0, 0, NULL, out, {0}};
+                    sinks, 0, 0.0f, 0, 0, NULL, out, {0}, 0.0, NULL};
     tq_fill_mags(&d);
     c.d = d;
     c.q_token_stride = q_token_stride;
