@@ -280,6 +280,24 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *                     TQ: num_blocks blocks of pkv_v_block_bytes bytes, laid out
  *                     as stated with pkv_dtype
  *   k_scale, v_scale  E4M3 caches only: per-tensor scales, finite and > 0
+ *   sparse_v_threshold  the sparse-V skip of TQ V caches ([p2]
+ *                     paged_decode_attn_fp8k_turbo3v: a position's V is not
+ *                     loaded or dequantised when its attention weight is at
+ *                     most a threshold whose value the pages do not give;
+ *                     [p1] calls its Turbo-V decodes "sparse V").  0 = exact
+ *                     decode; in (0, 1): a position whose weight relative to
+ *                     the largest score seen so far in its split-K piece,
+ *                     exp(s_t - running max), is at most the threshold leaves
+ *                     the sum over V (it stays in Z).  That weight is at least
+ *                     the softmax weight exp(s_t) / Z, so the positions left
+ *                     out are a subset of those whose weight is at most the
+ *                     threshold; which ones depends on the order and the
+ *                     split-K pieces in which positions are visited.  A
+ *                     16-token block none of whose positions is kept for any
+ *                     query head of the GQA group skips the V decode and the
+ *                     PV product (its V bytes are still read).  Outside
+ *                     [0, 1) (or NaN): PKV_ERR_INVALID; > 0 with a non-TQ V
+ *                     cache: PKV_ERR_UNSUPPORTED
  *   scale             softmax scale of the scores, finite and > 0 (else
  *                     PKV_ERR_INVALID)
  *   block_tables  in  int32 [num_seqs, max_blocks_per_seq]
@@ -304,7 +322,7 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *                 the same time (other streams) need workspaces of their own
  * Supported: (q, K, V) dtypes (BF16, BF16 or FP8_E4M3, BF16 or FP8_E4M3 or
  *   TQ2/3/4), (FP32, FP32, FP32); TQ V with head_dim 128; the decode of TQ V
- *   is exact (no weight-threshold skipping); num_q_heads % num_kv_heads == 0;
+ *   is exact unless sparse_v_threshold > 0; num_q_heads % num_kv_heads == 0;
  *   block_size 16;
  *   head_dim_qk in {64, 128, 192, 256}, head_dim_v in {64, 128} (BF16/E4M3
  *   caches: head_dim_qk == head_dim_v in {64, 128}, GQA group <= 16; FP32:
@@ -317,8 +335,9 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
 int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
                           const void* k_cache, pkv_dtype k_dtype, float k_scale,
                           const void* v_cache, pkv_dtype v_dtype, float v_scale,
-                          const int32_t* block_tables, uint32_t max_blocks_per_seq,
-                          const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
+                          float sparse_v_threshold, const int32_t* block_tables,
+                          uint32_t max_blocks_per_seq, const int32_t* seq_lens,
+                          uint32_t num_seqs, uint32_t num_blocks,
                           uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
                           uint32_t head_dim_v, uint32_t block_size, float scale,
                           uint32_t sliding_window, const float* sinks,
@@ -354,7 +373,8 @@ int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_strid
 int pkv_paged_decode_attn_noalloc(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
                                   const void* k_cache, pkv_dtype k_dtype, float k_scale,
                                   const void* v_cache, pkv_dtype v_dtype, float v_scale,
-                                  const int32_t* block_tables, uint32_t max_blocks_per_seq,
+                                  float sparse_v_threshold, const int32_t* block_tables,
+                                  uint32_t max_blocks_per_seq,
                                   const int32_t* seq_lens, uint32_t num_seqs,
                                   uint32_t num_blocks, uint32_t num_q_heads,
                                   uint32_t num_kv_heads, uint32_t head_dim_qk,

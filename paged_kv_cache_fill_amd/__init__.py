@@ -42,12 +42,12 @@ _SIGNATURES = {
     "pkv_cache_write_v": ([_P, _I32, _U64, _P, _U32, _U32, _U32, _U32, _U32, _P, _I32, _F32,
                            _P], _I32),
     "pkv_decode_workspace_bytes": ([_U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32], _SZ),
-    "pkv_paged_decode_attn": ([_P, _I32, _U64, _P, _I32, _F32, _P, _I32, _F32, _P, _U32, _P,
-                               _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32, _U32, _P, _I32,
-                               _F32, _U32, _U32, _P, _P, _U32, _P, _SZ, _P], _I32),
-    "pkv_paged_decode_attn_noalloc": ([_P, _I32, _U64, _P, _I32, _F32, _P, _I32, _F32, _P, _U32,
-                                       _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32, _U32,
-                                       _P, _I32, _F32, _U32, _U32, _P, _P, _U32, _P], _I32),
+    "pkv_paged_decode_attn": ([_P, _I32, _U64, _P, _I32, _F32, _P, _I32, _F32, _F32, _P, _U32,
+                               _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32, _U32, _P,
+                               _I32, _F32, _U32, _U32, _P, _P, _U32, _P, _SZ, _P], _I32),
+    "pkv_paged_decode_attn_noalloc": ([_P, _I32, _U64, _P, _I32, _F32, _P, _I32, _F32, _F32, _P,
+                                       _U32, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32,
+                                       _U32, _P, _I32, _F32, _U32, _U32, _P, _P, _U32, _P], _I32),
     "pkv_paged_prefill_attn": ([_P, _I32, _U64, _P, _U32, _U32, _P, _I32, _F32, _P, _I32, _F32,
                                 _P, _U32, _P, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _F32,
                                 _U32, _P, _P, _P], _I32),
@@ -244,8 +244,8 @@ def decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim_v, max_
 
 
 def _decode_args(q, k_cache, v_cache, block_tables, seq_lens, *, scale, k_scale, v_scale,
-                 sliding_window, sinks, gate, out, q_rope, q_rope_theta, q_rope_offset,
-                 q_rope_dim, split_tokens, v_tq_bits, alloc_out):
+                 sparse_v_threshold, sliding_window, sinks, gate, out, q_rope, q_rope_theta,
+                 q_rope_offset, q_rope_dim, split_tokens, v_tq_bits, alloc_out):
     """Checks the decode arguments; returns (leading C arguments up to and
     including split_tokens, out, (S, Hq, Hkv, Dv, M, B))."""
     _dev(q, k_cache, v_cache, block_tables, seq_lens, sinks, gate, out)
@@ -283,7 +283,8 @@ def _decode_args(q, k_cache, v_cache, block_tables, seq_lens, *, scale, k_scale,
     M = block_tables.shape[1]
     q_stride = q.stride(0) if S > 1 else Hq * Dqk
     args = (_ptr(q), _dtype(q), q_stride, _ptr(k_cache), _dtype(k_cache), k_scale,
-            _ptr(v_cache), v_dt, v_scale, _ptr(block_tables), M, _ptr(seq_lens), S, nb, Hq, Hkv,
+            _ptr(v_cache), v_dt, v_scale, sparse_v_threshold, _ptr(block_tables), M,
+            _ptr(seq_lens), S, nb, Hq, Hkv,
             Dqk, Dv, B, scale, sliding_window, _ptr(sinks), int(bool(q_rope)), q_rope_theta,
             q_rope_offset, q_rope_dim, _ptr(gate), _ptr(out), split_tokens)
     return args, out, (S, Hq, Hkv, Dv, M, B)
@@ -294,20 +295,22 @@ def paged_decode_attn(q, k_cache, v_cache, block_tables, seq_lens, *, scale: flo
                       sinks=None, gate=None, out=None, q_rope: bool = False,
                       q_rope_theta: float = 10000.0, q_rope_offset: int = 0,
                       q_rope_dim: int = 0, split_tokens: int = 0, workspace=None,
-                      v_tq_bits: int = 0):
+                      v_tq_bits: int = 0, sparse_v_threshold: float = 0.0):
     """One-query-token paged decode attention (pkv_paged_decode_attn).
 
     q [S, Hq, Dqk]; k_cache [nb, B, Hkv, Dqk]; v_cache [nb, B, Hkv, Dv];
     block_tables int32 [S, M]; seq_lens int32 [S]; sinks FP32 [Hq] or None;
     gate FP32 [S, Hq, Dv] or None.  Returns out FP32 [S, Hq, Dv].
     ``workspace`` (uint8 device tensor) is allocated here when not given.
+    ``sparse_v_threshold`` in [0, 1) (TQ V only): the sparse-V skip.
     """
     _dev(workspace)
     args, out, (S, Hq, Hkv, Dv, M, B) = _decode_args(
         q, k_cache, v_cache, block_tables, seq_lens, scale=scale, k_scale=k_scale,
-        v_scale=v_scale, sliding_window=sliding_window, sinks=sinks, gate=gate, out=out,
-        q_rope=q_rope, q_rope_theta=q_rope_theta, q_rope_offset=q_rope_offset,
-        q_rope_dim=q_rope_dim, split_tokens=split_tokens, v_tq_bits=v_tq_bits, alloc_out=True)
+        v_scale=v_scale, sparse_v_threshold=sparse_v_threshold, sliding_window=sliding_window,
+        sinks=sinks, gate=gate, out=out, q_rope=q_rope, q_rope_theta=q_rope_theta,
+        q_rope_offset=q_rope_offset, q_rope_dim=q_rope_dim, split_tokens=split_tokens,
+        v_tq_bits=v_tq_bits, alloc_out=True)
     need = decode_workspace_bytes(S, Hq, Hkv, Dv, M, B, split_tokens, sliding_window) if S else 0
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -321,16 +324,18 @@ def paged_decode_attn_noalloc(q, k_cache, v_cache, block_tables, seq_lens, *, ou
                               sliding_window: int = 0, sinks=None, gate=None,
                               q_rope: bool = False, q_rope_theta: float = 10000.0,
                               q_rope_offset: int = 0, q_rope_dim: int = 0,
-                              split_tokens: int = 0, v_tq_bits: int = 0):
+                              split_tokens: int = 0, v_tq_bits: int = 0,
+                              sparse_v_threshold: float = 0.0):
     """paged_decode_attn with the split partials in the library's device
     scratch (pkv_paged_decode_attn_noalloc): allocates nothing, so ``out``
     must be given.  Calls that may overlap on one GPU share the scratch and
     race; at most PKV_DECODE_SCRATCH_BYTES (32 MiB) of partials."""
     args, out, _ = _decode_args(
         q, k_cache, v_cache, block_tables, seq_lens, scale=scale, k_scale=k_scale,
-        v_scale=v_scale, sliding_window=sliding_window, sinks=sinks, gate=gate, out=out,
-        q_rope=q_rope, q_rope_theta=q_rope_theta, q_rope_offset=q_rope_offset,
-        q_rope_dim=q_rope_dim, split_tokens=split_tokens, v_tq_bits=v_tq_bits, alloc_out=False)
+        v_scale=v_scale, sparse_v_threshold=sparse_v_threshold, sliding_window=sliding_window,
+        sinks=sinks, gate=gate, out=out, q_rope=q_rope, q_rope_theta=q_rope_theta,
+        q_rope_offset=q_rope_offset, q_rope_dim=q_rope_dim, split_tokens=split_tokens,
+        v_tq_bits=v_tq_bits, alloc_out=False)
     _check(load().pkv_paged_decode_attn_noalloc(*args, _stream()))
     return out
 

@@ -90,6 +90,7 @@ struct DecodeArgs {
     uint32_t q_rope_offset;
     uint32_t q_rope_dim;
     float q_invf[128];
+    float spv_thr;          // sparse-V skip (TQ V): threshold x 2^15, the units of the FP16 weights
 };
 
 // ------------------------------------------------------------------ helpers
@@ -348,8 +349,9 @@ __device__ __forceinline__ void e4m3_pv(const float (&p)[4], const uint32_t (&v)
 // KT: 0 = BF16, 1 = E4M3 K cache.  VT: 0 = BF16, 1 = E4M3, 2/3/4 = the
 // TurboQuant-style V with that many bits per code (D = 128).  D: head dim
 // of q, K and V (64 or 128).  The K operand layout is KFrag (attn_common.h).
+// SPV (TQ V only): the sparse-V skip at threshold a.spv_thr.
 //
-template <int KT, int VT, int D, int PF, bool BAL>
+template <int KT, int VT, int D, int PF, bool BAL, bool SPV>
 __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t kv_groups)
 {
     using KF = KFrag<KT, D>;
@@ -359,6 +361,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
     constexpr int DPL = D / 16;                // V dims per lane
     constexpr bool TQ = VT >= 2;               // TurboQuant-style V, VT bits per code
     static_assert(!TQ || D == 128, "TQ V decode is for head dim 128");
+    static_assert(TQ || !SPV, "the sparse-V skip is for TQ V");
     constexpr uint32_t VES = VT == 0 ? 2 : 1;  // V element bytes (BF16 / E4M3)
     // V words per lane per token: 4, 2 or 1; TQ: the codes (an 8-byte window
     // for 3-bit codes, else one word) + the scale byte
@@ -622,6 +625,26 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
                         st.v[r][w] = 0u;
         }
         if constexpr (TQ) {
+            if constexpr (SPV) {
+                // Sparse-V skip (page 2, paged_decode_attn_fp8k_turbo3v): a
+                // position whose weight is at most the threshold leaves the
+                // PV product; its weight stays in l.  The weight at hand is
+                // p / 2^15 = exp(s - running max), which is at least the
+                // final softmax weight, so every position left out has a
+                // weight at most the threshold.  Rows past the GQA group
+                // never count.  A block with no position kept in any row
+                // skips the V decode and the PV MFMAs; its V words were
+                // loaded a block ahead, before its weights existed.
+                bool keep_any = false;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const bool keep = p[r] > a.spv_thr;
+                    p[r] = keep ? p[r] : 0.f;
+                    keep_any |= keep && (uint32_t)ln < a.G;
+                }
+                if (!__builtin_amdgcn_ballot_w64(keep_any))
+                    return;
+            }
             tq_pv<VT>(a, p, st.v, tq_shift, tq_ssel, o);
             return;
         } else if constexpr (VT == 1) {
@@ -1316,8 +1339,8 @@ namespace pkv {
 static int paged_decode(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
                         const void* k_cache, pkv_dtype k_dtype, float k_scale,
                         const void* v_cache, pkv_dtype v_dtype, float v_scale,
-                        const int32_t* block_tables, uint32_t max_blocks_per_seq,
-                        const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
+                        float sparse_v_threshold, const int32_t* block_tables,
+                        uint32_t max_blocks_per_seq, const int32_t* seq_lens, uint32_t num_seqs, uint32_t num_blocks,
                         uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim_qk,
                         uint32_t head_dim_v, uint32_t block_size, float scale,
                         uint32_t sliding_window, const float* sinks, int q_rope,
@@ -1359,6 +1382,10 @@ static int paged_decode(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
         return fail(PKV_ERR_INVALID, "paged_decode_attn: k_scale must be finite and > 0");
     if (v_dtype == PKV_FP8_E4M3 && !(v_scale > 0.0f && v_scale < INFINITY))
         return fail(PKV_ERR_INVALID, "paged_decode_attn: v_scale must be finite and > 0");
+    if (!(sparse_v_threshold >= 0.0f && sparse_v_threshold < 1.0f))
+        return fail(PKV_ERR_INVALID, "paged_decode_attn: sparse_v_threshold must be in [0, 1)");
+    if (sparse_v_threshold > 0.0f && !is_tq(v_dtype))
+        return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: the sparse-V skip is for TQ V caches");
     if (q_rope && q_rope_dim > 0) {
         if (!f32_path)
             return fail(PKV_ERR_UNSUPPORTED, "paged_decode_attn: query rotation is supported for FP32 q/K/V");
@@ -1445,6 +1472,7 @@ static int paged_decode(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
         for (int i = 0; i < 4; ++i)
             a.tq_f16[i] = book.f16_lut[i];
         a.out_scale = 1.f / 32768.f;          // the 2^15 on the FP16 weights
+        a.spv_thr = sparse_v_threshold * 32768.f;   // exact: a power-of-two factor
         a.v_blk_bytes = (uint32_t)tq_block_bytes(book.bits, kBS, num_kv_heads, head_dim_v);
     }
     a.q_rope = (q_rope && q_rope_dim > 0) ? 1u : 0u;
@@ -1467,15 +1495,19 @@ static int paged_decode(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
         const dim3 block(64 * kvpb);
         const int kt = k_dtype == PKV_FP8_E4M3;
         const int vt = is_tq(v_dtype) ? tq_bits(v_dtype) : v_dtype == PKV_FP8_E4M3;
-#define PKV_MFMA_B(KT, VT, D, BAL)                                                              \
-    if (kt == KT && vt == VT && head_dim_qk == D && bal == BAL)                                \
-        hipLaunchKernelGGL((decode_mfma_kernel<KT, VT, D, kPrefetch, BAL>), grid, block, 0, st, a, kvg);
-#define PKV_MFMA(KT, VT, D) PKV_MFMA_B(KT, VT, D, false) PKV_MFMA_B(KT, VT, D, true)
+#define PKV_MFMA_B(KT, VT, D, BAL, SPV)                                                         \
+    if (kt == KT && vt == VT && head_dim_qk == D && bal == BAL && spv == SPV)                  \
+        hipLaunchKernelGGL((decode_mfma_kernel<KT, VT, D, kPrefetch, BAL, SPV>), grid, block, 0, st, a, kvg);
+#define PKV_MFMA(KT, VT, D) PKV_MFMA_B(KT, VT, D, false, false) PKV_MFMA_B(KT, VT, D, true, false)
+#define PKV_MFMA_TQ(KT, VT)                                                                     \
+    PKV_MFMA(KT, VT, 128) PKV_MFMA_B(KT, VT, 128, false, true) PKV_MFMA_B(KT, VT, 128, true, true)
         const bool bal = plan.ranges != 0;
+        const bool spv = sparse_v_threshold > 0.0f;
         PKV_MFMA(0, 0, 128) PKV_MFMA(0, 0, 64) PKV_MFMA(1, 0, 128) PKV_MFMA(1, 0, 64)
         PKV_MFMA(0, 1, 128) PKV_MFMA(0, 1, 64) PKV_MFMA(1, 1, 128) PKV_MFMA(1, 1, 64)
-        PKV_MFMA(0, 2, 128) PKV_MFMA(0, 3, 128) PKV_MFMA(0, 4, 128)
-        PKV_MFMA(1, 2, 128) PKV_MFMA(1, 3, 128) PKV_MFMA(1, 4, 128)
+        PKV_MFMA_TQ(0, 2) PKV_MFMA_TQ(0, 3) PKV_MFMA_TQ(0, 4)
+        PKV_MFMA_TQ(1, 2) PKV_MFMA_TQ(1, 3) PKV_MFMA_TQ(1, 4)
+#undef PKV_MFMA_TQ
 #undef PKV_MFMA
 #undef PKV_MFMA_B
     } else {
@@ -1508,6 +1540,7 @@ static int paged_decode(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
 extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride,
                                      const void* k_cache, pkv_dtype k_dtype, float k_scale,
                                      const void* v_cache, pkv_dtype v_dtype, float v_scale,
+                                     float sparse_v_threshold,
                                      const int32_t* block_tables, uint32_t max_blocks_per_seq,
                                      const int32_t* seq_lens, uint32_t num_seqs,
                                      uint32_t num_blocks, uint32_t num_q_heads,
@@ -1520,7 +1553,8 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
                                      size_t workspace_bytes, void* stream)
 {
     return pkv::paged_decode(q, q_dtype, q_seq_stride, k_cache, k_dtype, k_scale, v_cache,
-                             v_dtype, v_scale, block_tables, max_blocks_per_seq, seq_lens,
+                             v_dtype, v_scale, sparse_v_threshold, block_tables,
+                             max_blocks_per_seq, seq_lens,
                              num_seqs, num_blocks, num_q_heads, num_kv_heads, head_dim_qk,
                              head_dim_v, block_size, scale, sliding_window, sinks, q_rope,
                              q_rope_theta, q_rope_offset, q_rope_dim, gate, out, split_tokens,
@@ -1530,7 +1564,8 @@ extern "C" int pkv_paged_decode_attn(const void* q, pkv_dtype q_dtype, uint64_t 
 extern "C" int pkv_paged_decode_attn_noalloc(
     const void* q, pkv_dtype q_dtype, uint64_t q_seq_stride, const void* k_cache,
     pkv_dtype k_dtype, float k_scale, const void* v_cache, pkv_dtype v_dtype, float v_scale,
-    const int32_t* block_tables, uint32_t max_blocks_per_seq, const int32_t* seq_lens,
+    float sparse_v_threshold, const int32_t* block_tables, uint32_t max_blocks_per_seq,
+    const int32_t* seq_lens,
     uint32_t num_seqs, uint32_t num_blocks, uint32_t num_q_heads, uint32_t num_kv_heads,
     uint32_t head_dim_qk, uint32_t head_dim_v, uint32_t block_size, float scale,
     uint32_t sliding_window, const float* sinks, int q_rope, float q_rope_theta,
@@ -1538,7 +1573,8 @@ extern "C" int pkv_paged_decode_attn_noalloc(
     uint32_t split_tokens, void* stream)
 {
     return pkv::paged_decode(q, q_dtype, q_seq_stride, k_cache, k_dtype, k_scale, v_cache,
-                             v_dtype, v_scale, block_tables, max_blocks_per_seq, seq_lens,
+                             v_dtype, v_scale, sparse_v_threshold, block_tables,
+                             max_blocks_per_seq, seq_lens,
                              num_seqs, num_blocks, num_q_heads, num_kv_heads, head_dim_qk,
                              head_dim_v, block_size, scale, sliding_window, sinks, q_rope,
                              q_rope_theta, q_rope_offset, q_rope_dim, gate, out, split_tokens,

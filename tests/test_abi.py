@@ -67,8 +67,8 @@ def test_zero_work_returns_ok_without_pointers(lib):
     assert lib.pkv_cache_write_v(None, 0, 0, None, 0, 8, 128, 16, 1, None, 0, 1.0, None) == 0
     assert lib.pkv_cache_write_k_fused(None, 0, 0, None, 1e-6, None, None, None, 1e4, 0, 128, 0,
                                        None, 0, 8, 128, 16, 1, None, 0, 1.0, None) == 0
-    assert lib.pkv_paged_decode_attn(None, 0, 0, None, 0, 1.0, None, 0, 1.0, None, 1, None, 0,
-                                     1, 8, 8, 128, 128, 16, 0.1, 0, None, 0, 1e4, 0, 0, None,
+    assert lib.pkv_paged_decode_attn(None, 0, 0, None, 0, 1.0, None, 0, 1.0, 0.0, None, 1, None,
+                                     0, 1, 8, 8, 128, 128, 16, 0.1, 0, None, 0, 1e4, 0, 0, None,
                                      None, 0, None, 0, None) == 0
     assert _err(lib) == ""
 
@@ -116,10 +116,10 @@ def test_bad_dtypes_and_shapes(lib):
 
 def test_decode_validation(lib):
     def call(**kw):
-        a = dict(q=FAKE, qd=0, qs=32 * 128, k=FAKE, kd=0, ks=1.0, v=FAKE, vd=0, vs=1.0, bt=FAKE,
-                 M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1, win=0,
-                 sinks=None, qr=0, qt=1e4, qo=0, qdim=0, gate=None, out=FAKE, split=0, ws=FAKE,
-                 wsb=1 << 30)
+        a = dict(q=FAKE, qd=0, qs=32 * 128, k=FAKE, kd=0, ks=1.0, v=FAKE, vd=0, vs=1.0, spv=0.0,
+                 bt=FAKE, M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1,
+                 win=0, sinks=None, qr=0, qt=1e4, qo=0, qdim=0, gate=None, out=FAKE, split=0,
+                 ws=FAKE, wsb=1 << 30)
         a.update(kw)
         return lib.pkv_paged_decode_attn(*a.values(), None)
     assert call(Hq=30) == -1                      # Hq % Hkv
@@ -128,6 +128,12 @@ def test_decode_validation(lib):
     assert call(kd=1, ks=0.0) == -1               # FP8 K needs a scale
     assert call(vd=1, vs=-1.0) == -1              # FP8 V needs a scale
     assert call(vd=2) == -2                       # (BF16, BF16, FP32) not a supported set
+    for bad in (-0.1, 1.0, float("nan"), float("inf")):
+        assert call(vd=pkv.TQ3, spv=bad) == -1    # sparse-V threshold in [0, 1)
+    assert "sparse_v_threshold" in _err(lib)
+    assert call(spv=0.01) == -2                   # the sparse-V skip is for TQ V only
+    assert call(vd=1, spv=0.01) == -2
+    assert "TQ" in _err(lib)
     assert call(Dqk=192, qs=32 * 192) == -2       # BF16 caches need Dqk == Dv
     assert call(qr=1, qdim=64) == -2              # query rotation: FP32 path only
     assert call(M=512, wsb=16) == -3              # workspace too small
@@ -150,9 +156,9 @@ def test_decode_noalloc_validation(lib):
     workspace entry point rejects, and a plan whose split partials exceed
     the library's static scratch."""
     def call(**kw):
-        a = dict(q=FAKE, qd=0, qs=32 * 128, k=FAKE, kd=0, ks=1.0, v=FAKE, vd=0, vs=1.0, bt=FAKE,
-                 M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1, win=0,
-                 sinks=None, qr=0, qt=1e4, qo=0, qdim=0, gate=None, out=FAKE, split=0)
+        a = dict(q=FAKE, qd=0, qs=32 * 128, k=FAKE, kd=0, ks=1.0, v=FAKE, vd=0, vs=1.0, spv=0.0,
+                 bt=FAKE, M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1,
+                 win=0, sinks=None, qr=0, qt=1e4, qo=0, qdim=0, gate=None, out=FAKE, split=0)
         a.update(kw)
         return lib.pkv_paged_decode_attn_noalloc(*a.values(), None)
     assert call(S=0) == 0                         # no work: nothing launched
@@ -262,13 +268,15 @@ def test_tq_validation(lib):
 
     def dec(**kw):
         a = dict(q=FAKE, qd=0, qs=32 * 128, k=FAKE, kd=0, ks=1.0, v=FAKE, vd=pkv.TQ3, vs=1.0,
-                 bt=FAKE, M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1,
+                 spv=0.0, bt=FAKE, M=4, sl=FAKE, S=2, nb=8, Hq=32, Hkv=8, Dqk=128, Dv=128, B=16, scale=0.1,
                  win=0, sinks=None, qr=0, qt=1e4, qo=0, qdim=0, gate=None, out=FAKE, split=0,
                  ws=FAKE, wsb=1 << 30)
         a.update(kw)
         return lib.pkv_paged_decode_attn(*a.values(), None)
     assert dec(Dqk=64, Dv=64, qs=32 * 64) == -2   # TQ V decode: head dim 128 only
     assert dec(qd=2, kd=2) == -2                  # FP32 q/K with TQ V
+    assert dec(Dqk=64, Dv=64, qs=32 * 64, spv=0.01) == -2
+    assert dec(spv=1.5) == -1
     pre = lib.pkv_paged_prefill_attn(FAKE, 0, 32 * 128, FAKE, 8, 64, FAKE, 0, 1.0, FAKE, pkv.TQ3,
                                      1.0, FAKE, 4, FAKE, 2, 8, 32, 8, 128, 128, 16, 0.1, 0, None,
                                      FAKE, None)
