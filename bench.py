@@ -24,7 +24,9 @@ MRoPE; the one-sequence gated MLA-style FP32 decode, RoPE and NoPE), each call
 timed after a scratch write that flushes the last-level cache.
 ``decode_bf16k_tq3v_256seq`` is the first workload with its V
 cache in the 3-bit TurboQuant-style format (3-bit codes plus one E4M3 scale
-per 16 elements: 0.4375 bytes per element).  ``prefill_bf16_256seq_chunk256`` is chunked prefill on the first
+per 16 elements: 0.4375 bytes per element); ``..._sparse_v`` is the same
+with peaked attention (one heavy key every 64 positions, see SPARSE_V) and
+the sparse-V skip at threshold 1e-3.  ``prefill_bf16_256seq_chunk256`` is chunked prefill on the first
 workload's pool: the last min(256, n) tokens of every sequence are the new
 chunk (slots, K write, V write, then causal prefill attention over the whole
 cache); its metric is the attention's algorithmic TFLOP/s and its roofline
@@ -58,7 +60,15 @@ WORKLOADS = {
     "decode_fp8kv_64seq_long": (3, "fp8", 0, False),
     "decode_fp8k_64seq_long_window4096_sinks": (3, "bf16", 4096, True),
     "decode_bf16k_tq3v_256seq": (2, "tq3", 0, False),
+    "decode_bf16k_tq3v_256seq_sparse_v": (2, "tq3", 0, False),
 }
+# sparse-V workloads: name -> (threshold, heavy-position stride, heavy key
+# length).  The history's key at every stride-th position (0, stride, ...)
+# is replaced by heavy_len times the unit vector of the sum of its GQA
+# group's queries, so that a few positions hold nearly all of the softmax
+# mass (scores ~13-21 above the N(0, 1) bulk); the decode runs with the
+# sparse-V skip at the threshold.
+SPARSE_V = {"decode_bf16k_tq3v_256seq_sparse_v": (1e-3, 64, 40.0)}
 
 
 def v_elem_bytes(v_kind):
@@ -289,6 +299,11 @@ def run_decode(name, args):
     k_new = W.device_normal(idx, W.S_KNEW, (S, Hkv, D), torch.bfloat16, dev, outliers=fp8)
     v_new = W.device_normal(idx, W.S_VNEW, (S, Hkv, Dv), torch.bfloat16, dev)
     q = W.device_normal(idx, W.S_Q, (S, Hq, D), torch.bfloat16, dev, outliers=fp8)
+    spv_tau = 0.0
+    if name in SPARSE_V:
+        spv_tau, stride, heavy_len = SPARSE_V[name]
+        n_heavy = heavy_keys(k_pool, q, lay, stride, heavy_len)
+        log(f"sparse V: threshold {spv_tau:g}, {n_heavy} heavy keys (every {stride} positions)")
     start_d, cu_d, pos_d = W.positions_decode(lay)
     start_d_t = torch.from_numpy(start_d).to(dev)
     cu_d_t = torch.from_numpy(cu_d.astype(np.int32)).to(dev)
@@ -309,7 +324,8 @@ def run_decode(name, args):
     def step_attn():
         pkv.paged_decode_attn(q, k_pool, v_pool, bt, seq_lens, scale=scale, k_scale=k_scale,
                               v_scale=v_scale, sliding_window=window, sinks=sinks, out=out,
-                              split_tokens=args.split_tokens, workspace=ws, v_tq_bits=tq)
+                              split_tokens=args.split_tokens, workspace=ws, v_tq_bits=tq,
+                              sparse_v_threshold=spv_tau)
 
     def step():
         step_writes()
@@ -401,10 +417,37 @@ def run_decode(name, args):
                      "traffic": traffic, "kernel": "paged_decode_attn (split-K + merge)"},
         "cpu_baseline": None,
     }
+    if name in SPARSE_V:
+        result["config"].update(sparse_v_threshold=spv_tau, heavy_key_stride=stride,
+                                heavy_key_length=heavy_len)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(idx, lay, k_scale, v_kind, v_scale, window,
-                                              None if sinks is None else sinks.cpu().numpy())
+                                              None if sinks is None else sinks.cpu().numpy(),
+                                              sparse_v=SPARSE_V.get(name))
     return result
+
+
+def heavy_keys(k_pool, q, lay, stride, heavy_len):
+    """Writes the heavy keys of a sparse-V workload into a BF16 K pool
+    [nb, 16, Hkv, D]: at history positions 0, stride, 2 stride, ... of every
+    sequence, for every kv head, heavy_len times the unit vector of the sum
+    of the head's GQA group of queries q [S, Hq, D].  Returns their count."""
+    import torch
+    S, Hq, D = q.shape
+    Hkv = k_pool.shape[2]
+    u = q.float().view(S, Hkv, Hq // Hkv, D).sum(2)
+    u = u / u.norm(dim=-1, keepdim=True)
+    seq, pos = [], []
+    for s in range(S):
+        t = np.arange(0, int(lay.seq_lens[s]) - 1, stride)
+        seq.append(np.full(t.size, s))
+        pos.append(t)
+    seq, pos = np.concatenate(seq), np.concatenate(pos)
+    blk = lay.block_tables[seq, pos // 16]
+    dev = k_pool.device
+    k_pool[torch.from_numpy(blk).to(dev).long(), torch.from_numpy(pos % 16).to(dev).long()] = \
+        (heavy_len * u[torch.from_numpy(seq).to(dev).long()]).to(k_pool.dtype)
+    return int(seq.size)
 
 
 def history_k_scale(k_hist, pos, w, cfg, B=16):
@@ -781,7 +824,8 @@ def oracle_timing(run, nbytes, sample, unit_scale=1e9, unit="GB/s"):
                                              f"{cores}"}
 
 
-def cpu_baseline(idx, lay, k_scale, v_kind="bf16", v_scale=1.0, window=0, sinks=None):
+def cpu_baseline(idx, lay, k_scale, v_kind="bf16", v_scale=1.0, window=0, sinks=None,
+                 sparse_v=None):
     """The oracle, as it stands, timed on this host on a bounded sample of the
     decode step: the first sequences of the workload (in its order) up to
     CPU_SAMPLE_TOKENS tokens -- slots, K write and V write of their new
@@ -789,7 +833,9 @@ def cpu_baseline(idx, lay, k_scale, v_kind="bf16", v_scale=1.0, window=0, sinks=
     all the threads this process may use (at most 16, the CPU share of one
     GPU on the benchmark hosts), median of 3 runs each.  The sampled
     sequences' blocks are drawn by the seeded generator on the device and
-    copied to the host; nothing in them comes from the HIP path."""
+    copied to the host; nothing in them comes from the HIP path.  With
+    sparse_v = (threshold, stride, heavy length) the sample gets the heavy
+    keys of the sparse-V workload and the oracle's sparse-V decode runs."""
     import torch
 
     import oracle
@@ -846,6 +892,25 @@ def cpu_baseline(idx, lay, k_scale, v_kind="bf16", v_scale=1.0, window=0, sinks=
     sub = W.Layout(idx, lens, bt, nb, -1, 16, cfg)
     start, cu, pos = W.positions_decode(sub)
 
+    if sparse_v is not None:
+        _, stride, heavy_len = sparse_v
+        G = Hq // Hkv
+        u = oracle.to_f64(q, "bf16").reshape(S, Hkv, G, D).sum(2)
+        u /= np.linalg.norm(u, axis=-1, keepdims=True)
+        for s in range(S):
+            for t in range(0, int(lens[s]) - 1, stride):
+                kp[bt[s, t // 16], t % 16] = W.bf16_bits((heavy_len * u[s]).astype(np.float32))
+
+    def decode(threads):
+        kw = dict(num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=Dv, block_size=16,
+                  scale=D ** -0.5, k_scale=k_scale, v_scale=v_scale, sliding_window=window,
+                  sinks=sinks, nthreads=threads)
+        if sparse_v is not None:
+            oracle.paged_decode_sparse_v(q, "bf16", kp, cfg["k_cache_dtype"], vp, v_kind, bt,
+                                         lens, tau=sparse_v[0], **kw)
+        else:
+            oracle.paged_decode(q, "bf16", kp, cfg["k_cache_dtype"], vp, v_kind, bt, lens, **kw)
+
     def run(threads):
         t0 = time.perf_counter()
         slots = oracle.fill_slots(bt, start, cu, S, 16)
@@ -854,18 +919,16 @@ def cpu_baseline(idx, lay, k_scale, v_kind="bf16", v_scale=1.0, window=0, sinks=
                              theta=cfg["theta"], k_scale=k_scale, nthreads=threads)
         oracle.cache_write_v(v_new, "bf16", slots, vp, num_kv_heads=Hkv, head_dim_v=Dv,
                              block_size=16, cache_dtype=v_kind, v_scale=v_scale)
-        oracle.paged_decode(q, "bf16", kp, cfg["k_cache_dtype"], vp, v_kind, bt, lens,
-                            num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=Dv,
-                            block_size=16, scale=D ** -0.5, k_scale=k_scale, v_scale=v_scale,
-                            sliding_window=window, sinks=sinks, nthreads=threads)
+        decode(threads)
         return time.perf_counter() - t0
 
     b = (decode_bytes(lens, Hq, Hkv, D, Dv, 1 if fp8 else 2, vb, 2, window=window,
                       sinks=sinks is not None)
          + kwrite_bytes(S, Hkv, D, 2, 1 if fp8 else 2)
          + vwrite_bytes(S, Hkv, Dv, 2, vb) + slots_bytes(S, S))
+    what = "sparse-V attention" if sparse_v is not None else "attention"
     return oracle_timing(run, b, f"decode step (slots, K and V write of the new token, "
-                                 f"attention over the whole history) of the first {S} of "
+                                 f"{what} over the whole history) of the first {S} of "
                                  f"{lay.num_seqs} sequences, {int(lens.sum())} tokens")
 
 

@@ -12,7 +12,9 @@ with the automatic split plan.  Checked against the oracle:
     step); V rows of the same tokens bit-exact (copy, E4M3 or TQ bytes);
   * the attention output of sampled sequences (the shortest, the longest and
     random ones), recomputed by the oracle over the blocks those sequences
-    own (gathered from the device pools): <= 2e-3 row-relative.
+    own (gathered from the device pools): <= 2e-3 row-relative; with the
+    sparse-V skip (heavy keys written into the pool, as the bench does),
+    within the oracle's bound of its sparse-V output plus 2e-3.
 The prefill workload is checked the same way on sampled sequences.
 """
 import numpy as np
@@ -152,6 +154,11 @@ def test_full_size_decode_step_sampled(name):
     k_new = W.device_normal(idx, W.S_KNEW, (S, Hkv, D), torch.bfloat16, dev, outliers=fp8)
     v_new = W.device_normal(idx, W.S_VNEW, (S, Hkv, D), torch.bfloat16, dev)
     q = W.device_normal(idx, W.S_Q, (S, Hq, D), torch.bfloat16, dev, outliers=fp8)
+    tau, stride = 0.0, 0
+    if name in bench.SPARSE_V:
+        tau, stride, heavy_len = bench.SPARSE_V[name]
+        n_heavy = bench.heavy_keys(k_pool, q, lay, stride, heavy_len)
+        say(f"  sparse V: threshold {tau:g}, {n_heavy} heavy keys")
     start_d, cu_d, pos_d = W.positions_decode(lay)
     slots_d = torch.empty(S, dtype=torch.int64, device=dev)
     pkv.fill_slots(slots_d, bt, _i32(start_d), _i32(cu_d), B)
@@ -165,7 +172,7 @@ def test_full_size_decode_step_sampled(name):
     out = pkv.paged_decode_attn(q, k_pool, v_pool, bt, seq_lens, scale=D ** -0.5,
                                 k_scale=k_scale, v_scale=v_scale, sliding_window=window,
                                 sinks=None if sinks is None else torch.from_numpy(sinks).to(dev),
-                                workspace=ws, v_tq_bits=tq)
+                                workspace=ws, v_tq_bits=tq, sparse_v_threshold=tau)
     torch.cuda.synchronize()
 
     # slots of the step: all of them
@@ -177,6 +184,8 @@ def test_full_size_decode_step_sampled(name):
     # saturate)
     rng = np.random.default_rng(idx)
     hist_tok = np.sort(rng.choice(Th, size=96, replace=False))
+    if stride:                                  # heavy keys were written over the K write's
+        hist_tok = hist_tok[pos_h[hist_tok] % stride != 0]
     seqs = _sample_seqs(lens, 4, 100 + idx)
     tok_idx = torch.from_numpy(hist_tok).to(dev)
     h_slots = host(slots_h)[hist_tok]
@@ -195,12 +204,22 @@ def test_full_size_decode_step_sampled(name):
     # attention output of sampled sequences
     kp, vp, bt_sub = _sub_pool(lay, seqs, k_pool, v_pool)
     qs = _bits(q)[seqs]
-    ref = oracle.paged_decode(qs, "bf16", kp, k_dt, vp, v_kind, bt_sub, lay.seq_lens[seqs],
-                              num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=D,
-                              block_size=B, scale=D ** -0.5, k_scale=k_scale, v_scale=v_scale,
-                              sliding_window=window, sinks=sinks, nthreads=8)
+    kw = dict(num_q_heads=Hq, num_kv_heads=Hkv, head_dim_qk=D, head_dim_v=D, block_size=B,
+              scale=D ** -0.5, k_scale=k_scale, v_scale=v_scale, sliding_window=window,
+              sinks=sinks, nthreads=8)
+    ref = oracle.paged_decode(qs, "bf16", kp, k_dt, vp, v_kind, bt_sub, lay.seq_lens[seqs], **kw)
     got = host(out)[seqs]
-    err = attn_err(got, ref)
+    if tau:
+        # the skip leaves out a subset of the positions whose softmax weight
+        # is at most tau: within the oracle's bound of its sparse output
+        sp, bound = oracle.paged_decode_sparse_v(qs, "bf16", kp, k_dt, vp, v_kind, bt_sub,
+                                                 lay.seq_lens[seqs], tau=tau, **kw)
+        den = np.abs(ref).max(axis=-1, keepdims=True)
+        err = float(((np.abs(got - sp) - bound) / np.where(den > 0, den, 1.0)).max())
+        say(f"  sequences {seqs}: excess over the sparse-V bound {err:.3e}, "
+            f"exact vs sparse {attn_err(ref, sp):.3e}")
+    else:
+        err = attn_err(got, ref)
     say(f"  sequences {seqs} (lengths {lens[seqs].tolist()}): err {err:.3e}")
     assert np.isfinite(got).all() and err <= ATTN_TOL
 
