@@ -34,6 +34,7 @@
 // FP32 caches (VALU path).  Four tokens per wave step (16 lanes per token
 // row, 16-byte loads), one online-softmax stream per row, merged at the end.
 #include <mutex>
+#include <type_traits>
 
 #include "attn_common.h"
 
@@ -483,19 +484,24 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
 
     // An unmapped block is read from block 0 instead (always inside the pool):
     // compute_block masks all of its tokens, so what it holds never counts.
-    auto load_block = [&](uint32_t bi, Stage& st) {
+    // do_k / do_v (std::true_type or std::false_type) select the K and V loads.
+    auto load_parts = [&](uint32_t bi, Stage& st, auto do_k, auto do_v) {
         int32_t pb = table_entry(bi - b0);
         pb = (pb >= 0 && (uint32_t)pb < a.num_blocks) ? pb : 0;
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(kbase + (uint64_t)pb * kblk_bytes), 0, (int)kblk_bytes, kBufferFlags);
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(vbase + (uint64_t)pb * vblk_bytes), 0, (int)vblk_bytes, kBufferFlags);
+        if constexpr (decltype(do_k)::value) {
 #pragma unroll
-        for (int j = 0; j < NL; ++j) {                                    // K: token t = ln
-            const u32x4 w = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff, j * kstep, kNT));
-            st.k[j] = w;
+            for (int j = 0; j < NL; ++j) {                                // K: token t = ln
+                const u32x4 w = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, koff, j * kstep, kNT));
+                st.k[j] = w;
+            }
         }
+        if constexpr (!decltype(do_v)::value)
+            return;
         if constexpr (TQ) {                                               // scales of 16 tokens
             const u32x4 s4 = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, tq_soff, 0, kNT));
@@ -529,8 +535,17 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
             }
         }
     };
+    auto load_block = [&](uint32_t bi, Stage& st) {
+        load_parts(bi, st, std::true_type{}, std::true_type{});
+    };
 
-    auto compute_block = [&](uint32_t bi, Stage& st) {
+    // Scores of block bi from its K rows in st: the softmax weights p of the
+    // lane's tokens relative to the new running maximum (FP16 PV paths: times
+    // 2^15; tokens that do not count: 0) and the factor alpha that takes
+    // values relative to the old maximum to the new one; m and l are
+    // updated.  [tlo, ntok) are the block's tokens that count.
+    auto score_block = [&](uint32_t bi, Stage& st, float (&p)[4], float& alpha, int& ntok_out,
+                           int& tlo_out) {
         const int32_t pb = table_entry(bi - b0);
         const bool blk_ok = pb >= 0 && (uint32_t)pb < a.num_blocks;
         const int32_t rem = n - (int32_t)(bi * kBS);
@@ -585,7 +600,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         // while no token has counted yet (m_new = -inf) use 0 as the reference:
         // masked scores give p = 0, and alpha = 0 leaves the zero state zero
         const float m_ref = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m - m_ref);
+        alpha = __builtin_amdgcn_exp2f(m - m_ref);
         // TQ and E4M3 V: the weights go to the PV product as FP16 scaled by
         // 2^15 (kept clear of FP16 subnormals; p <= 1); the normalisation
         // divides it out
@@ -594,7 +609,6 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         // the exponent is the difference of the rounded scaled score and the
         // reference, never an FMA of the raw score: with kPOff = 0 the row's
         // largest score gives exactly 1 (one attended token returns its V row)
-        float p[4];
         {
 #pragma clang fp contract(off)
 #pragma unroll
@@ -604,6 +618,11 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         const float psum = (p[0] + p[1]) + (p[2] + p[3]);
         l = F16PV ? __builtin_fmaf(psum, 1.f / 32768.f, l * alpha) : l * alpha + psum;
         m = m_new;
+        ntok_out = ntok;
+        tlo_out = tlo;
+    };
+    // O rows are g = 4kg + r; their factor lives in lane g
+    auto rescale_o = [&](float alpha) {
         if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
             // O rows are g = 4kg + r; their factor lives in lane g
 #pragma unroll
@@ -614,8 +633,9 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
                     o[nt][r] *= ar;
             }
         }
-
-        // masked tokens must not bring NaN/Inf into 0 * V
+    };
+    // masked tokens must not bring NaN/Inf into 0 * V
+    auto mask_v = [&](Stage& st, int ntok, int tlo) {
         if (ntok < kBS || tlo > 0) {
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -624,27 +644,15 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
                     for (int w = 0; w < VW; ++w)
                         st.v[r][w] = 0u;
         }
+    };
+
+    auto compute_block = [&](uint32_t bi, Stage& st) {
+        float p[4], alpha;
+        int ntok, tlo;
+        score_block(bi, st, p, alpha, ntok, tlo);
+        rescale_o(alpha);
+        mask_v(st, ntok, tlo);
         if constexpr (TQ) {
-            if constexpr (SPV) {
-                // Sparse-V skip (page 2, paged_decode_attn_fp8k_turbo3v): a
-                // position whose weight is at most the threshold leaves the
-                // PV product; its weight stays in l.  The weight at hand is
-                // p / 2^15 = exp(s - running max), which is at least the
-                // final softmax weight, so every position left out has a
-                // weight at most the threshold.  Rows past the GQA group
-                // never count.  A block with no position kept in any row
-                // skips the V decode and the PV MFMAs; its V words were
-                // loaded a block ahead, before its weights existed.
-                bool keep_any = false;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const bool keep = p[r] > a.spv_thr;
-                    p[r] = keep ? p[r] : 0.f;
-                    keep_any |= keep && (uint32_t)ln < a.G;
-                }
-                if (!__builtin_amdgcn_ballot_w64(keep_any))
-                    return;
-            }
             tq_pv<VT>(a, p, st.v, tq_shift, tq_ssel, o);
             return;
         } else if constexpr (VT == 1) {
@@ -682,6 +690,69 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         }
     };
 
+    if constexpr (SPV) {
+        // Sparse-V skip (page 2, paged_decode_attn_fp8k_turbo3v: the V load
+        // and dequantisation of a position are skipped when its attention
+        // weight is at most the threshold).  The weight at hand when block b
+        // is scored is p / 2^15 = exp(s - running max), at least the final
+        // softmax weight, so every position left out has a weight at most the
+        // threshold; its weight stays in l, and rows past the GQA group never
+        // count.  V of block b is loaded only when some position is kept,
+        // right after the block's scores; its PV product waits two blocks, so
+        // that the load has a block of work to arrive under, and its weights
+        // are rescaled to the running maximum meanwhile.  K is loaded a block
+        // ahead as on the exact path.  Block b's K and V live in stage
+        // (b - b0) % 2 and its pending weights in pw[(b - b0) % 2].
+        static_assert(PF == 1, "the sparse-V loop keeps one block of K prefetch");
+        Stage st[2];
+        float pw[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        bool keep[2] = {false, false};             // wave-uniform
+        int pn[2] = {0, 0}, pt[2] = {0, 0};        // [tlo, ntok) of the pending blocks
+        auto pv_pending = [&](int u) {
+            if (keep[u]) {
+                mask_v(st[u], pn[u], pt[u]);
+                tq_pv<VT>(a, pw[u], st[u].v, tq_shift, tq_ssel, o);
+            }
+        };
+        auto step = [&](uint32_t b, int u, bool prefetch) {
+            if (prefetch)
+                load_parts(b + 1, st[u ^ 1], std::true_type{}, std::false_type{});
+            float p[4], alpha;
+            int ntok, tlo;
+            score_block(b, st[u], p, alpha, ntok, tlo);
+            pv_pending(u);                          // block b - 2, at the old maximum
+            rescale_o(alpha);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pw[u ^ 1][r] *= alpha;              // block b - 1 to the new maximum
+            bool kept = false;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool k = p[r] > a.spv_thr;
+                pw[u][r] = k ? p[r] : 0.f;
+                kept |= k && (uint32_t)ln < a.G;
+            }
+            keep[u] = __builtin_amdgcn_ballot_w64(kept) != 0;
+            pn[u] = ntok;
+            pt[u] = tlo;
+            if (keep[u])
+                load_parts(b, st[u], std::false_type{}, std::true_type{});
+        };
+        load_parts(b0, st[0], std::true_type{}, std::false_type{});
+        uint32_t bi = b0;
+        for (; bi + 2 < b1; bi += 2) {
+            step(bi, 0, true);
+            step(bi + 1, 1, true);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            if (bi + u >= b1)
+                break;
+            step(bi + u, u, bi + u + 1 < b1);
+        }
+        pv_pending(0);
+        pv_pending(1);
+    } else {
     // Ring of PF + 1 register stages; block b lives in stage (b - b0) % NS.
     // The main loop prefetches unconditionally (every block it handles has a
     // block PF ahead), so the compiler's wait before each compute covers only
@@ -708,6 +779,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         if (b + PF < b1)
             load_block(b + PF, st[(u + PF) % NS]);
         compute_block(b, st[u % NS]);
+    }
     }
 
     l = row_sum_xor16_32(l);

@@ -159,7 +159,9 @@ def test_random_scores_within_the_bound(split):
 
 def test_tiny_threshold_equals_the_exact_decode():
     """A threshold below every weight runs the skipping kernels and leaves
-    nothing out: the same output as the exact call, bit for bit."""
+    nothing out: the exact call's output up to rounding (the skipping kernels
+    rescale a pending block's weights instead of the accumulator, so their
+    FP16 weights round differently: 1e-5 row-relative)."""
     lay = W.layout_for(2, [0, 1, 17, 300, 999])
     Hkv, G, bits = 2, 4, 3
     q, kp, vp = _peaked(lay, Hkv, G, bits, "fp8", 80, lambda s, n: list(range(0, n, 16)))
@@ -170,7 +172,9 @@ def test_tiny_threshold_equals_the_exact_decode():
                                        split_tokens=split))
         b = host(pkv.paged_decode_attn(*args, scale=D ** -0.5, k_scale=0.5, v_tq_bits=bits,
                                        split_tokens=split, sparse_v_threshold=1e-30))
-        assert np.array_equal(a, b)
+        err = attn_err(b, a)
+        say(f"  split {split}: {err:.3e} from the exact call")
+        assert np.isfinite(b).all() and err <= 1e-5
 
 
 def test_noalloc_call_matches():
