@@ -44,6 +44,10 @@ namespace pkv {
 // Launch shape of the MFMA path.
 constexpr uint32_t kKvPerGroup = 2;     // kv heads (waves) per work-group, at most
 constexpr int kPrefetch = 1;            // cache blocks loaded ahead of the one in use
+// Sparse-V loop: K blocks loaded ahead.  On the 256-sequence 3-bit TQ V
+// workload with one heavy key every 64 positions, 1, 2 and 3 blocks gave the
+// same call time (0.445-0.449 ms).
+constexpr int kPrefetchSpv = 1;
 constexpr bool kKDirect = false;        // K loaded straight into the operand layout
 constexpr uint64_t kTargetGroups = 768; // (sequence, split, kv group) work-groups wanted
 // FP32 path: (sequence, kv head, split) waves wanted -- about one per CU.
@@ -484,14 +488,16 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
 
     // An unmapped block is read from block 0 instead (always inside the pool):
     // compute_block masks all of its tokens, so what it holds never counts.
-    // do_k / do_v (std::true_type or std::false_type) select the K and V loads.
-    auto load_parts = [&](uint32_t bi, Stage& st, auto do_k, auto do_v) {
+    // do_k / do_v (std::true_type or std::false_type) select the K and V
+    // loads; vrec is the record count of the block's V resource (0: the V
+    // loads return zeros and move no data).
+    auto load_parts = [&](uint32_t bi, Stage& st, auto do_k, auto do_v, uint32_t vrec) {
         int32_t pb = table_entry(bi - b0);
         pb = (pb >= 0 && (uint32_t)pb < a.num_blocks) ? pb : 0;
         const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
             (void*)(kbase + (uint64_t)pb * kblk_bytes), 0, (int)kblk_bytes, kBufferFlags);
         const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(vbase + (uint64_t)pb * vblk_bytes), 0, (int)vblk_bytes, kBufferFlags);
+            (void*)(vbase + (uint64_t)pb * vblk_bytes), 0, (int)vrec, kBufferFlags);
         if constexpr (decltype(do_k)::value) {
 #pragma unroll
             for (int j = 0; j < NL; ++j) {                                // K: token t = ln
@@ -536,7 +542,7 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         }
     };
     auto load_block = [&](uint32_t bi, Stage& st) {
-        load_parts(bi, st, std::true_type{}, std::true_type{});
+        load_parts(bi, st, std::true_type{}, std::true_type{}, vblk_bytes);
     };
 
     // Scores of block bi from its K rows in st: the softmax weights p of the
@@ -700,55 +706,75 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         // count.  V of block b is loaded only when some position is kept,
         // right after the block's scores; its PV product waits two blocks, so
         // that the load has a block of work to arrive under, and its weights
-        // are rescaled to the running maximum meanwhile.  K is loaded a block
-        // ahead as on the exact path.  Block b's K and V live in stage
-        // (b - b0) % 2 and its pending weights in pw[(b - b0) % 2].
-        static_assert(PF == 1, "the sparse-V loop keeps one block of K prefetch");
-        Stage st[2];
+        // are rescaled to the running maximum meanwhile.  K is loaded
+        // kPrefetchSpv blocks ahead.  Block b's K lives in kst[(b - b0) % KS],
+        // its V in vst[(b - b0) % 2] and its pending weights in
+        // pw[(b - b0) % 2].
+        constexpr int KPF = kPrefetchSpv;          // K blocks loaded ahead
+        constexpr int KS = KPF + 1;                 // K stages
+        constexpr int P = KS % 2 ? 2 * KS : KS;     // unroll period: K stages and V parity
+        Stage kst[KS], vst[2];                      // K in kst[].k, V in vst[].v
         float pw[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         bool keep[2] = {false, false};             // wave-uniform
         int pn[2] = {0, 0}, pt[2] = {0, 0};        // [tlo, ntok) of the pending blocks
-        auto pv_pending = [&](int u) {
-            if (keep[u]) {
-                mask_v(st[u], pn[u], pt[u]);
-                tq_pv<VT>(a, pw[u], st[u].v, tq_shift, tq_ssel, o);
+        auto pv_pending = [&](int v) {
+            if (keep[v]) {
+                mask_v(vst[v], pn[v], pt[v]);
+                tq_pv<VT>(a, pw[v], vst[v].v, tq_shift, tq_ssel, o);
             }
         };
+        // block b = b0 + (multiple of P) + u
         auto step = [&](uint32_t b, int u, bool prefetch) {
             if (prefetch)
-                load_parts(b + 1, st[u ^ 1], std::true_type{}, std::false_type{});
+                load_parts(b + KPF, kst[(u + KPF) % KS], std::true_type{}, std::false_type{}, 0u);
             float p[4], alpha;
             int ntok, tlo;
-            score_block(b, st[u], p, alpha, ntok, tlo);
-            pv_pending(u);                          // block b - 2, at the old maximum
+            score_block(b, kst[u % KS], p, alpha, ntok, tlo);
+            const int v = u % 2;
+            pv_pending(v);                          // block b - 2, at the old maximum
             rescale_o(alpha);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                pw[u ^ 1][r] *= alpha;              // block b - 1 to the new maximum
+                pw[v ^ 1][r] *= alpha;              // block b - 1 to the new maximum
             bool kept = false;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const bool k = p[r] > a.spv_thr;
-                pw[u][r] = k ? p[r] : 0.f;
+                pw[v][r] = k ? p[r] : 0.f;
                 kept |= k && (uint32_t)ln < a.G;
             }
-            keep[u] = __builtin_amdgcn_ballot_w64(kept) != 0;
-            pn[u] = ntok;
-            pt[u] = tlo;
-            if (keep[u])
-                load_parts(b, st[u], std::false_type{}, std::true_type{});
+            keep[v] = __builtin_amdgcn_ballot_w64(kept) != 0;
+            pn[v] = ntok;
+            pt[v] = tlo;
+            // issued whether or not the block is kept (a skipped block's
+            // resource holds no records, so its loads move no data): the
+            // count of loads in flight stays fixed, which keeps the
+            // compiler's waits to the loads each use needs
+            load_parts(b, vst[v], std::false_type{}, std::true_type{}, keep[v] ? vblk_bytes : 0u);
         };
-        load_parts(b0, st[0], std::true_type{}, std::false_type{});
-        uint32_t bi = b0;
-        for (; bi + 2 < b1; bi += 2) {
-            step(bi, 0, true);
-            step(bi + 1, 1, true);
-        }
+        // The first two steps run ahead of the loop, so that the loop is
+        // entered with the loads in flight in the order of its back edge
+        // (K of the next block behind V of the last one): the compiler's
+        // waits, which must hold on both paths, then wait only for the loads
+        // each use needs.
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            if (bi + u >= b1)
-                break;
-            step(bi + u, u, bi + u + 1 < b1);
+        for (int f = 0; f < KPF; ++f)
+            load_parts(b0 + f < b1 ? b0 + f : b1 - 1, kst[f], std::true_type{}, std::false_type{}, 0u);
+        step(b0, 0, b0 + KPF < b1);
+        if (b0 + 1 < b1) {
+            step(b0 + 1, 1, b0 + 1 + KPF < b1);
+            uint32_t bi = b0 + 2;
+            for (; bi + P + KPF - 1 < b1; bi += P) {
+#pragma unroll
+                for (int u = 0; u < P; ++u)
+                    step(bi + u, u, true);
+            }
+#pragma unroll
+            for (int u = 0; u < P + KPF - 1; ++u) {
+                if (bi + u >= b1)
+                    break;
+                step(bi + u, u, bi + u + KPF < b1);
+            }
         }
         pv_pending(0);
         pv_pending(1);
