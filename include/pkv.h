@@ -284,20 +284,20 @@ size_t pkv_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
  *                     paged_decode_attn_fp8k_turbo3v: a position's V is not
  *                     loaded or dequantised when its attention weight is at
  *                     most a threshold whose value the pages do not give;
- *                     [p1] calls its Turbo-V decodes "sparse V").  0 = exact
- *                     decode; in (0, 1): a position whose weight relative to
- *                     the largest score seen so far in its split-K piece,
- *                     exp(s_t - running max), is at most the threshold leaves
- *                     the sum over V (it stays in Z).  That weight is at least
- *                     the softmax weight exp(s_t) / Z, so the positions left
- *                     out are a subset of those whose weight is at most the
- *                     threshold; which ones depends on the order and the
- *                     split-K pieces in which positions are visited.  A
- *                     16-token block none of whose positions is kept for any
- *                     query head of the GQA group skips the V decode and the
- *                     PV product (its V bytes are still read).  Outside
- *                     [0, 1) (or NaN): PKV_ERR_INVALID; > 0 with a non-TQ V
- *                     cache: PKV_ERR_UNSUPPORTED
+ *                     [p1] describes its Turbo-V decodes as sparse in V).
+ *                     0 = exact decode.  In (0, 1): a position whose weight
+ *                     relative to the largest score seen so far in its
+ *                     split-K piece, exp(s_t - running max), is at most the
+ *                     threshold leaves the sum over V (it stays in Z).  That
+ *                     weight is never below the softmax weight exp(s_t) / Z,
+ *                     so the positions left out are a subset of those whose
+ *                     weight is at most the threshold; which ones depends on
+ *                     the order and the split-K pieces in which positions
+ *                     are visited.  A 16-token block none of whose positions
+ *                     is kept for any query head of the GQA group reads no V
+ *                     bytes and skips the V decode and the PV product.
+ *                     Outside [0, 1) (or NaN): PKV_ERR_INVALID; > 0 with a
+ *                     non-TQ V cache: PKV_ERR_UNSUPPORTED
  *   scale             softmax scale of the scores, finite and > 0 (else
  *                     PKV_ERR_INVALID)
  *   block_tables  in  int32 [num_seqs, max_blocks_per_seq]

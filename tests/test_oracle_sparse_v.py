@@ -2,8 +2,8 @@
 
 Page 2 (kv_cache_fp8k.rs, paged_decode_attn_fp8k_turbo3v) skips the V load
 and dequantisation of a position whose attention weight is at most a
-threshold, and page 1 marks its Turbo-V decodes "sparse V"; the threshold's
-value is not given.  The oracle returns the sum of w_t v_t over the positions
+threshold, and page 1 describes its Turbo-V decodes as sparse in V; the
+threshold's value is not given.  The oracle returns the sum of w_t v_t over the positions
 with w_t > tau and, as ``bound``, the sum of w_t |v_t| over the others.
 
 Pinned against: the exact decode (tau = 0, itself pinned in
