@@ -31,6 +31,11 @@
 // the PV product and v_scale is applied with the final normalisation.
 // Online softmax runs in the log2 domain.
 //
+// TQ V caches may skip V per block (page 2, paged_decode_attn_fp8k_turbo3v:
+// the sparse-V skip at a caller's threshold): separate instantiations score
+// a block first and load, decode and multiply its V only when some weight
+// exceeds the threshold.
+//
 // FP32 caches (VALU path).  Four tokens per wave step (16 lanes per token
 // row, 16-byte loads), one online-softmax stream per row, merged at the end.
 #include <mutex>
@@ -713,6 +718,8 @@ __global__ __launch_bounds__(512) void decode_mfma_kernel(DecodeArgs a, uint32_t
         constexpr int KPF = kPrefetchSpv;          // K blocks loaded ahead
         constexpr int KS = KPF + 1;                 // K stages
         constexpr int P = KS % 2 ? 2 * KS : KS;     // unroll period: K stages and V parity
+        static_assert(P == 2, "the two steps run ahead of the loop keep (b - b0) % P == u "
+                              "at the loop's entry only for a period of two");
         Stage kst[KS], vst[2];                      // K in kst[].k, V in vst[].v
         float pw[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
         bool keep[2] = {false, false};             // wave-uniform
