@@ -66,6 +66,8 @@ def main():
         pkv.paged_decode_attn(q, kc, vc, bt, lens, scale=0.1, out=out, workspace=ws)
         pkv.paged_decode_attn(q, kc8, vtq, bt, lens, scale=0.1, k_scale=0.5, out=out,
                               workspace=ws, v_tq_bits=3)
+        pkv.paged_decode_attn(q, kc8, vtq, bt, lens, scale=0.1, k_scale=0.5, out=out,
+                              workspace=ws, v_tq_bits=3, sparse_v_threshold=0.01)
         pkv.paged_decode_attn_noalloc(q, kc, vc, bt, lens, scale=0.1, out=out)
         pkv.paged_prefill_attn(qp, cu_q, kc, vc, bt, lens, max_q_len=32, scale=0.1, out=outp)
         pkv.mla_cache_assemble(lat, rope, slots, mk, mv, kv_lora=512, rope=64)
@@ -94,6 +96,8 @@ def main():
     pkv.cache_write_v(e_k, e_slots, vc)
     pkv.cache_write_v(e_k, e_slots, vtq, tq_bits=3)
     pkv.paged_decode_attn(e_q, kc, vc, e_bt, e_i32, scale=0.1, out=e_out, workspace=ws)
+    pkv.paged_decode_attn(e_q, kc8, vtq, e_bt, e_i32, scale=0.1, k_scale=0.5, out=e_out,
+                          workspace=ws, v_tq_bits=3, sparse_v_threshold=0.01)
     pkv.paged_decode_attn_noalloc(e_q, kc, vc, e_bt, e_i32, scale=0.1, out=e_out)
     pkv.paged_prefill_attn(e_q, e_cu, kc, vc, e_bt, e_i32, max_q_len=1, scale=0.1, out=e_outp)
     pkv.mla_cache_assemble(e_lat, e_rope, e_slots, mk, mv, kv_lora=512, rope=64)
@@ -104,7 +108,7 @@ def main():
     calls()
     roctx.roctxRangePop()
     torch.cuda.synchronize()
-    print("launch contract child: 9 zero-work calls, 10 calls with work", flush=True)
+    print("launch contract child: 10 zero-work calls, 11 calls with work", flush=True)
 
 
 if __name__ == "__main__":

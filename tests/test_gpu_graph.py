@@ -1,7 +1,9 @@
 """The decode step (slot fill, fused K write, V write, decode attention with
 its split-K merge) captured in a HIP graph and replayed: every replay, with
 the program's own eager work and synchronisations in between, gives the
-eager step's output and pools bit for bit."""
+eager step's output and pools bit for bit.  Cases: BF16 V, 3-bit TQ V, and
+3-bit TQ V with the sparse-V skip at a threshold (0.05) that both skips and
+keeps blocks of these scores."""
 import numpy as np
 import pytest
 import torch
@@ -13,13 +15,14 @@ from _util import host, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("v_kind", ["bf16", "tq3"])
+@pytest.mark.parametrize("v_kind", ["bf16", "tq3", "tq3_sparse"])
 def test_decode_step_graph_replays_match_eager(v_kind):
     lay = W.layout(2, num_seqs=32)
     cfg = lay.cfg
     S, Hq, Hkv, D, B = lay.num_seqs, cfg["num_q_heads"], cfg["num_kv_heads"], cfg["head_dim"], 16
     dev = torch.device("cuda")
-    tq = 3 if v_kind == "tq3" else 0
+    tq = 3 if v_kind.startswith("tq3") else 0
+    tau = 0.05 if v_kind == "tq3_sparse" else 0.0
     g = torch.Generator(device=dev)
     g.manual_seed(5)
     k_pool = torch.randn((lay.num_blocks, B, Hkv, D), device=dev, generator=g).to(torch.bfloat16)
@@ -48,7 +51,7 @@ def test_decode_step_graph_replays_match_eager(v_kind):
                                 theta=cfg["theta"])
         pkv.cache_write_v(v_new, slots, v_pool, tq_bits=tq)
         pkv.paged_decode_attn(q, k_pool, v_pool, bt, seq_lens, scale=D ** -0.5, out=out,
-                              workspace=ws, v_tq_bits=tq)
+                              workspace=ws, v_tq_bits=tq, sparse_v_threshold=tau)
 
     say(f"graph replay of a decode step, V {v_kind}")
     step()
