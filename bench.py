@@ -115,6 +115,25 @@ def log(*a):
 # algorithmic bytes (what the method must move)
 # --------------------------------------------------------------------------
 
+def event_average(fn, reps, stream, rounds=3):
+    """Average duration (ms) of one fn() call on `stream`, from HIP events
+    recorded on that stream around a batch of `reps` back-to-back calls;
+    the median of `rounds` batches, so that a batch in which the host or
+    the device paused does not set the figure."""
+    import torch
+    res = []
+    for _ in range(rounds):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / reps)
+    return float(np.median(res))
+
+
 def decode_bytes(lens, Hq, Hkv, D, Dv, kb, vb, qb, B=16, window=0, sinks=False):
     """KV rows read + block-table entries + seq_len + q read + FP32 out written
     (+ sink logits); with a window only the attended tokens [n - W, n) and the
@@ -362,9 +381,9 @@ def run_decode(name, args):
     use_graph = ms_graph is not None and ms_graph < ms_eager
     ms_per_step = ms_graph if use_graph else ms_eager
 
-    # per-call HIP-event timings on the launch stream
-    attn_ms = float(np.mean(time_call(step_attn, args.steps)))
-    write_ms = float(np.mean(time_call(step_writes, args.steps)))
+    # average call durations from HIP events on the launch stream (median of three batches)
+    attn_ms = event_average(step_attn, args.steps, stream)
+    write_ms = event_average(step_writes, args.steps, stream)
     log(f"step {ms_per_step:.3f} ms ({'graph replay' if use_graph else 'eager'}; eager "
         f"{ms_eager:.3f} ms, graph {'-' if ms_graph is None else f'{ms_graph:.3f}'} ms; decode call "
         f"{attn_ms:.3f} ms, step writes {write_ms * 1e3:.1f} us)")
@@ -549,16 +568,6 @@ def run_prefill(args):
         step_writes()
         step_attn()
 
-    def time_call(fn, reps):
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
-        for e0, e1 in evs:
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return [e0.elapsed_time(e1) for e0, e1 in evs]
-
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -567,8 +576,8 @@ def run_prefill(args):
         step()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    attn_ms = float(np.mean(time_call(step_attn, args.steps)))
-    write_ms = float(np.mean(time_call(step_writes, args.steps)))
+    attn_ms = event_average(step_attn, args.steps, stream)
+    write_ms = event_average(step_writes, args.steps, stream)
     flops = prefill_flops(lens, qlens, Hq, D, D)
     tflops = flops / (attn_ms * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms (prefill attention {attn_ms:.3f} ms = {tflops:.1f} TFLOP/s, "
