@@ -1,7 +1,7 @@
 """Helpers shared by the GPU parity tests: host<->device moves of the seeded
 inputs and the comparison rules.
 
-Comparison rules (derived in the design doc):
+Comparison rules:
   * slots and V: bit-exact;
   * K stored as BF16: at most 1 BF16 ulp, or |diff| <= 2^-20 * max|row|
     (a rotation can cancel to a value whose BF16 ulp is below FP32 noise;
