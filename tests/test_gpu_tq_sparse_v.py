@@ -91,7 +91,7 @@ def _run(q, kp, k_dt, vp, bits, lay, Hq, Hkv, tau, *, window=0, sinks=None, spli
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("k_dt", ["bf16", "fp8"])
-@pytest.mark.parametrize("G", [1, 4])
+@pytest.mark.parametrize("G", [1, 4, 16])
 def test_one_dominant_position_per_block(bits, k_dt, G):
     lay = W.layout_for(2, [0, 1, 15, 16, 17, 300, 999, 640])
     Hkv = 2
