@@ -753,11 +753,10 @@ static void attend(const decode_ctx* c, uint32_t s, uint32_t g, uint32_t h, int3
 }
 
 /* Sparse-V skip (p1 Turbo-V decode docs: the V loads and dequantisation are
- * sparse on both the batched and the remainder paths;
- * p2 paged_decode_attn_fp8k_turbo3v: a position's V load and
- * dequantisation are skipped when its attention
- * weight is at most TQ_PLUS_SPARSE_V_THRESHOLD, a value the pages do not
- * give).  Reading taken: the attention weight of position t is its softmax
+ * sparse on both the batched and the remainder paths; p2
+ * paged_decode_attn_fp8k_turbo3v: a position's V load and dequantisation
+ * are skipped when its attention weight is at most
+ * TQ_PLUS_SPARSE_V_THRESHOLD, a value the pages do not give).  Reading taken: the attention weight of position t is its softmax
  * weight w_t = exp(s_t) / Z with Z the exact decode's denominator (sinks
  * included); a skipped position leaves the sum over V and stays in Z (its
  * score is computed either way).  With threshold tau, for query head h:
