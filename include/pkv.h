@@ -385,8 +385,8 @@ int pkv_paged_decode_attn_noalloc(const void* q, pkv_dtype q_dtype, uint64_t q_s
                                   uint32_t split_tokens, void* stream);
 
 /*
- * pkv_paged_prefill_attn -- [p1] "batched prefill variants (N tokens)" of
- * the paged kernels (the page names them and gives no more): causal
+ * pkv_paged_prefill_attn -- [p1] the batched prefill variants of the paged
+ * kernels over N tokens (the page names them and gives no more): causal
  * attention of the new tokens of every sequence over the same paged cache,
  * after their K/V rows have been written (pkv_cache_write_k_fused /
  * pkv_cache_write_v).  Reading taken: the q_len = cu_q[s+1] - cu_q[s]

@@ -10,9 +10,9 @@
  * calls it, and the two share no source, header, table or helper.
  *
  * Arithmetic is FP64 except where the pages fix the precision:
- *   - the K path is held in FP32 at the store ("K stays FP32 between the
- *     three operations and is rounded only at the cache write": page 1,
- *     kv_cache.rs, doc of fused_k_norm_rope_cache_write_bf16), so the
+ *   - the K path is held in FP32 at the store (page 1, kv_cache.rs, doc of
+ *     fused_k_norm_rope_cache_write_bf16: K is kept in FP32 through the
+ *     three operations and rounded once, at the cache write), so the
  *     quantisation decision is taken on fl32 of the FP64 result;
  *   - the RoPE angle is an FP32 product of the FP32 position and an FP32
  *     inverse frequency (the FP32 regime of the same doc; our reading).
@@ -104,8 +104,8 @@ double pkvo_f64_from_e4m3(uint8_t c)
 
 /* x -> E4M3FN by round-to-nearest-even over the 127 non-negative finite
  * codes, saturating: a magnitude above 448 (infinity included) becomes 448
- * ("saturating FP8 cast": p1 kv_cache.rs, doc of
- * fused_k_norm_rope_cache_write_fp8).  NaN becomes the NaN code of the same
+ * (p1 kv_cache.rs, doc of fused_k_norm_rope_cache_write_fp8: the cast to
+ * FP8 saturates).  NaN becomes the NaN code of the same
  * sign.  Zero keeps its sign.  Written as a nearest-value search over the
  * code table, so it follows the format definition directly. */
 uint8_t pkvo_e4m3_from_f64(double x)

@@ -1,6 +1,7 @@
 // prefill_attn.hip -- pkv_paged_prefill_attn: causal attention of the N new
 // tokens of every sequence over its paged KV cache (page 1, kv_cache.rs,
-// "batched prefill variants (N tokens)" of the paged kernels; the reading:
+// the section on batched prefill variants of the paged kernels over N
+// tokens; the reading:
 // the q_len queries of a sequence are its last q_len tokens, already written
 // to the cache, and query i at position p = seq_len - q_len + i attends to
 // [lo, p], lo from the sliding window as in decode; sinks as in decode).
