@@ -51,7 +51,7 @@ constexpr uint32_t kKvPerGroup = 2;     // kv heads (waves) per work-group, at m
 constexpr int kPrefetch = 1;            // cache blocks loaded ahead of the one in use
 // Sparse-V loop: K blocks loaded ahead.  On the 256-sequence 3-bit TQ V
 // workload with one heavy key every 64 positions, 1, 2 and 3 blocks gave the
-// same call time (0.445-0.449 ms).
+// same call time (0.386-0.403 ms, batch-averaged).
 constexpr int kPrefetchSpv = 1;
 constexpr bool kKDirect = false;        // K loaded straight into the operand layout
 constexpr uint64_t kTargetGroups = 768; // (sequence, split, kv group) work-groups wanted
