@@ -97,7 +97,7 @@ def test_one_dominant_position_per_block(bits, k_dt, G):
     Hkv = 2
     q, kp, vp = _peaked(lay, Hkv, G, bits, k_dt, 40 + bits,
                         lambda s, n: list(range(0, n, 16)))
-    for split in (0, 64):
+    for split in (0, 16, 64):                # balanced ranges, one-block and four-block pieces
         got, out, bound, ref = _run(q, kp, k_dt, vp, bits, lay, Hkv * G, Hkv, TAU, split=split)
         err, moved = attn_err(got, out), attn_err(ref, out)
         say(f"  err vs sparse oracle {err:.3e}; exact vs sparse {moved:.3e}")
