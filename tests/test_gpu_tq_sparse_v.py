@@ -134,12 +134,13 @@ def test_whole_blocks_skipped_after_a_dominant_first_position(G):
     assert np.isfinite(got).all() and err <= ATTN_TOL and moved > 0.1
 
 
-@pytest.mark.parametrize("split", [0, 48])
-def test_random_scores_within_the_bound(split):
+@pytest.mark.parametrize("split,Hkv", [(0, 4), (48, 4), (0, 3)])
+def test_random_scores_within_the_bound(split, Hkv):
     """Unstructured peaked scores: the kernel's result lies within the
-    oracle's bound of its sparse output (plus the attention bar)."""
+    oracle's bound of its sparse output (plus the attention bar); an odd
+    kv-head count puts one kv head in each work-group."""
     lay = W.layout_for(3, [5, 100, 513, 4000, 2222])
-    Hkv, G = 4, 4
+    G = 4
     rng = np.random.default_rng(91)
     q = W.bf16_bits(rng.standard_normal((lay.num_seqs, Hkv * G, D)).astype(np.float32) * 3.0)
     kp = W.bf16_bits(rng.standard_normal((lay.num_blocks, 16, Hkv, D)).astype(np.float32))
